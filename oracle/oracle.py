@@ -1,0 +1,222 @@
+"""numpy/ctypes front end of the C oracle (test infrastructure only)."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "stq_oracle.c")
+_LIB = os.path.join(_DIR, "libstq_oracle.so")
+_CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fexcess-precision=standard",
+           "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
+
+__all__ = ["build", "lib", "refit", "dequant", "requant_fixed", "pack", "unpack",
+           "tile_bytes", "tile_stride", "update_f64", "OraclePool", "num_threads", "clip_events"]
+
+
+def build(force=False):
+    """Compile the oracle with gcc (binary32 ops, no contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc"] + _CFLAGS + ["-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L.orc_tile_bytes.restype = ctypes.c_size_t
+        L.orc_tile_bytes.argtypes = [I, I, I]
+        L.orc_tile_stride.restype = ctypes.c_size_t
+        L.orc_tile_stride.argtypes = [I, I, I]
+        L.orc_refit.argtypes = [I, I, P, P, P, P, P, P, P]
+        L.orc_dequant.argtypes = [I, I, P, P, P, P, P]
+        L.orc_requant_fixed.argtypes = [I, I, P, P, P, P, P]
+        L.orc_pack.argtypes = [I, I, I, P, P, P, P]
+        L.orc_unpack.argtypes = [I, I, I, P, P, P, P]
+        D = [I, I, I, I, I, I, I, P]
+        L.orc_pool_bytes.restype = ctypes.c_size_t
+        L.orc_pool_bytes.argtypes = D
+        L.orc_pool_init.argtypes = D + [P, P]
+        L.orc_pool_store.argtypes = D + [P, P, I, P]
+        L.orc_pool_fetch.argtypes = D + [P, P, I, P]
+        L.orc_pool_requant_fixed.argtypes = D + [P, P, I]
+        L.orc_decode_step.argtypes = D + [P, P, I, P, P, P, P, P, P]
+        L.orc_window_flush.argtypes = D + [P, P, I]
+        L.orc_update_f64.argtypes = [I, I, P, P, P, P, P, I, ctypes.c_double, P, P]
+        L.orc_num_threads.restype = I
+        L.orc_clip_events.restype = ctypes.c_long
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def num_threads():
+    return lib().orc_num_threads()
+
+
+def clip_events():
+    return lib().orc_clip_events()
+
+
+def tile_bytes(n, dk, dv):
+    return lib().orc_tile_bytes(n, dk, dv)
+
+
+def tile_stride(n, dk, dv):
+    return lib().orc_tile_stride(n, dk, dv)
+
+
+def refit(S, w, nb):
+    """R on one fp32 tile.  nb: width per row (16 = pivot).
+    Returns (sigma bf16 bits, c bf16 bits, Q int32 (pivot rows: binary16 bits), E)."""
+    S = _c(S, np.float32)
+    dk, dv = S.shape
+    w = _c(w, np.float32)
+    nb = _c(np.broadcast_to(nb, (dk,)), np.int32)
+    sig = np.zeros(dk, np.uint16)
+    cst = np.zeros(dv, np.uint16)
+    Q = np.zeros((dk, dv), np.int32)
+    E = np.zeros(1, np.int32)
+    lib().orc_refit(dk, dv, _p(S), _p(w), _p(nb), _p(sig), _p(cst), _p(Q), _p(E))
+    return sig, cst, Q, int(E[0])
+
+
+def update_f64(S, q, k, v, a, b):
+    """Binary64 gated delta update + readout of one tile.  a: scalar (GDN) or
+    [dk] (KDA).  Returns (S', o)."""
+    S = _c(S, np.float64)
+    dk, dv = S.shape
+    a = np.atleast_1d(_c(a, np.float64))
+    per_row = 1 if a.size == dk and dk > 1 else 0
+    Sp = np.zeros((dk, dv), np.float64)
+    o = np.zeros(dv, np.float64)
+    lib().orc_update_f64(dk, dv, _p(S), _p(_c(q, np.float64)), _p(_c(k, np.float64)),
+                         _p(_c(v, np.float64)), _p(a), per_row, float(b), _p(Sp), _p(o))
+    return Sp, o
+
+
+def dequant(sig, cst, Q, nb):
+    Q = _c(Q, np.int32)
+    dk, dv = Q.shape
+    nb = _c(np.broadcast_to(nb, (dk,)), np.int32)
+    S = np.zeros((dk, dv), np.float32)
+    lib().orc_dequant(dk, dv, _p(_c(sig, np.uint16)), _p(_c(cst, np.uint16)), _p(Q), _p(nb), _p(S))
+    return S
+
+
+def requant_fixed(S, sig, cst, nb):
+    S = _c(S, np.float32)
+    dk, dv = S.shape
+    nb = _c(np.broadcast_to(nb, (dk,)), np.int32)
+    Q = np.zeros((dk, dv), np.int32)
+    lib().orc_requant_fixed(dk, dv, _p(S), _p(_c(sig, np.uint16)), _p(_c(cst, np.uint16)), _p(nb), _p(Q))
+    return Q
+
+
+def pack(n, Q, sig, cst):
+    Q = _c(Q, np.int32)
+    dk, dv = Q.shape
+    t = np.zeros(tile_bytes(n, dk, dv), np.uint8)
+    lib().orc_pack(n, dk, dv, _p(Q), _p(_c(sig, np.uint16)), _p(_c(cst, np.uint16)), _p(t))
+    return t
+
+
+def unpack(n, dk, dv, tile):
+    tile = _c(tile, np.uint8)
+    Q = np.zeros((dk, dv), np.int32)
+    sig = np.zeros(dk, np.uint16)
+    cst = np.zeros(dv, np.uint16)
+    lib().orc_unpack(n, dk, dv, _p(tile), _p(Q), _p(sig), _p(cst))
+    return Q, sig, cst
+
+
+class OraclePool:
+    """Host image of a whole pool buffer, advanced by the oracle."""
+
+    def __init__(self, n_slots, n_heads, d_k, d_v, bits, row_weight, gate_kind=0,
+                 unit_kind=0, window=0, image=None):
+        self.n_slots, self.H, self.dk, self.dv = n_slots, n_heads, d_k, d_v
+        self.gate, self.unit, self.W = gate_kind, unit_kind, window
+        self.bits = _c(bits, np.int32)
+        self.wt = _c(row_weight, np.float32).reshape(n_heads, d_k)
+        self.nbytes = lib().orc_pool_bytes(*self._d())
+        if image is None:
+            self.img = np.zeros(self.nbytes, np.uint8)
+            lib().orc_pool_init(*self._d(), _p(self.wt), _p(self.img))
+        else:
+            assert image.size == self.nbytes
+            self.img = _c(image, np.uint8).copy()
+
+    def _d(self):
+        return (self.n_slots, self.H, self.dk, self.dv, self.gate, self.unit, self.W,
+                _p(self.bits))
+
+    def store(self, slots, S):
+        slots = _c(slots, np.int32)
+        S = _c(S, np.float32)
+        assert S.shape == (slots.size, self.H, self.dk, self.dv)
+        lib().orc_pool_store(*self._d(), _p(self.img), _p(slots), slots.size, _p(S))
+
+    def fetch(self, slots):
+        slots = _c(slots, np.int32)
+        S = np.zeros((slots.size, self.H, self.dk, self.dv), np.float32)
+        lib().orc_pool_fetch(*self._d(), _p(self.img), _p(slots), slots.size, _p(S))
+        return S
+
+    def requant_fixed(self, slots):
+        slots = _c(slots, np.int32)
+        lib().orc_pool_requant_fixed(*self._d(), _p(self.img), _p(slots), slots.size)
+
+    def step(self, slots, q, k, v, a, b):
+        """One decode token; returns the binary64 readout o [n][H][d_v]."""
+        slots = _c(slots, np.int32)
+        n = slots.size
+        q = _c(q, np.float32).reshape(n, self.H, self.dk)
+        k = _c(k, np.float32).reshape(n, self.H, self.dk)
+        v = _c(v, np.float32).reshape(n, self.H, self.dv)
+        a = _c(a, np.float32)
+        assert a.size == (n * self.H * self.dk if self.gate else n * self.H)
+        b = _c(b, np.float32).reshape(n, self.H)
+        o = np.zeros((n, self.H, self.dv), np.float64)
+        lib().orc_decode_step(*self._d(), _p(self.img), _p(slots), n, _p(q), _p(k), _p(v),
+                              _p(a), _p(b), _p(o))
+        return o
+
+    def window_flush(self, slots):
+        slots = _c(slots, np.int32)
+        lib().orc_window_flush(*self._d(), _p(self.img), _p(slots), slots.size)
+
+    # byte views ------------------------------------------------------
+    def hdr_bytes(self):
+        woff = (64 + 8 * self.H + 255) // 256 * 256
+        return (woff + 4 * self.H * self.dk + 255) // 256 * 256
+
+    def head_offsets(self):
+        offs, s = [], 0
+        for h in range(self.H):
+            offs.append(s)
+            s += tile_stride(int(self.bits[h]), self.dk, self.dv)
+        return offs, s
+
+    def tile_view(self, slot, h, img=None):
+        img = self.img if img is None else img
+        offs, sb = self.head_offsets()
+        base = self.hdr_bytes() + slot * sb + offs[h]
+        return img[base: base + tile_bytes(int(self.bits[h]), self.dk, self.dv)]
