@@ -184,7 +184,7 @@ typedef struct stq_pool_desc {
   int32_t d_k, d_v;     /* each 64 or 128                                   */
   int32_t gate_kind;    /* STQ_GATE_HEAD or STQ_GATE_CHANNEL                */
   int32_t unit_kind;    /* STQ_UNIT_HEAD (this build) or STQ_UNIT_ROW       */
-  int32_t window;       /* 0 = requantize every token; W in [1,63] = window */
+  int32_t window;       /* 0 = requantize every token; W in [1,32] = window */
   const int32_t* unit_bits;  /* [H] widths, each 4, 6, 8 or 16                */
   const float* row_weight;   /* [H][d_k] row-impact weights, finite and > 0   */
 } stq_pool_desc;

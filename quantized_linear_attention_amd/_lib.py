@@ -1,0 +1,165 @@
+"""ctypes marshalling for libstq.so (no computation happens here)."""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_PATH = os.path.join(_PKG, "libstq.so")
+
+STQ_OK = 0
+STQ_GATE_HEAD, STQ_GATE_CHANNEL = 0, 1
+STQ_UNIT_HEAD, STQ_UNIT_ROW = 0, 1
+
+
+class StqError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s: %s" % (what, stq_status_str(status)))
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("gate_kind", ctypes.c_int32), ("unit_kind", ctypes.c_int32),
+                ("window", ctypes.c_int32),
+                ("unit_bits", ctypes.POINTER(ctypes.c_int32)),
+                ("row_weight", ctypes.POINTER(ctypes.c_float))]
+
+
+def library_path():
+    return _PATH
+
+
+def _load():
+    if not os.path.exists(_PATH):
+        raise ImportError("libstq.so is not built (%s); run quantized_linear_attention_amd/build.py "
+                          "or __graft_entry__.build()" % _PATH)
+    L = ctypes.CDLL(_PATH)
+    P, I, St = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    DP = ctypes.POINTER(_Desc)
+    L.stq_status_str.restype = ctypes.c_char_p
+    L.stq_status_str.argtypes = [I]
+    L.stq_pool_bytes.restype = ctypes.c_size_t
+    L.stq_pool_bytes.argtypes = [DP]
+    L.stq_pool_create.restype = I
+    L.stq_pool_create.argtypes = [DP, P, ctypes.c_size_t, St, ctypes.POINTER(P)]
+    L.stq_pool_destroy.restype = I
+    L.stq_pool_destroy.argtypes = [P]
+    for name in ("stq_pool_store", "stq_pool_fetch"):
+        getattr(L, name).restype = I
+        getattr(L, name).argtypes = [P, P, I, P, St]
+    L.stq_decode_step.restype = I
+    L.stq_decode_step.argtypes = [P, P, I, P, P, P, P, P, P, St]
+    for name in ("stq_window_flush", "stq_requant_fixed_scales"):
+        getattr(L, name).restype = I
+        getattr(L, name).argtypes = [P, P, I, St]
+    return L
+
+
+_L = _load()
+
+
+def stq_status_str(status):
+    return _L.stq_status_str(int(status)).decode()
+
+
+def _check(status, what):
+    if status != STQ_OK:
+        raise StqError(status, what)
+
+
+def make_desc(n_slots, n_heads, d_k, d_v, unit_bits, row_weight, gate_kind=STQ_GATE_HEAD,
+              unit_kind=STQ_UNIT_HEAD, window=0):
+    """Build a stq_pool_desc; the returned object keeps its host arrays alive."""
+    bits = np.ascontiguousarray(unit_bits, dtype=np.int32).reshape(-1)
+    wt = np.ascontiguousarray(row_weight, dtype=np.float32).reshape(-1)
+    d = _Desc(int(n_slots), int(n_heads), int(d_k), int(d_v), int(gate_kind), int(unit_kind),
+              int(window), bits.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+              wt.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    d._keep = (bits, wt)
+    return d
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def _dev(t, dtype, what):
+    import torch
+    if t is None:
+        return None
+    if not (t.is_cuda and t.is_contiguous() and t.dtype == dtype):
+        raise StqError(-1, "%s must be a contiguous %s CUDA tensor" % (what, dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def stq_pool_bytes(desc):
+    return int(_L.stq_pool_bytes(ctypes.byref(desc)))
+
+
+class _Pool:
+    def __init__(self, handle, desc, buf):
+        self.handle, self.desc, self.buf = handle, desc, buf
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            _L.stq_pool_destroy(self.handle)
+            self.handle = None
+
+
+def stq_pool_create(desc, buf, stream=None):
+    """buf: uint8 CUDA tensor of at least stq_pool_bytes(desc) bytes (256-aligned)."""
+    import torch
+    out = ctypes.c_void_p()
+    p = _dev(buf, torch.uint8, "pool buffer")
+    _check(_L.stq_pool_create(ctypes.byref(desc), p, buf.numel(), _stream(stream), ctypes.byref(out)),
+           "stq_pool_create")
+    return _Pool(out, desc, buf)
+
+
+def stq_pool_destroy(pool):
+    if pool.handle:
+        _check(_L.stq_pool_destroy(pool.handle), "stq_pool_destroy")
+        pool.handle = None
+
+
+def _slots(slots):
+    import torch
+    return _dev(slots, torch.int32, "slots"), int(slots.numel())
+
+
+def stq_pool_store(pool, slots, S, stream=None):
+    import torch
+    sp, n = _slots(slots)
+    _check(_L.stq_pool_store(pool.handle, sp, n, _dev(S, torch.float32, "S"), _stream(stream)),
+           "stq_pool_store")
+
+
+def stq_pool_fetch(pool, slots, S_out, stream=None):
+    import torch
+    sp, n = _slots(slots)
+    _check(_L.stq_pool_fetch(pool.handle, sp, n, _dev(S_out, torch.float32, "S_out"), _stream(stream)),
+           "stq_pool_fetch")
+
+
+def stq_decode_step(pool, slots, q, k, v, a, b, o, stream=None):
+    import torch
+    f = torch.float32
+    sp, n = _slots(slots)
+    _check(_L.stq_decode_step(pool.handle, sp, n, _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"),
+                              _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"), _stream(stream)),
+           "stq_decode_step")
+
+
+def stq_window_flush(pool, slots, stream=None):
+    sp, n = _slots(slots)
+    _check(_L.stq_window_flush(pool.handle, sp, n, _stream(stream)), "stq_window_flush")
+
+
+def stq_requant_fixed_scales(pool, slots, stream=None):
+    sp, n = _slots(slots)
+    _check(_L.stq_requant_fixed_scales(pool.handle, sp, n, _stream(stream)), "stq_requant_fixed_scales")

@@ -1,0 +1,840 @@
+// stq.hip — gfx950 kernels and C ABI of the low-bit recurrent-state pool
+// (contract: include/stq.h).
+//
+// One workgroup per (request, head) tile.  Each 64-lane wave owns all d_k
+// rows of CPW value columns; each lane owns a 16 x 4 block, so every column
+// reduction (the two matvecs u = A^T k, w = A^T q and the column absmax of
+// the refit) closes inside a wave with three DPP steps, and only the row
+// absmax crosses waves (through LDS).  Codes are loaded and stored with one
+// 16-byte access per lane per chunk (1 KiB contiguous per wave).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "stq.h"
+#include "stq_device.h"
+
+using namespace stq;
+
+namespace {
+
+enum { MODE_STEP = 0, MODE_STORE = 1 };
+
+struct KArgs {
+  uint8_t* pool;
+  const int32_t* slots;      // nullptr: slot = request index
+  int n, H, n_slots, gate, W;
+  uint64_t slots_off, slot_bytes, cache_off, cache_stride;
+  const int32_t* head_bits;  // device: header tables
+  const uint32_t* head_off;
+  const float* weights;      // [H][d_k]
+  const float *q, *k, *v, *a, *b;
+  float* o;
+  const float* S_in;         // store: [n][H][d_k][d_v] (nullptr: zeros)
+  float* S_out;              // fetch
+};
+
+template <int DK, int DV>
+struct Smem {
+  float alpha[DK] __attribute__((aligned(16)));   // [rb][r]: g k
+  float beta[DK] __attribute__((aligned(16)));    // g q
+  float kappa[DK] __attribute__((aligned(16)));   // k / g
+  float gg[DK] __attribute__((aligned(16)));      // g = gate * old row scale
+  float rowh[DK] __attribute__((aligned(16)));    // new X factor per row
+  float part[Geo<DK, DV>::NP * DK] __attribute__((aligned(16)));
+  float kqp[Geo<DK, DV>::NW];
+  int esum[Geo<DK, DV>::NW];
+  int ecnt[Geo<DK, DV>::NW];
+};
+
+// XCD-aware tile order: workgroups are dealt round-robin over the 8 XCDs, so
+// give XCD x the contiguous tile range [x*per, (x+1)*per): every XCD then
+// sees the same mix of head widths and its L2 serves whole slots.
+__device__ __forceinline__ int tile_of_block(int T) {
+  int per = (T + 7) >> 3;
+  return (int)(blockIdx.x & 7u) * per + (int)(blockIdx.x >> 3);
+}
+
+// ------------------------------------------------------------------------
+// Shared refit + store stage.  Y[4r+c] holds S'_ij / g_i for the lane's
+// elements (g_i in sm.gg, visible after the next barrier); for a binary16
+// pivot tile Y holds S' itself.  Writes codes, row and column scales.
+// ------------------------------------------------------------------------
+template <int DK, int DV, int N>
+__device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, float* Y, uint8_t* tile, int h) {
+  using G = Geo<DK, DV>;
+  constexpr int K = N / 2;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int rb = l % G::RB, cb = l / G::RB;
+  const int j0 = w * G::CPW + 4 * cb;
+  uint8_t* codes = tile;
+  uint16_t* scl = (uint16_t*)(tile + DK * DV * N / 8);
+  uint32_t raw[2 * N];
+  if constexpr (N == 16) {
+    // binary16 pivot tile: saturate, round to nearest even
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; h2++) {
+        float s0 = __builtin_fminf(__builtin_fmaxf(Y[4 * r + 2 * h2], -65504.f), 65504.f);
+        float s1 = __builtin_fminf(__builtin_fmaxf(Y[4 * r + 2 * h2 + 1], -65504.f), 65504.f);
+        raw[2 * r + h2] = h2_bits(f16x2{(f16)s0, (f16)s1});
+      }
+  } else {
+    const int rho = tid / G::TPR, rsub = tid % G::TPR;
+    const int irow = (rho >> 4) + G::RB * (rho & 15);
+    // ---- row refit: partial row absmax -> LDS -> one thread (pair) per row ----
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      f32x4 m4;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        int r = 4 * r4 + q;
+        m4[q] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(Y[4 * r]), __builtin_fabsf(Y[4 * r + 1])),
+                                __builtin_fmaxf(__builtin_fabsf(Y[4 * r + 2]), __builtin_fabsf(Y[4 * r + 3])));
+      }
+      *(f32x4*)&sm.part[(w * G::CBW + cb) * DK + rb * 16 + 4 * r4] = m4;
+    }
+    __syncthreads();
+    float mx = 0.f;
+#pragma unroll
+    for (int p = 0; p < G::NP / G::TPR; p++) mx = __builtin_fmaxf(mx, sm.part[(rsub * (G::NP / G::TPR) + p) * DK + rho]);
+    if (G::TPR == 2) mx = __builtin_fmaxf(mx, dpp<0xB1>(mx));
+    const float g = sm.gg[rho];
+    const float m = g * mx;                        // row absmax of S'
+    const float pw = m * A.weights[(size_t)h * DK + irow];
+    uint32_t s = 0x3F80u;
+    int e = 0, cnt = 0;
+    if (pw > 0.f) {
+      s = bf16_rne(__builtin_sqrtf(pw));          // correctly rounded sqrt
+      e = (int)((s >> 7) & 0xFFu) - 127;
+      cnt = 1;
+    }
+    if (rsub != 0) { e = 0; cnt = 0; }
+    const float rs = 1.0f / bf16f(s);             // IEEE division
+    if (rsub == 0) sm.rowh[rho] = g * rs;
+    e = wave_sum_i(e);
+    cnt = wave_sum_i(cnt);
+    if (l == 0) { sm.esum[w] = e; sm.ecnt[w] = cnt; }
+    __syncthreads();
+    int es = 0, ec = 0;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) { es += sm.esum[ww]; ec += sm.ecnt[ww]; }
+    const int E = ec ? mean_exp(es, ec) : 0;
+    if (rsub == 0) scl[irow] = (uint16_t)bf16_adj(s, -E);
+    // ---- column refit ----
+    float hr[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&hr[4 * r4] = *(const f32x4*)&sm.rowh[rb * 16 + 4 * r4];
+    float cm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        Y[4 * r + c] = Y[4 * r + c] * hr[r];
+        cm[c] = __builtin_fmaxf(cm[c], __builtin_fabsf(Y[4 * r + c]));
+      }
+    float rc[4];
+    uint32_t cst[4];
+    constexpr float RQ = 1.0f / (float)Fmt<N>::QMAX;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      float M = rb_max<G::RB>(cm[c]) * RQ;
+      uint32_t t = 0x3F80u;
+      if (M > 0.f) {
+        t = bf16_ru_pos(M);
+        if (t < 0x0080u) t = 0x0080u;            // at least 2^-126
+      }
+      rc[c] = 1.0f / bf16f(t);
+      cst[c] = bf16_adj(t, E);
+    }
+    if (rb == 0) *(u32x2*)(scl + DK + j0) = u32x2{cst[0] | (cst[1] << 16), cst[2] | (cst[3] << 16)};
+    // ---- requantize: nearest code of the exact product, field in the low bits ----
+    uint32_t yb[64];
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        yb[4 * r + c] = __float_as_uint(__builtin_fmaf(Y[4 * r + c], rc[c], Fmt<N>::MAGIC));
+    pack<N>(yb, raw);
+  }
+#pragma unroll
+  for (int k = 0; k < K; k++) *(u32x4*)(codes + 16 * ((w * K + k) * 64 + l)) = *(const u32x4*)&raw[4 * k];
+}
+
+// ------------------------------------------------------------------------
+// Tile body: MODE_STEP = decode step (unpack, gate, delta update, readout,
+// then refit_store); MODE_STORE = refit_store of a given fp32 tile.
+// ------------------------------------------------------------------------
+template <int DK, int DV, int MODE, int N>
+__device__ __forceinline__ void tile_body(const KArgs& A, Smem<DK, DV>& sm, uint8_t* tile,
+                                          size_t x, int h, uint8_t* cache) {
+  using G = Geo<DK, DV>;
+  constexpr int K = N / 2;                 // 16-byte chunks per lane stream
+  constexpr bool PIV = (N == 16);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int rb = l % G::RB, cb = l / G::RB;
+  const int j0 = w * G::CPW + 4 * cb;
+  uint8_t* codes = tile;
+  uint16_t* scl = (uint16_t*)(tile + DK * DV * N / 8);   // sigma[DK], c[DV]
+  // row-stage assignment: slot rho of the [rb][r] order, row irow
+  const int rho = tid / G::TPR, rsub = tid % G::TPR;
+  const int irow = (rho >> 4) + G::RB * (rho & 15);
+  float Y[64];
+
+  if constexpr (MODE == MODE_STEP) {
+    uint32_t raw[2 * N];
+    f16x2 P[32];
+    float cc[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int k = 0; k < K; k++)
+      *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+    // ---- per-row factors (once per row) ----
+    float ai = 1.f, kq = 0.f;
+    if (rsub == 0) {
+      float kk = A.k[x * DK + irow], qq = A.q[x * DK + irow];
+      ai = A.gate ? A.a[x * DK + irow] : A.a[x];
+      float sg = PIV ? 1.f : bf16f(scl[irow]);
+      float g = ai * sg;
+      sm.alpha[rho] = g * kk;
+      sm.beta[rho] = g * qq;
+      sm.kappa[rho] = PIV ? kk : kk / g;          // pivots update S' directly
+      sm.gg[rho] = g;
+      kq = kk * qq;
+    }
+    kq = wave_sum(kq);
+    if (l == 0) sm.kqp[w] = kq;
+    const int allone = __syncthreads_and(ai == 1.f);
+    // ---- u = A^T k, w = A^T q ----
+    unpack<N>(raw, P);
+    float al[16], be[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      *(f32x4*)&al[4 * r4] = *(const f32x4*)&sm.alpha[rb * 16 + 4 * r4];
+      *(f32x4*)&be[4 * r4] = *(const f32x4*)&sm.beta[rb * 16 + 4 * r4];
+    }
+    float U[4] = {0.f, 0.f, 0.f, 0.f}, Wr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        float qv = code_at<N>(P, r, c);
+        U[c] = __builtin_fmaf(qv, al[r], U[c]);
+        Wr[c] = __builtin_fmaf(qv, be[r], Wr[c]);
+      }
+    if constexpr (!PIV) {
+      u32x2 cw = *(const u32x2*)(scl + DK + j0);
+      cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
+      cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
+    }
+    float kqs = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqp[ww];
+    const float bb = A.b[x];
+    const f32x4 vv = *(const f32x4*)(A.v + x * DV + j0);
+    float delta[4];
+    f32x4 ov;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      float u = cc[c] * rb_sum<G::RB>(U[c]);
+      float wq = cc[c] * rb_sum<G::RB>(Wr[c]);
+      delta[c] = bb * (vv[c] - u);
+      ov[c] = __builtin_fmaf(delta[c], kqs, wq);
+    }
+    if (rb == 0) *(f32x4*)(A.o + x * DV + j0) = ov;
+    if (bb == 0.f && allone) return;      // identity update: keep the encoding
+    float ka[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&ka[4 * r4] = *(const f32x4*)&sm.kappa[rb * 16 + 4 * r4];
+    if constexpr (PIV) {
+      // S' = fma(k, delta, g H): two roundings on the way to binary16
+      float gr[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&gr[4 * r4] = *(const f32x4*)&sm.gg[rb * 16 + 4 * r4];
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+          Y[4 * r + c] = __builtin_fmaf(ka[r], delta[c], gr[r] * code_at<N>(P, r, c));
+    } else {
+      // S' / g in registers: Y = c Q + (k / g) delta
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+          Y[4 * r + c] = __builtin_fmaf(code_at<N>(P, r, c), cc[c], ka[r] * delta[c]);
+    }
+  } else {
+    // ---- store: Y = the given fp32 tile, g = 1 ----
+    const float* S = A.S_in ? A.S_in + x * DK * DV : nullptr;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      f32x4 s4 = S ? *(const f32x4*)(S + (size_t)(rb + G::RB * r) * DV + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; c++) Y[4 * r + c] = s4[c];
+    }
+    if (rsub == 0) sm.gg[rho] = 1.f;
+    if (cache) {
+      if (A.S_in) {
+        if (tid == 0) *(int32_t*)cache = 0;                 // empty the window
+      } else {                                              // pool creation: clear the whole cache
+        for (uint64_t off = 16 * (uint64_t)tid; off < A.cache_stride; off += 16 * G::NT)
+          *(u32x4*)(cache + off) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (!A.S_in) {                                          // pool creation: clear the tile padding
+      constexpr int TB = DK * DV * N / 8 + (PIV ? 0 : 2 * (DK + DV));
+      constexpr int TS = (TB + 255) / 256 * 256;
+      for (int off = TB + 16 * tid; off < TS; off += 16 * G::NT) *(u32x4*)(tile + off) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  refit_store<DK, DV, N>(A, sm, Y, tile, h);
+}
+
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_tile(KArgs A) {
+  __shared__ Smem<DK, DV> sm;
+  const int T = A.n * A.H;
+  const int tau = tile_of_block(T);
+  if (tau >= T) return;
+  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int slot = A.slots ? A.slots[ci] : ci;
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+  uint8_t* cache = A.W ? A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride : nullptr;
+  const size_t x = (size_t)ci * A.H + h;
+  switch (A.head_bits[h]) {
+    case 4: tile_body<DK, DV, MODE, 4>(A, sm, tile, x, h, cache); break;
+    case 6: tile_body<DK, DV, MODE, 6>(A, sm, tile, x, h, cache); break;
+    case 8: tile_body<DK, DV, MODE, 8>(A, sm, tile, x, h, cache); break;
+    default: tile_body<DK, DV, MODE, 16>(A, sm, tile, x, h, cache); break;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Window mode: the quantized base S0 is frozen inside a window of W tokens;
+// the cache of the tile holds, per token s of the open window, k_s, the
+// written vector u_s and G_s (product of the gates since the window opened),
+// all binary32.  FLUSH = fold the open window now (no new token).
+// ------------------------------------------------------------------------
+constexpr int WMAX = 32;
+
+template <int DK>
+struct WSmem {
+  float kap[WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i), [s][rb][r]
+  float cfk[WMAX];                                        // (G_t/G_s) k_s.k_t
+  float cfq[WMAX];                                        // (G_t/G_s) k_s.q_t
+};
+
+template <int DK, int DV, int N, bool FLUSH>
+__device__ __forceinline__ void window_body(const KArgs& A, Smem<DK, DV>& sm, WSmem<DK>& ws, uint8_t* tile,
+                                            uint8_t* cache, size_t x, int h) {
+  using G = Geo<DK, DV>;
+  constexpr int K = N / 2;
+  constexpr bool PIV = (N == 16);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int rb = l % G::RB, cb = l / G::RB;
+  const int j0 = w * G::CPW + 4 * cb;
+  const int rho = tid / G::TPR, rsub = tid % G::TPR;
+  const int irow = (rho >> 4) + G::RB * (rho & 15);
+  uint8_t* codes = tile;
+  const uint16_t* scl = (const uint16_t*)(tile + DK * DV * N / 8);
+  const int W = A.W;
+  int32_t* cntp = (int32_t*)cache;
+  float* Gc = (float*)(cache + 4);
+  float* Kc = (float*)(cache + 256);
+  float* Uc = Kc + (size_t)W * DK;
+  const int t = *cntp;                         // tokens already in the window
+  if (FLUSH && t == 0) return;                 // nothing to fold
+  const bool fold = FLUSH || (t + 1 == W);
+  const int ns = FLUSH ? t : t + 1;            // tokens in the fold
+  float Gt;
+  if constexpr (FLUSH) {
+    Gt = Gc[t - 1];
+  } else {
+    const float a = A.a[x];
+    Gt = t ? Gc[t - 1] * a : a;                // binary32 running product
+  }
+  uint32_t raw[2 * N];
+  f16x2 P[32];
+#pragma unroll
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+  float cc[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (!PIV) {
+    u32x2 cw = *(const u32x2*)(scl + DK + j0);
+    cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
+    cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
+  }
+  // ---- per-row work (once per row) ----
+  float kq = 0.f;
+  if (rsub == 0) {
+    const float sg = PIV ? 1.f : bf16f(scl[irow]);
+    if constexpr (!FLUSH) {
+      const float kk = A.k[x * DK + irow], qq = A.q[x * DK + irow];
+      sm.alpha[rho] = sg * kk;
+      sm.beta[rho] = sg * qq;
+      kq = kk * qq;
+      Kc[(size_t)t * DK + irow] = kk;                       // append k_t
+      if (fold) ws.kap[t * DK + rho] = kk / (Gt * sg);
+    }
+    if (fold) {
+      for (int s = 0; s < t; s++) ws.kap[s * DK + rho] = Kc[(size_t)s * DK + irow] / (Gc[s] * sg);
+      sm.gg[rho] = Gt * sg;
+    }
+  }
+  if constexpr (!FLUSH) {
+    kq = wave_sum(kq);
+    if (l == 0) sm.kqp[w] = kq;
+    // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: RB consecutive lanes per dot
+    for (int sd = tid / G::RB; sd < 2 * t; sd += G::NT / G::RB) {
+      const int s = sd % t;
+      const float* vec = (sd < t ? A.k : A.q) + x * DK;
+      const int i0 = 16 * (tid % G::RB);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i0 + i);
+        f32x4 vv = *(const f32x4*)(vec + i0 + i);
+        acc = __builtin_fmaf(ks[0], vv[0], acc); acc = __builtin_fmaf(ks[1], vv[1], acc);
+        acc = __builtin_fmaf(ks[2], vv[2], acc); acc = __builtin_fmaf(ks[3], vv[3], acc);
+      }
+      acc = rb_sum<G::RB>(acc);
+      if (tid % G::RB == 0) {
+        const float f = (Gt / Gc[s]) * acc;
+        if (sd < t) ws.cfk[s] = f; else ws.cfq[s] = f;
+      }
+    }
+  }
+  __syncthreads();
+  unpack<N>(raw, P);
+  float u4[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!FLUSH) {
+    // ---- readout and written vector from the frozen base and the cache ----
+    float al[16], be[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      *(f32x4*)&al[4 * r4] = *(const f32x4*)&sm.alpha[rb * 16 + 4 * r4];
+      *(f32x4*)&be[4 * r4] = *(const f32x4*)&sm.beta[rb * 16 + 4 * r4];
+    }
+    float U[4] = {0.f, 0.f, 0.f, 0.f}, Wr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        float qv = code_at<N>(P, r, c);
+        U[c] = __builtin_fmaf(qv, al[r], U[c]);
+        Wr[c] = __builtin_fmaf(qv, be[r], Wr[c]);
+      }
+    float kqs = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqp[ww];
+    const float bb = A.b[x];
+    const f32x4 vv = *(const f32x4*)(A.v + x * DV + j0);
+    float rr[4], oo[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      rr[c] = vv[c] - Gt * (cc[c] * rb_sum<G::RB>(U[c]));
+      oo[c] = Gt * (cc[c] * rb_sum<G::RB>(Wr[c]));
+    }
+    for (int s = 0; s < t; s++) {
+      const f32x4 us = *(const f32x4*)(Uc + (size_t)s * DV + j0);
+      const float fk = ws.cfk[s], fq = ws.cfq[s];
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        rr[c] = __builtin_fmaf(-fk, us[c], rr[c]);
+        oo[c] = __builtin_fmaf(fq, us[c], oo[c]);
+      }
+    }
+    f32x4 ov, uv;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      u4[c] = bb * rr[c];
+      uv[c] = u4[c];
+      ov[c] = __builtin_fmaf(kqs, u4[c], oo[c]);
+    }
+    if (rb == 0) {
+      *(f32x4*)(A.o + x * DV + j0) = ov;
+      *(f32x4*)(Uc + (size_t)t * DV + j0) = uv;           // append u_t
+    }
+    if (tid == 0) {
+      Gc[t] = Gt;
+      if (!fold) *cntp = t + 1;
+    }
+    if (!fold) return;
+  }
+  // ---- fold: S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T  ->  refit, window emptied ----
+  float Y[64];
+#pragma unroll
+  for (int r = 0; r < 64; r++) Y[r] = 0.f;
+  for (int s = 0; s < ns; s++) {
+    f32x4 us;
+    if (!FLUSH && s == t) us = f32x4{u4[0], u4[1], u4[2], u4[3]};
+    else us = *(const f32x4*)(Uc + (size_t)s * DV + j0);
+    float kp[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&kp[4 * r4] = *(const f32x4*)&ws.kap[s * DK + rb * 16 + 4 * r4];
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) Y[4 * r + c] = __builtin_fmaf(kp[r], us[c], Y[4 * r + c]);
+  }
+  if constexpr (PIV) {
+    float gr[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&gr[4 * r4] = *(const f32x4*)&sm.gg[rb * 16 + 4 * r4];
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) Y[4 * r + c] = gr[r] * (code_at<N>(P, r, c) + Y[4 * r + c]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) Y[4 * r + c] = __builtin_fmaf(code_at<N>(P, r, c), cc[c], Y[4 * r + c]);
+  }
+  if (tid == 0) *cntp = 0;
+  refit_store<DK, DV, N>(A, sm, Y, tile, h);
+}
+
+template <int DK, int DV, bool FLUSH>
+__global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_window(KArgs A) {
+  __shared__ Smem<DK, DV> sm;
+  __shared__ WSmem<DK> ws;
+  const int T = A.n * A.H;
+  const int tau = tile_of_block(T);
+  if (tau >= T) return;
+  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int slot = A.slots[ci];
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+  uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
+  const size_t x = (size_t)ci * A.H + h;
+  switch (A.head_bits[h]) {
+    case 4: window_body<DK, DV, 4, FLUSH>(A, sm, ws, tile, cache, x, h); break;
+    case 6: window_body<DK, DV, 6, FLUSH>(A, sm, ws, tile, cache, x, h); break;
+    case 8: window_body<DK, DV, 8, FLUSH>(A, sm, ws, tile, cache, x, h); break;
+    default: window_body<DK, DV, 16, FLUSH>(A, sm, ws, tile, cache, x, h); break;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Fetch (D) and fixed-scale requantization.
+// ------------------------------------------------------------------------
+template <int DK, int DV, int N, bool REQ>
+__device__ __forceinline__ void fetch_body(const KArgs& A, uint8_t* tile, size_t x) {
+  using G = Geo<DK, DV>;
+  constexpr int K = N / 2;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int rb = l % G::RB, cb = l / G::RB;
+  const int j0 = w * G::CPW + 4 * cb;
+  uint8_t* codes = tile;
+  const uint16_t* scl = (const uint16_t*)(tile + DK * DV * N / 8);
+  uint32_t raw[2 * N];
+  f16x2 P[32];
+#pragma unroll
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+  unpack<N>(raw, P);
+  float sg[16], cc[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+  for (int r = 0; r < 16; r++) sg[r] = (N == 16) ? 1.f : bf16f(scl[rb + G::RB * r]);
+  if (N != 16) {
+    u32x2 cw = *(const u32x2*)(scl + DK + j0);
+    cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
+    cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
+  }
+  float Y[64];
+#pragma unroll
+  for (int r = 0; r < 16; r++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      float qv = code_at<N>(P, r, c);
+      Y[4 * r + c] = (N == 16) ? qv : (sg[r] * cc[c]) * qv;
+    }
+  if constexpr (!REQ) {
+    float* S = A.S_out + x * DK * DV;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      *(f32x4*)(S + (size_t)(rb + G::RB * r) * DV + j0) = f32x4{Y[4 * r], Y[4 * r + 1], Y[4 * r + 2], Y[4 * r + 3]};
+  } else if constexpr (N != 16) {
+    float rs[16], rc[4];
+#pragma unroll
+    for (int r = 0; r < 16; r++) rs[r] = 1.0f / sg[r];
+#pragma unroll
+    for (int c = 0; c < 4; c++) rc[c] = 1.0f / cc[c];
+    uint32_t yb[64];
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        float X = Y[4 * r + c] * rs[r];
+        float q = __builtin_fmaf(X, rc[c], Fmt<N>::MAGIC);
+        q = __builtin_fminf(__builtin_fmaxf(q, Fmt<N>::MAGIC - Fmt<N>::QMAX), Fmt<N>::MAGIC + Fmt<N>::QMAX);
+        yb[4 * r + c] = __float_as_uint(q);
+      }
+    pack<N>(yb, raw);
+#pragma unroll
+    for (int k = 0; k < K; k++) *(u32x4*)(codes + 16 * ((w * K + k) * 64 + l)) = *(const u32x4*)&raw[4 * k];
+  }
+}
+
+template <int DK, int DV, bool REQ>
+__global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_fetch(KArgs A) {
+  const int T = A.n * A.H;
+  const int tau = tile_of_block(T);
+  if (tau >= T) return;
+  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int slot = A.slots[ci];
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+  const size_t x = (size_t)ci * A.H + h;
+  switch (A.head_bits[h]) {
+    case 4: fetch_body<DK, DV, 4, REQ>(A, tile, x); break;
+    case 6: fetch_body<DK, DV, 6, REQ>(A, tile, x); break;
+    case 8: fetch_body<DK, DV, 8, REQ>(A, tile, x); break;
+    default: fetch_body<DK, DV, 16, REQ>(A, tile, x); break;
+  }
+}
+
+}  // namespace
+
+// ==========================================================================
+// Host side
+// ==========================================================================
+struct stq_pool {
+  int32_t n_slots, H, dk, dv, gate, unit, W;
+  std::vector<int32_t> bits;
+  std::vector<uint32_t> head_off;
+  uint64_t hdr, woff, slot_bytes, slots_off, cache_off, cache_stride, total;
+  uint8_t* dev;
+  std::vector<uint8_t> header;  // host staging copy of the header
+};
+
+namespace {
+
+uint64_t ru256(uint64_t x) { return (x + 255) / 256 * 256; }
+uint64_t tile_stride(int n, int dk, int dv) {
+  uint64_t b = (uint64_t)dk * dv * n / 8 + (n == 16 ? 0 : 2ull * (dk + dv));
+  return ru256(b);
+}
+
+bool desc_ok(const stq_pool_desc* d) {
+  if (!d || d->n_slots < 1 || d->n_heads < 1 || d->n_heads > 4096) return false;
+  if (!((d->d_k == 64 || d->d_k == 128) && (d->d_v == 64 || d->d_v == 128))) return false;
+  if (d->gate_kind != STQ_GATE_HEAD && d->gate_kind != STQ_GATE_CHANNEL) return false;
+  if (d->unit_kind != STQ_UNIT_HEAD && d->unit_kind != STQ_UNIT_ROW) return false;
+  if (d->window < 0 || d->window > 32) return false;
+  if (!d->unit_bits || !d->row_weight) return false;
+  const int nb = d->unit_kind == STQ_UNIT_ROW ? d->n_heads * d->d_k : d->n_heads;
+  for (int i = 0; i < nb; i++) {
+    int b = d->unit_bits[i];
+    if (b != 4 && b != 6 && b != 8 && b != 16) return false;
+  }
+  for (long i = 0; i < (long)d->n_heads * d->d_k; i++) {
+    float w = d->row_weight[i];
+    if (!(w > 0.f) || !(w < 3.0e38f)) return false;
+  }
+  return true;
+}
+
+void layout(const stq_pool_desc* d, stq_pool* p) {
+  p->n_slots = d->n_slots; p->H = d->n_heads; p->dk = d->d_k; p->dv = d->d_v;
+  p->gate = d->gate_kind; p->unit = d->unit_kind; p->W = d->window;
+  p->bits.assign(d->unit_bits, d->unit_bits + d->n_heads);
+  p->head_off.resize(d->n_heads);
+  uint64_t s = 0;
+  for (int h = 0; h < d->n_heads; h++) { p->head_off[h] = (uint32_t)s; s += tile_stride(p->bits[h], p->dk, p->dv); }
+  p->slot_bytes = s;
+  p->woff = ru256(64 + 8ull * p->H);
+  p->hdr = ru256(p->woff + 4ull * p->H * p->dk);
+  p->slots_off = p->hdr;
+  p->cache_off = p->slots_off + (uint64_t)p->n_slots * p->slot_bytes;
+  p->cache_stride = p->W ? 256 + 4ull * p->W * (p->dk + p->dv) : 0;
+  p->total = p->cache_off + (uint64_t)p->n_slots * p->H * p->cache_stride;
+}
+
+void put32(uint8_t* b, uint32_t v) { memcpy(b, &v, 4); }
+void put64(uint8_t* b, uint64_t v) { memcpy(b, &v, 8); }
+
+KArgs base_args(const stq_pool* p, const int32_t* slots, int n) {
+  KArgs A;
+  memset(&A, 0, sizeof(A));
+  A.pool = p->dev;
+  A.slots = slots;
+  A.n = n; A.H = p->H; A.n_slots = p->n_slots; A.gate = p->gate; A.W = p->W;
+  A.slots_off = p->slots_off; A.slot_bytes = p->slot_bytes;
+  A.cache_off = p->cache_off; A.cache_stride = p->cache_stride;
+  A.head_bits = (const int32_t*)(p->dev + 64);
+  A.head_off = (const uint32_t*)(p->dev + 64 + 4 * p->H);
+  A.weights = (const float*)(p->dev + p->woff);
+  return A;
+}
+
+unsigned grid_of(int n, int H) {
+  long T = (long)n * H;
+  return (unsigned)(((T + 7) / 8) * 8);
+}
+
+template <template <int, int> class L>
+stq_status dispatch(const stq_pool* p, const KArgs& A, hipStream_t st) {
+  const unsigned g = grid_of(A.n, A.H);
+  if (p->dk == 128 && p->dv == 128) L<128, 128>::go(A, g, st);
+  else if (p->dk == 64 && p->dv == 64) L<64, 64>::go(A, g, st);
+  else if (p->dk == 64 && p->dv == 128) L<64, 128>::go(A, g, st);
+  else L<128, 64>::go(A, g, st);
+  return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
+}
+
+template <int MODE>
+struct LTile {
+  template <int DK, int DV>
+  struct T {
+    static void go(const KArgs& A, unsigned g, hipStream_t st) {
+      hipLaunchKernelGGL((k_tile<DK, DV, MODE>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
+    }
+  };
+};
+template <bool FLUSH>
+struct LWindow {
+  template <int DK, int DV>
+  struct T {
+    static void go(const KArgs& A, unsigned g, hipStream_t st) {
+      hipLaunchKernelGGL((k_window<DK, DV, FLUSH>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
+    }
+  };
+};
+template <bool REQ>
+struct LFetch {
+  template <int DK, int DV>
+  struct T {
+    static void go(const KArgs& A, unsigned g, hipStream_t st) {
+      hipLaunchKernelGGL((k_fetch<DK, DV, REQ>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
+    }
+  };
+};
+
+stq_status check_call(const stq_pool* p, const int32_t* slots, int32_t n) {
+  if (!p) return STQ_ERR_ARG;
+  if (n < 0 || n > p->n_slots) return STQ_ERR_ARG;
+  if (n > 0 && !slots) return STQ_ERR_ARG;
+  return STQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* stq_status_str(stq_status s) {
+  switch (s) {
+    case STQ_OK: return "STQ_OK";
+    case STQ_ERR_ARG: return "STQ_ERR_ARG: invalid argument or descriptor";
+    case STQ_ERR_LAYOUT: return "STQ_ERR_LAYOUT: buffer too small or misaligned";
+    case STQ_ERR_HIP: return "STQ_ERR_HIP: HIP runtime or launch failure";
+    case STQ_ERR_STATE: return "STQ_ERR_STATE: call not valid for this pool";
+    case STQ_ERR_UNSUPPORTED: return "STQ_ERR_UNSUPPORTED: not implemented in this build";
+    default: return "unknown stq_status";
+  }
+}
+
+size_t stq_pool_bytes(const stq_pool_desc* d) {
+  if (!desc_ok(d) || d->unit_kind != STQ_UNIT_HEAD) return 0;
+  stq_pool p;
+  layout(d, &p);
+  return (size_t)p.total;
+}
+
+stq_status stq_pool_create(const stq_pool_desc* d, void* dev_buf, size_t bytes, hipStream_t stream,
+                           stq_pool** out) {
+  if (!out) return STQ_ERR_ARG;
+  *out = nullptr;
+  if (!desc_ok(d)) return STQ_ERR_ARG;
+  if (d->unit_kind != STQ_UNIT_HEAD) return STQ_ERR_UNSUPPORTED;
+  if (d->window > 0 && d->gate_kind != STQ_GATE_HEAD) return STQ_ERR_UNSUPPORTED;
+  if (!dev_buf || ((uintptr_t)dev_buf & 255u)) return STQ_ERR_LAYOUT;
+  stq_pool* p = new (std::nothrow) stq_pool;
+  if (!p) return STQ_ERR_ARG;
+  layout(d, p);
+  if (bytes < p->total) { delete p; return STQ_ERR_LAYOUT; }
+  p->dev = (uint8_t*)dev_buf;
+  p->header.assign(p->hdr, 0);
+  uint8_t* hb = p->header.data();
+  put32(hb + 0, 0x31515453u);
+  put32(hb + 4, p->n_slots); put32(hb + 8, p->H); put32(hb + 12, p->dk); put32(hb + 16, p->dv);
+  put32(hb + 20, p->gate); put32(hb + 24, p->unit); put32(hb + 28, p->W);
+  put64(hb + 32, p->slot_bytes); put64(hb + 40, p->slots_off); put64(hb + 48, p->cache_off);
+  put64(hb + 56, p->cache_stride);
+  for (int h = 0; h < p->H; h++) {
+    put32(hb + 64 + 4 * h, (uint32_t)p->bits[h]);
+    put32(hb + 64 + 4 * p->H + 4 * h, p->head_off[h]);
+  }
+  memcpy(hb + p->woff, d->row_weight, 4ull * p->H * p->dk);
+  if (hipMemcpyAsync(p->dev, hb, p->hdr, hipMemcpyHostToDevice, stream) != hipSuccess) {
+    delete p;
+    return STQ_ERR_HIP;
+  }
+  // zero state in every slot (codes 0, scales 1) and empty windows
+  KArgs A = base_args(p, nullptr, p->n_slots);
+  stq_status s = dispatch<LTile<MODE_STORE>::T>(p, A, stream);
+  if (s != STQ_OK) { delete p; return s; }
+  *out = p;
+  return STQ_OK;
+}
+
+stq_status stq_pool_destroy(stq_pool* p) {
+  if (!p) return STQ_ERR_ARG;
+  delete p;
+  return STQ_OK;
+}
+
+stq_status stq_pool_store(stq_pool* p, const int32_t* slots, int32_t n, const float* S, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (n == 0) return STQ_OK;
+  if (!S) return STQ_ERR_ARG;
+  KArgs A = base_args(p, slots, n);
+  A.S_in = S;
+  return dispatch<LTile<MODE_STORE>::T>(p, A, st);
+}
+
+stq_status stq_pool_fetch(const stq_pool* p, const int32_t* slots, int32_t n, float* S, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (n == 0) return STQ_OK;
+  if (!S) return STQ_ERR_ARG;
+  KArgs A = base_args(p, slots, n);
+  A.S_out = S;
+  return dispatch<LFetch<false>::T>(p, A, st);
+}
+
+stq_status stq_requant_fixed_scales(stq_pool* p, const int32_t* slots, int32_t n, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (n == 0) return STQ_OK;
+  KArgs A = base_args(p, slots, n);
+  return dispatch<LFetch<true>::T>(p, A, st);
+}
+
+stq_status stq_decode_step(stq_pool* p, const int32_t* slots, int32_t n, const float* q, const float* k,
+                           const float* v, const float* a, const float* b, float* o, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (n == 0) return STQ_OK;
+  if (!q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
+  KArgs A = base_args(p, slots, n);
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  if (p->W > 0) return dispatch<LWindow<false>::T>(p, A, st);
+  return dispatch<LTile<MODE_STEP>::T>(p, A, st);
+}
+
+stq_status stq_window_flush(stq_pool* p, const int32_t* slots, int32_t n, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (p->W == 0) return STQ_ERR_STATE;
+  if (n == 0) return STQ_OK;
+  KArgs A = base_args(p, slots, n);
+  return dispatch<LWindow<true>::T>(p, A, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry
+point declared in include/stq.h, sizes pools like the (independent) oracle,
+and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "stq.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(stq_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def stq():
+    import quantized_linear_attention_amd as q
+    return q
+
+
+def test_exports_every_declared_symbol(stq):
+    names = _declared()
+    assert "stq_decode_step" in names and "stq_window_flush" in names and "stq_pool_create" in names
+    lib = ctypes.CDLL(stq.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("key,B", [("C1", 4), ("C2", 64), ("C3", 512), ("C5", 512)])
+def test_pool_bytes_agree_with_oracle(stq, orc, key, B):
+    from workloads import Workload
+    wl = Workload(key, B=B)
+    d = stq.make_desc(B, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, wl.cfg.gate, wl.cfg.unit,
+                      wl.cfg.window)
+    P = orc.OraclePool(B, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, wl.cfg.gate, wl.cfg.unit,
+                       wl.cfg.window)
+    assert stq.stq_pool_bytes(d) == P.nbytes
+
+
+def test_c3_pool_size(stq):
+    from workloads import Workload
+    wl = Workload("C3")
+    d = stq.make_desc(512, 32, 128, 128, wl.bits, wl.row_weight)
+    n = stq.stq_pool_bytes(d)
+    assert n - 512 * 417280 < 64 * 1024                 # header is small
+    assert 512 * 417280 == 213647360                    # 213.6 MB of packed state
+
+
+def test_invalid_descriptors(stq):
+    ok = dict(n_slots=2, n_heads=2, d_k=128, d_v=128, unit_bits=[6, 6], row_weight=np.ones(256))
+    assert stq.stq_pool_bytes(stq.make_desc(**ok)) > 0
+    bad = [dict(ok, n_slots=0), dict(ok, d_k=96), dict(ok, d_v=32), dict(ok, unit_bits=[6, 5]),
+           dict(ok, row_weight=np.r_[np.ones(255), 0.0]), dict(ok, row_weight=np.r_[np.ones(255), np.nan]),
+           dict(ok, window=64), dict(ok, gate_kind=3)]
+    for b in bad:
+        assert stq.stq_pool_bytes(stq.make_desc(**b)) == 0
+
+
+def test_create_rejects_on_host(stq):
+    lib = ctypes.CDLL(stq.library_path())
+    lib.stq_pool_create.restype = ctypes.c_int32
+    d = stq.make_desc(2, 2, 128, 128, [6, 6], np.ones(256))
+    out = ctypes.c_void_p()
+    need = stq.stq_pool_bytes(d)
+    # misaligned device pointer / too small: layout errors, nothing enqueued
+    r = lib.stq_pool_create(ctypes.byref(d), ctypes.c_void_p(0x1001), ctypes.c_size_t(need), None, ctypes.byref(out))
+    assert r == -2 and not out.value
+    r = lib.stq_pool_create(ctypes.byref(d), ctypes.c_void_p(0x10000), ctypes.c_size_t(need - 1), None, ctypes.byref(out))
+    assert r == -2
+    bad = stq.make_desc(2, 2, 128, 128, [6, 7], np.ones(256))
+    r = lib.stq_pool_create(ctypes.byref(bad), ctypes.c_void_p(0x10000), ctypes.c_size_t(need), None, ctypes.byref(out))
+    assert r == -1
+    assert "LAYOUT" in stq.stq_status_str(-2)

@@ -1,0 +1,271 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar (written here): store/fetch/fixed-scale requantization bit-exact; fused
+step: code mismatch rate <= 1e-4 with every mismatch <= 1 code step, readout
+within 1e-3 relative (per element, with a floor of 1% of the tile's largest
+output), checked teacher-forced (the oracle steps from the GPU's bytes)."""
+import numpy as np
+import pytest
+
+from gpu_util import Pair, compare_codes, readout_ok, say
+from workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+MISMATCH_MAX = 1e-4
+
+# (config, B, slot-pool size, slot permutation seed): ragged request counts
+STORE_CASES = [("C1", 4, 4), ("C2", 64, 64), ("C3", 37, 50), ("C5", 21, 24)]
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+@pytest.mark.parametrize("key,B,NS", STORE_CASES)
+def test_create_and_store_bitexact(torch_cuda, orc, key, B, NS):
+    say("case store", key, B, NS)
+    wl = Workload(key, B=B)
+    P = Pair(orc, wl, n_slots=NS)
+    np.testing.assert_array_equal(P.image(), P.ref.img)          # header + zero state
+    slots = np.random.default_rng(1).permutation(NS)[:B]
+    P.store(slots, wl.state(slots))
+    g = P.image()
+    diff = np.nonzero(g != P.ref.img)[0]
+    assert diff.size == 0, "first differing bytes at %s" % diff[:10]
+
+
+@pytest.mark.parametrize("key,B,NS", STORE_CASES)
+def test_fetch_and_fixed_requant_exact(torch_cuda, orc, key, B, NS):
+    say("case fetch", key, B, NS)
+    torch = torch_cuda
+    wl = Workload(key, B=B)
+    P = Pair(orc, wl, n_slots=NS)
+    slots = np.arange(NS)[::-1][:B].copy()
+    P.store(slots, wl.state(slots))
+    out = torch.empty((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    P.stq.stq_pool_fetch(P.pool, P.slots_t(slots), out)
+    np.testing.assert_array_equal(out.cpu().numpy(), P.ref.fetch(slots))
+    before = P.image()
+    P.stq.stq_requant_fixed_scales(P.pool, P.slots_t(slots))
+    np.testing.assert_array_equal(P.image(), before)
+
+
+@pytest.mark.parametrize("key", ["C1", "C2"])
+def test_identity_update_keeps_bytes(torch_cuda, orc, key):
+    say("case identity", key)
+    wl = Workload(key, B=min(16, Workload(key).B))
+    P = Pair(orc, wl)
+    slots = np.arange(wl.B)
+    P.store(slots, wl.state(slots))
+    before = P.image()
+    q, k, v, a, b = wl.token(0)
+    o = P.gpu_step(slots, q, k, v, np.ones_like(a), np.zeros_like(b))
+    np.testing.assert_array_equal(P.image(), before)
+    o_ref = P.ref.step(slots, q, k, v, np.ones_like(a), np.zeros_like(b))
+    assert readout_ok(o, o_ref) <= 1.0
+
+
+def _assert_codes(r):
+    """Stored codes = integer codes of the quantized units + binary16 values of
+    the pivot units.  Bar: combined mismatch <= 1e-4, integer codes <= 1e-4,
+    every mismatch one step (one code, or one binary16 rounding).  A binary16
+    grid is ~2^11 levels per binade, so binary32-vs-binary64 arithmetic alone
+    flips ~1e-4 of pivot values by one ulp: those are bounded at 1e-3."""
+    assert (r["mism"] + r["piv_mism"]) <= MISMATCH_MAX * max(r["codes"] + r["piv"], 1)
+    assert r["mism"] <= MISMATCH_MAX * max(r["codes"], 1)
+    assert r["maxd"] <= 1
+    assert r["piv_mism"] <= 1e-3 * max(r["piv"], 1)
+    assert r["piv_bad"] == 0
+
+
+def _teacher_forced(orc, wl, P, slots, T):
+    worst = dict(mism=0, codes=0, maxd=0, scale_mism=0, scales=0, piv_bad=0, piv=0, piv_mism=0, o=0.0)
+    for t in range(T):
+        img = P.image()
+        ref = orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight,
+                             wl.cfg.gate, wl.cfg.unit, wl.cfg.window, image=img)
+        q, k, v, a, b = wl.token(t, len(slots))
+        o = P.gpu_step(slots, q, k, v, a, b)
+        o_ref = ref.step(slots, q, k, v, a, b)
+        r = compare_codes(orc, ref, P.image(), ref.img, slots)
+        for key in ("mism", "codes", "scale_mism", "scales", "piv_bad", "piv", "piv_mism"):
+            worst[key] += r[key]
+        worst["maxd"] = max(worst["maxd"], r["maxd"])
+        worst["o"] = max(worst["o"], readout_ok(o, o_ref))
+    return worst
+
+
+@pytest.mark.parametrize("key,B,T", [("C1", 4, 32), ("C2", 64, 1), ("C3", 40, 4)])
+def test_fused_step_teacher_forced(torch_cuda, orc, key, B, T):
+    say("case step", key, B, T)
+    wl = Workload(key, B=B)
+    P = Pair(orc, wl, n_slots=B + 3)
+    slots = np.random.default_rng(2).permutation(B + 3)[:B]
+    P.store(slots, wl.state(slots))
+    r = _teacher_forced(orc, wl, P, slots, T)
+    rate = r["mism"] / max(r["codes"], 1)
+    say("  code mismatch %.2e (%d of %d), max |dQ| %d, scale mismatch %d of %d, pivot mismatch %d "
+        "(beyond one step: %d) of %d, readout err/bound %.3f"
+        % (rate, r["mism"], r["codes"], r["maxd"], r["scale_mism"], r["scales"], r["piv_mism"],
+           r["piv_bad"], r["piv"], r["o"]))
+    _assert_codes(r)
+    assert r["o"] <= 1.0
+
+
+def test_full_c3_step_sampled(torch_cuda, orc):
+    """B = 512, H = 32, d = 128 (the benchmark shape, same launch): one step,
+    512 sampled tiles re-stepped by the oracle from the GPU's bytes."""
+    say("case full C3 sampled")
+    wl = Workload("C3")
+    P = Pair(orc, wl)
+    slots = np.arange(512)
+    P.store(slots, wl.state(slots))
+    pre = P.image()
+    q, k, v, a, b = wl.token(0)
+    o = P.gpu_step(slots, q, k, v, a, b)
+    post = P.image()
+    rng = np.random.default_rng(11)
+    samp = rng.choice(512, 16, replace=False)
+    ref = orc.OraclePool(512, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, image=pre)
+    o_ref = ref.step(samp, q[samp], k[samp], v[samp], a[samp], b[samp])
+    r = compare_codes(orc, ref, post, ref.img, samp)
+    rate = r["mism"] / r["codes"]
+    say("  sampled code mismatch %.2e, max |dQ| %d, pivot mismatch %d of %d, readout %.3f"
+        % (rate, r["maxd"], r["piv_mism"], r["piv"], readout_ok(o[samp], o_ref)))
+    _assert_codes(r)
+    assert readout_ok(o[samp], o_ref) <= 1.0
+    # untouched-by-sample tiles still decode to finite values
+    assert np.isfinite(o).all()
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_other_tile_shapes(torch_cuda, orc, dk, dv):
+    say("case shape", dk, dv)
+    wl = Workload("C2", B=6, H=8)
+    wl.dk, wl.dv = dk, dv
+    wl.row_weight = wl.row_weight[:, :dk].copy()
+    rng = np.random.default_rng(dk + dv)
+    wl.bits = np.array([4, 6, 8, 16, 6, 4, 8, 6], np.int32)
+    P = Pair(orc, wl)
+    slots = np.arange(6)
+    S = (rng.standard_normal((6, 8, dk, dv)) * np.exp(rng.normal(0, 1.5, (1, 8, dk, 1)))).astype(np.float32)
+    P.store(slots, S)
+    np.testing.assert_array_equal(P.image(), P.ref.img)
+    q = rng.standard_normal((6, 8, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((6, 8, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((6, 8, dv))
+    a = rng.uniform(0.9, 1, (6, 8)); b = rng.uniform(0, 1, (6, 8))
+    f = lambda x: x.astype(np.float32)
+    pre = P.image()
+    o = P.gpu_step(slots, f(q), f(k), f(v), f(a), f(b))
+    ref = P.orc.OraclePool(6, 8, dk, dv, wl.bits, wl.row_weight, image=pre)
+    o_ref = ref.step(slots, f(q), f(k), f(v), f(a), f(b))
+    r = compare_codes(orc, ref, P.image(), ref.img, slots)
+    assert r["mism"] / r["codes"] <= 1e-3 and r["maxd"] <= 1
+    assert readout_ok(o, o_ref) <= 1.0
+
+
+def test_empty_and_out_of_range(torch_cuda, orc):
+    say("case edges")
+    torch = torch_cuda
+    wl = Workload("C1", B=4)
+    P = Pair(orc, wl)
+    P.store(np.arange(4), wl.state(np.arange(4)))
+    before = P.image()
+    z = torch.empty(0, dtype=torch.int32, device="cuda")
+    e = torch.empty(0, dtype=torch.float32, device="cuda")
+    P.stq.stq_decode_step(P.pool, z, e, e, e, e, e, e)
+    P.stq.stq_pool_store(P.pool, z, e)
+    np.testing.assert_array_equal(P.image(), before)
+    # a slot index outside the pool is skipped on the device
+    q, k, v, a, b = wl.token(0, 2)
+    P.gpu_step(np.array([7, 99]), q, k, v, a, b)
+    np.testing.assert_array_equal(P.image(), before)
+
+
+def _cache_view(ref, img, slot, h):
+    """(count, G[W], K[W][dk], U[W][dv]) of one tile's window cache."""
+    offs, sb = ref.head_offsets()
+    stride = 256 + 4 * ref.W * (ref.dk + ref.dv)
+    base = ref.hdr_bytes() + ref.n_slots * sb + (slot * ref.H + h) * stride
+    c = img[base: base + stride]
+    cnt = int(c[:4].view(np.int32)[0])
+    G = c[4: 4 + 4 * ref.W].view(np.float32)
+    K = c[256: 256 + 4 * ref.W * ref.dk].view(np.float32).reshape(ref.W, ref.dk)
+    U = c[256 + 4 * ref.W * ref.dk: stride].view(np.float32).reshape(ref.W, ref.dv)
+    return cnt, G, K, U
+
+
+@pytest.mark.parametrize("W,T", [(16, 19), (4, 9)])
+def test_window_teacher_forced(torch_cuda, orc, W, T):
+    """Window mode (4-bit base frozen inside the window, fp32 cache, fold after
+    token W): the oracle steps from the GPU's bytes at every token."""
+    say("case window", W, T)
+    wl = Workload("C5", B=24)
+    P = Pair(orc, wl, n_slots=26, window=W)
+    slots = np.random.default_rng(3).permutation(26)[:24]
+    P.store(slots, wl.state(slots))
+    agg = dict(mism=0, codes=0, maxd=0, scale_mism=0, scales=0, piv_bad=0, piv=0, piv_mism=0)
+    worst_o = worst_u = 0.0
+    for t in range(T):
+        img = P.image()
+        ref = orc.OraclePool(26, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, window=W, image=img)
+        q, k, v, a, b = wl.token(t, 24)
+        o = P.gpu_step(slots, q, k, v, a, b)
+        o_ref = ref.step(slots, q, k, v, a, b)
+        post = P.image()
+        worst_o = max(worst_o, readout_ok(o, o_ref))
+        for s in slots[:6]:
+            for h in range(wl.H):
+                cg, Gg, Kg, Ug = _cache_view(ref, post, int(s), h)
+                cr, Gr, Kr, Ur = _cache_view(ref, ref.img, int(s), h)
+                assert cg == cr == (t + 1) % W
+                np.testing.assert_array_equal(Gg[:cg], Gr[:cr])
+                np.testing.assert_array_equal(Kg[:cg], Kr[:cr])
+                if cg:
+                    scale = np.abs(Ur[:cg]).max()
+                    worst_u = max(worst_u, float(np.abs(Ug[:cg] - Ur[:cr]).max() / scale))
+        if (t + 1) % W == 0:                  # a fold happened: compare the new base
+            r = compare_codes(orc, ref, post, ref.img, slots)
+            for key in agg:
+                agg[key] = max(agg[key], r[key]) if key == "maxd" else agg[key] + r[key]
+        else:                                 # base frozen: bytes of the tiles unchanged
+            for s in slots[:4]:
+                for h in range(wl.H):
+                    np.testing.assert_array_equal(ref.tile_view(int(s), h, post), ref.tile_view(int(s), h, img))
+    say("  window W=%d: readout %.3f, cache u rel err %.2e, fold code mismatch %d of %d (max |dQ| %d)"
+        % (W, worst_o, worst_u, agg["mism"], agg["codes"], agg["maxd"]))
+    assert worst_o <= 1.0
+    assert worst_u <= 1e-4
+    _assert_codes(agg)
+
+
+def test_window_flush(torch_cuda, orc):
+    say("case window flush")
+    W = 16
+    wl = Workload("C5", B=8)
+    P = Pair(orc, wl, window=W)
+    slots = np.arange(8)
+    P.store(slots, wl.state(slots))
+    before = P.image()
+    P.stq.stq_window_flush(P.pool, P.slots_t(slots))         # empty windows: no-op
+    np.testing.assert_array_equal(P.image(), before)
+    for t in range(5):
+        P.gpu_step(slots, *wl.token(t, 8))
+    img = P.image()
+    ref = orc.OraclePool(8, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, window=W, image=img)
+    part = np.array([1, 4, 6])
+    P.stq.stq_window_flush(P.pool, P.slots_t(part))
+    ref.window_flush(part)
+    post = P.image()
+    r = compare_codes(orc, ref, post, ref.img, part)
+    _assert_codes(r)
+    for s in part:
+        assert _cache_view(ref, post, int(s), 0)[0] == 0
+    for s in (0, 2, 3, 5, 7):                                   # untouched slots keep their window
+        assert _cache_view(ref, post, int(s), 0)[0] == 5
+        np.testing.assert_array_equal(ref.tile_view(int(s), 0, post), ref.tile_view(int(s), 0, img))
