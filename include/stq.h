@@ -244,6 +244,12 @@ stq_status stq_window_flush(stq_pool* pool, const int32_t* slots_dev, int32_t n,
 stq_status stq_requant_fixed_scales(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                                     hipStream_t stream);
 
+/* Diagnostic: out_dev[b] (fp32 [65536]) := the kernels' correctly rounded
+ * reciprocal of the bf16 value with bit pattern b (meaningful for positive
+ * normal values whose reciprocal is normal).  Used by the tests to check the
+ * device reciprocal exhaustively against IEEE division. */
+stq_status stq_debug_rcp_bf16(float* out_dev, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

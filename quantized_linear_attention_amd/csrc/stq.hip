@@ -46,6 +46,7 @@ struct Smem {
   float rowh[DK] __attribute__((aligned(16)));    // new X factor per row
   float part[Geo<DK, DV>::NP * DK] __attribute__((aligned(16)));
   float kqp[Geo<DK, DV>::NW];
+  int notone[Geo<DK, DV>::NW];     // per wave: some gate of the tile differs from 1
   int esum[Geo<DK, DV>::NW];
   int ecnt[Geo<DK, DV>::NW];
 };
@@ -63,7 +64,7 @@ __device__ __forceinline__ int tile_of_block(int T) {
 // elements (g_i in sm.gg, visible after the next barrier); for a binary16
 // pivot tile Y holds S' itself.  Writes codes, row and column scales.
 // ------------------------------------------------------------------------
-template <int DK, int DV, int N>
+template <int DK, int DV, int N, bool EXACT>
 __device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, float* Y, uint8_t* tile, int h) {
   using G = Geo<DK, DV>;
   constexpr int K = N / 2;
@@ -99,26 +100,28 @@ __device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, fl
       *(f32x4*)&sm.part[(w * G::CBW + cb) * DK + rb * 16 + 4 * r4] = m4;
     }
     __syncthreads();
-    float mx = 0.f;
+    uint32_t mxb = 0u;                              // non-negative: compare bit patterns
 #pragma unroll
-    for (int p = 0; p < G::NP / G::TPR; p++) mx = __builtin_fmaxf(mx, sm.part[(rsub * (G::NP / G::TPR) + p) * DK + rho]);
-    if (G::TPR == 2) mx = __builtin_fmaxf(mx, dpp<0xB1>(mx));
+    for (int p = 0; p < G::NP / G::TPR; p++)
+      mxb = __builtin_elementwise_max(mxb, __float_as_uint(sm.part[(rsub * (G::NP / G::TPR) + p) * DK + rho]));
+    if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
+    const float mx = __uint_as_float(mxb);
     const float g = sm.gg[rho];
     const float m = g * mx;                        // row absmax of S'
     const float pw = m * A.weights[(size_t)h * DK + irow];
     uint32_t s = 0x3F80u;
-    int e = 0, cnt = 0;
+    int epk = 0;                                   // exponent sum * 256 + row count
     if (pw > 0.f) {
-      s = bf16_rne(__builtin_sqrtf(pw));          // correctly rounded sqrt
-      e = (int)((s >> 7) & 0xFFu) - 127;
-      cnt = 1;
+      // ingest: correctly rounded sqrt (bit-exact refit); decode step: v_sqrt
+      // (1 ulp), which can move a row scale by one bf16 step in rare rows
+      s = bf16_rne(EXACT ? __builtin_sqrtf(pw) : __builtin_amdgcn_sqrtf(pw));
+      epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
     }
-    if (rsub != 0) { e = 0; cnt = 0; }
-    const float rs = 1.0f / bf16f(s);             // IEEE division
+    if (rsub != 0) epk = 0;
+    const float rs = rcp_bf16(bf16f(s));          // correctly rounded
     if (rsub == 0) sm.rowh[rho] = g * rs;
-    e = wave_sum_i(e);
-    cnt = wave_sum_i(cnt);
-    if (l == 0) { sm.esum[w] = e; sm.ecnt[w] = cnt; }
+    epk = wave_sum_i(epk);
+    if (l == 0) { sm.esum[w] = epk >> 8; sm.ecnt[w] = epk & 0xFF; }
     __syncthreads();
     int es = 0, ec = 0;
 #pragma unroll
@@ -137,21 +140,25 @@ __device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, fl
         Y[4 * r + c] = Y[4 * r + c] * hr[r];
         cm[c] = __builtin_fmaxf(cm[c], __builtin_fabsf(Y[4 * r + c]));
       }
-    float rc[4];
-    uint32_t cst[4];
+    // column scales: lane q of every quad fits column q of its block, then
+    // the four reciprocals are broadcast inside the quad
     constexpr float RQ = 1.0f / (float)Fmt<N>::QMAX;
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      float M = rb_max<G::RB>(cm[c]) * RQ;
-      uint32_t t = 0x3F80u;
-      if (M > 0.f) {
-        t = bf16_ru_pos(M);
-        if (t < 0x0080u) t = 0x0080u;            // at least 2^-126
-      }
-      rc[c] = 1.0f / bf16f(t);
-      cst[c] = bf16_adj(t, E);
+    for (int c = 0; c < 4; c++) cm[c] = rb_max_pos<G::RB>(cm[c]);
+    const int qd = l & 3;
+    const float Mq = (qd == 0 ? cm[0] : qd == 1 ? cm[1] : qd == 2 ? cm[2] : cm[3]) * RQ;
+    uint32_t t = 0x3F80u;
+    if (Mq > 0.f) {
+      t = bf16_ru_pos(Mq);
+      if (t < 0x0080u) t = 0x0080u;              // at least 2^-126
     }
-    if (rb == 0) *(u32x2*)(scl + DK + j0) = u32x2{cst[0] | (cst[1] << 16), cst[2] | (cst[3] << 16)};
+    const float rcq = rcp_bf16(bf16f(t));
+    if (rb < 4) scl[DK + j0 + qd] = (uint16_t)bf16_adj(t, E);
+    float rc[4];
+    rc[0] = quad_bcast<0>(rcq);
+    rc[1] = quad_bcast<1>(rcq);
+    rc[2] = quad_bcast<2>(rcq);
+    rc[3] = quad_bcast<3>(rcq);
     // ---- requantize: nearest code of the exact product, field in the low bits ----
     uint32_t yb[64];
 #pragma unroll
@@ -201,13 +208,17 @@ __device__ __forceinline__ void tile_body(const KArgs& A, Smem<DK, DV>& sm, uint
       float g = ai * sg;
       sm.alpha[rho] = g * kk;
       sm.beta[rho] = g * qq;
-      sm.kappa[rho] = PIV ? kk : kk / g;          // pivots update S' directly
+      sm.kappa[rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(g);   // pivots update S' directly
       sm.gg[rho] = g;
       kq = kk * qq;
     }
     kq = wave_sum(kq);
-    if (l == 0) sm.kqp[w] = kq;
-    const int allone = __syncthreads_and(ai == 1.f);
+    const bool ne1 = __ballot(ai != 1.f) != 0;
+    if (l == 0) { sm.kqp[w] = kq; sm.notone[w] = ne1; }
+    __syncthreads();
+    int allone = 1;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) allone &= !sm.notone[ww];
     // ---- u = A^T k, w = A^T q ----
     unpack<N>(raw, P);
     float al[16], be[16];
@@ -249,6 +260,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, Smem<DK, DV>& sm, uint
     float ka[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&ka[4 * r4] = *(const f32x4*)&sm.kappa[rb * 16 + 4 * r4];
+    opaque(P);
     if constexpr (PIV) {
       // S' = fma(k, delta, g H): two roundings on the way to binary16
       float gr[16];
@@ -291,7 +303,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, Smem<DK, DV>& sm, uint
       for (int off = TB + 16 * tid; off < TS; off += 16 * G::NT) *(u32x4*)(tile + off) = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  refit_store<DK, DV, N>(A, sm, Y, tile, h);
+  refit_store<DK, DV, N, MODE == MODE_STORE>(A, sm, Y, tile, h);
 }
 
 template <int DK, int DV, int MODE>
@@ -466,6 +478,7 @@ __device__ __forceinline__ void window_body(const KArgs& A, Smem<DK, DV>& sm, WS
     if (!fold) return;
   }
   // ---- fold: S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T  ->  refit, window emptied ----
+  opaque(P);
   float Y[64];
 #pragma unroll
   for (int r = 0; r < 64; r++) Y[r] = 0.f;
@@ -496,7 +509,7 @@ __device__ __forceinline__ void window_body(const KArgs& A, Smem<DK, DV>& sm, WS
       for (int c = 0; c < 4; c++) Y[4 * r + c] = __builtin_fmaf(code_at<N>(P, r, c), cc[c], Y[4 * r + c]);
   }
   if (tid == 0) *cntp = 0;
-  refit_store<DK, DV, N>(A, sm, Y, tile, h);
+  refit_store<DK, DV, N, false>(A, sm, Y, tile, h);
 }
 
 template <int DK, int DV, bool FLUSH>
@@ -561,9 +574,9 @@ __device__ __forceinline__ void fetch_body(const KArgs& A, uint8_t* tile, size_t
   } else if constexpr (N != 16) {
     float rs[16], rc[4];
 #pragma unroll
-    for (int r = 0; r < 16; r++) rs[r] = 1.0f / sg[r];
+    for (int r = 0; r < 16; r++) rs[r] = rcp_bf16(sg[r]);
 #pragma unroll
-    for (int c = 0; c < 4; c++) rc[c] = 1.0f / cc[c];
+    for (int c = 0; c < 4; c++) rc[c] = rcp_bf16(cc[c]);
     uint32_t yb[64];
 #pragma unroll
     for (int r = 0; r < 16; r++)
@@ -596,6 +609,11 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_fetch(KArgs A) {
     case 8: fetch_body<DK, DV, 8, REQ>(A, tile, x); break;
     default: fetch_body<DK, DV, 16, REQ>(A, tile, x); break;
   }
+}
+
+__global__ void k_debug_rcp(float* out) {
+  const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < 65536u) out[b] = rcp_bf16(bf16f(b));
 }
 
 }  // namespace
@@ -835,6 +853,12 @@ stq_status stq_window_flush(stq_pool* p, const int32_t* slots, int32_t n, hipStr
   if (n == 0) return STQ_OK;
   KArgs A = base_args(p, slots, n);
   return dispatch<LWindow<true>::T>(p, A, st);
+}
+
+stq_status stq_debug_rcp_bf16(float* out_dev, hipStream_t st) {
+  if (!out_dev) return STQ_ERR_ARG;
+  hipLaunchKernelGGL(k_debug_rcp, dim3(256), dim3(256), 0, st, out_dev);
+  return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
 }
 
 }  // extern "C"

@@ -48,6 +48,20 @@ __device__ __forceinline__ uint32_t bf16_adj(uint32_t b, int k) {
   e = e < 1 ? 1 : (e > 254 ? 254 : e);
   return (b & 0x807Fu) | ((uint32_t)e << 7);
 }
+// Correctly rounded 1/x for x with at most 8 significant bits (every bf16
+// value with a normal reciprocal): v_rcp_f32 (within 1 ulp) and one Newton
+// step leave an error near 2^-45 relative, while 1/x of an 8-bit significand
+// is at least 2^-32 relative away from any binary32 rounding midpoint.
+__device__ __forceinline__ float rcp_bf16(float x) {
+  float r = __builtin_amdgcn_rcpf(x);
+  float e = __builtin_fmaf(-x, r, 1.0f);
+  return __builtin_fmaf(e, r, r);
+}
+// keep a constant in a VGPR (gfx9 VOP3 encodings take no literal and one SGPR)
+__device__ __forceinline__ uint32_t vconst(uint32_t k) {
+  asm volatile("" : "+v"(k));
+  return k;
+}
 // floor((2*s + n) / (2n)), n > 0
 __device__ __forceinline__ int mean_exp(int s, int n) {
   int num = 2 * s + n, den = 2 * n;
@@ -76,22 +90,46 @@ __device__ __forceinline__ float rb_sum(float x) {
   if (RB == 8) x = x + dpp<0x141>(x);
   return x;
 }
+// max over the RB lanes of NON-NEGATIVE floats: their bit patterns order like
+// unsigned integers, so the DPP steps run on v_max_u32 (no NaN canonicalising)
 template <int RB>
-__device__ __forceinline__ float rb_max(float x) {
-  x = __builtin_fmaxf(x, dpp<0xB1>(x));
-  x = __builtin_fmaxf(x, dpp<0x4E>(x));
-  if (RB == 8) x = __builtin_fmaxf(x, dpp<0x141>(x));
-  return x;
+__device__ __forceinline__ float rb_max_pos(float v) {
+  uint32_t x = __float_as_uint(v);
+  x = __builtin_elementwise_max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
+  x = __builtin_elementwise_max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
+  if (RB == 8)
+    x = __builtin_elementwise_max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
+  return __uint_as_float(x);
 }
+// value of lane (quad base + Q) of every quad
+template <int Q>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return dpp<Q * 0x55>(x);
+}
+// Wave-wide sums, uniform result: DPP butterflies inside each 16-lane row,
+// then the four row totals are read out and added in a fixed order.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+  x = x + dpp<0xB1>(x);
+  x = x + dpp<0x4E>(x);
+  x = x + dpp<0x141>(x);
+  x = x + dpp<0x140>(x);
+  const int b = __builtin_bit_cast(int, x);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
 }
 __device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+  x += dppi<0xB1>(x);
+  x += dppi<0x4E>(x);
+  x += dppi<0x141>(x);
+  x += dppi<0x140>(x);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
 }
 
 // ------------------------------------------------------ lane-stream codecs
@@ -124,14 +162,16 @@ __device__ __forceinline__ void unpack(const uint32_t* raw, f16x2* P) {
     }
   } else if constexpr (N == 4) {
     const f16x2 off = {(f16)-1032.0f, (f16)-1032.0f};
+    const uint32_t k64 = vconst(0x64006400u);
 #pragma unroll
     for (int m = 0; m < 8; m++) {
       uint32_t d = raw[m];
 #pragma unroll
-      for (int c = 0; c < 4; c++) P[4 * m + c] = as_h2(((d >> (4 * c)) & 0x000F000Fu) | 0x64006400u) + off;
+      for (int c = 0; c < 4; c++) P[4 * m + c] = as_h2(((d >> (4 * c)) & 0x000F000Fu) | k64) + off;
     }
   } else if constexpr (N == 6) {
     const f16x2 off = {(f16)-1056.0f, (f16)-1056.0f};
+    const uint32_t k64 = vconst(0x64006400u);
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       uint32_t d0 = raw[3 * u], d1 = raw[3 * u + 1], d2 = raw[3 * u + 2];
@@ -147,8 +187,8 @@ __device__ __forceinline__ void unpack(const uint32_t* raw, f16x2* P) {
         u16x2 lo = xv >> (u16x2){0, 4};     // (c0, c2) in bits 0..5 of each half
         u16x2 hi = xv >> (u16x2){6, 10};    // (c1, c3)
         int r = 4 * u + q;
-        P[2 * r] = as_h2((__builtin_bit_cast(uint32_t, lo) & 0x003F003Fu) | 0x64006400u) + off;
-        P[2 * r + 1] = as_h2((__builtin_bit_cast(uint32_t, hi) & 0x003F003Fu) | 0x64006400u) + off;
+        P[2 * r] = as_h2((__builtin_bit_cast(uint32_t, lo) & 0x003F003Fu) | k64) + off;
+        P[2 * r + 1] = as_h2((__builtin_bit_cast(uint32_t, hi) & 0x003F003Fu) | k64) + off;
       }
     }
   } else {
@@ -160,6 +200,12 @@ __device__ __forceinline__ void unpack(const uint32_t* raw, f16x2* P) {
 template <int N>
 __device__ __forceinline__ float code_at(const f16x2* P, int r, int c) {
   return (float)P[preg<N>(r, c)][phalf<N>(r, c)];
+}
+// Make the fp16 pairs opaque so that a later use of a code converts it inside
+// its own v_fma_mix_f32 instead of reusing a materialised binary32 copy.
+__device__ __forceinline__ void opaque(f16x2* P) {
+#pragma unroll
+  for (int k = 0; k < 32; k++) asm volatile("" : "+v"(P[k]));
 }
 
 // y[4r+c]: binary32 bit patterns 2^23 + field (field in the low bits, nothing
