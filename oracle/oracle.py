@@ -12,7 +12,7 @@ _CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fexcess-precision=standard"
            "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
 
 __all__ = ["build", "lib", "refit", "dequant", "requant_fixed", "pack", "unpack",
-           "tile_bytes", "tile_stride", "update_f64", "OraclePool", "num_threads", "clip_events"]
+           "tile_bytes", "tile_stride", "update_f64", "pack_rows", "unpack_rows", "row_tile_bytes", "OraclePool", "num_threads", "clip_events"]
 
 
 def build(force=False):
@@ -43,6 +43,8 @@ def lib():
         L.orc_requant_fixed.argtypes = [I, I, P, P, P, P, P]
         L.orc_pack.argtypes = [I, I, I, P, P, P, P]
         L.orc_unpack.argtypes = [I, I, I, P, P, P, P]
+        L.orc_pack_rows.argtypes = [I, I, P, P, P, P, P]
+        L.orc_unpack_rows.argtypes = [I, I, P, P, P, P, P]
         D = [I, I, I, I, I, I, I, P]
         L.orc_pool_bytes.restype = ctypes.c_size_t
         L.orc_pool_bytes.argtypes = D
@@ -138,6 +140,31 @@ def pack(n, Q, sig, cst):
     return t
 
 
+def row_tile_bytes(nb, dv):
+    return int(sum(dv * int(n) // 8 for n in nb)) + 2 * (len(nb) + dv)
+
+
+def pack_rows(nb, Q, sig, cst):
+    """Row-record tile of a per-row-width head (rows sorted by width)."""
+    Q = _c(Q, np.int32)
+    dk, dv = Q.shape
+    nb = _c(nb, np.int32)
+    t = np.zeros(row_tile_bytes(nb, dv), np.uint8)
+    lib().orc_pack_rows(dk, dv, _p(nb), _p(Q), _p(_c(sig, np.uint16)), _p(_c(cst, np.uint16)), _p(t))
+    return t
+
+
+def unpack_rows(nb, dv, tile):
+    nb = _c(nb, np.int32)
+    dk = nb.size
+    tile = _c(tile, np.uint8)
+    Q = np.zeros((dk, dv), np.int32)
+    sig = np.zeros(dk, np.uint16)
+    cst = np.zeros(dv, np.uint16)
+    lib().orc_unpack_rows(dk, dv, _p(nb), _p(tile), _p(Q), _p(sig), _p(cst))
+    return Q, sig, cst
+
+
 def unpack(n, dk, dv, tile):
     tile = _c(tile, np.uint8)
     Q = np.zeros((dk, dv), np.int32)
@@ -205,18 +232,42 @@ class OraclePool:
 
     # byte views ------------------------------------------------------
     def hdr_bytes(self):
-        woff = (64 + 8 * self.H + 255) // 256 * 256
-        return (woff + 4 * self.H * self.dk + 255) // 256 * 256
+        ru = lambda x: (x + 255) // 256 * 256
+        roff = ru(ru(64 + 8 * self.H) + 4 * self.H * self.dk)
+        if self.unit == 1:
+            return ru(roff + 2 * self.H * self.dk + 16 * self.H)
+        return roff
+
+    def head_bits(self, h):
+        """Width of every row of head h."""
+        if self.unit == 1:
+            return self.bits.reshape(self.H, self.dk)[h]
+        return np.full(self.dk, int(self.bits[h]), np.int32)
+
+    def _tile_bytes(self, h):
+        if self.unit == 1:
+            return row_tile_bytes(self.head_bits(h), self.dv)
+        return tile_bytes(int(self.bits[h]), self.dk, self.dv)
 
     def head_offsets(self):
         offs, s = [], 0
         for h in range(self.H):
             offs.append(s)
-            s += tile_stride(int(self.bits[h]), self.dk, self.dv)
+            s += (self._tile_bytes(h) + 255) // 256 * 256
         return offs, s
 
     def tile_view(self, slot, h, img=None):
         img = self.img if img is None else img
         offs, sb = self.head_offsets()
         base = self.hdr_bytes() + slot * sb + offs[h]
-        return img[base: base + tile_bytes(int(self.bits[h]), self.dk, self.dv)]
+        return img[base: base + self._tile_bytes(h)]
+
+    def decode_tile(self, slot, h, img=None):
+        """(Q, sigma, c, widths) of one tile, rows in original order."""
+        t = self.tile_view(slot, h, img)
+        nb = self.head_bits(h)
+        if self.unit == 1:
+            Q, sg, cs = unpack_rows(nb, self.dv, t)
+        else:
+            Q, sg, cs = unpack(int(self.bits[h]), self.dk, self.dv, t)
+        return Q, sg, cs, nb

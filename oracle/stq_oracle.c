@@ -114,6 +114,12 @@ static uint16_t bf16_adj(uint16_t b, int k) {
 
 static int qmax_of(int n) { return (1 << (n - 1)) - 1; }
 
+typedef struct {
+  int n_slots, H, dk, dv, gate, unit, W;
+  const int32_t* bits;   /* [H] (per-head units) or [H*dk] (per-row units) */
+  const float* wt;       /* [H*dk] */
+} orc_desc;
+
 /* ------------------------------------------------------------------ */
 /* R: refit + quantize one fp32 tile (row-major dk x dv, any shape).    */
 /* nb[i] = width of row i (16 = pivot row).  Outputs: stored sigma[dk],  */
@@ -317,29 +323,107 @@ void orc_unpack(int n, int dk, int dv, const uint8_t* tile, int32_t* Q, uint16_t
     cst[j] = (n == 16) ? 0x3F80 : (uint16_t)(sp[2 * dk + 2 * j] | (sp[2 * dk + 2 * j + 1] << 8));
 }
 
+/* 4 codes of one row (columns 4m..4m+3) as the n/2-byte group encoding */
+static void group_enc(int n, const int32_t* q, uint8_t* out) {
+  int32_t f[4];
+  for (int c = 0; c < 4; c++) f[c] = (n == 16) ? q[c] : q[c] + (1 << (n - 1));
+  if (n == 4) {
+    out[0] = (uint8_t)(f[0] | (f[1] << 4));
+    out[1] = (uint8_t)(f[2] | (f[3] << 4));
+  } else if (n == 6) {
+    uint32_t g = (uint32_t)f[0] | ((uint32_t)f[1] << 6) | ((uint32_t)f[2] << 12) | ((uint32_t)f[3] << 18);
+    out[0] = g & 0xFF; out[1] = (g >> 8) & 0xFF; out[2] = (g >> 16) & 0xFF;
+  } else if (n == 8) {
+    for (int c = 0; c < 4; c++) out[c] = (uint8_t)f[c];
+  } else {
+    for (int c = 0; c < 4; c++) { out[2 * c] = f[c] & 0xFF; out[2 * c + 1] = (f[c] >> 8) & 0xFF; }
+  }
+}
+static void group_dec(int n, const uint8_t* in, int32_t* q) {
+  for (int c = 0; c < 4; c++) {
+    uint32_t f;
+    if (n == 4) f = (c % 2) ? (in[c / 2] >> 4) : (in[c / 2] & 15);
+    else if (n == 6) f = (((uint32_t)in[0] | ((uint32_t)in[1] << 8) | ((uint32_t)in[2] << 16)) >> (6 * c)) & 63;
+    else if (n == 8) f = in[c];
+    else f = (uint32_t)in[2 * c] | ((uint32_t)in[2 * c + 1] << 8);
+    q[c] = (n == 16) ? (int32_t)f : (int32_t)f - (1 << (n - 1));
+  }
+}
+
+/* Row-record tile (per-row widths nb[dk], original row order in Q/sig). */
+void orc_pack_rows(int dk, int dv, const int32_t* nb, const int32_t* Q, const uint16_t* sig,
+                   const uint16_t* cst, uint8_t* tile) {
+  static const int W4[4] = {4, 6, 8, 16};
+  size_t off = 0;
+  for (int k = 0; k < 4; k++)
+    for (int i = 0; i < dk; i++) {
+      if (nb[i] != W4[k]) continue;
+      int n = nb[i];
+      for (int m = 0; m < dv / 4; m++) group_enc(n, Q + (size_t)i * dv + 4 * m, tile + off + (size_t)m * n / 2);
+      off += (size_t)dv * n / 8;
+    }
+  for (int i = 0; i < dk; i++) { tile[off + 2 * i] = sig[i] & 0xFF; tile[off + 2 * i + 1] = sig[i] >> 8; }
+  off += 2 * (size_t)dk;
+  for (int j = 0; j < dv; j++) { tile[off + 2 * j] = cst[j] & 0xFF; tile[off + 2 * j + 1] = cst[j] >> 8; }
+}
+
+void orc_unpack_rows(int dk, int dv, const int32_t* nb, const uint8_t* tile, int32_t* Q, uint16_t* sig,
+                     uint16_t* cst) {
+  static const int W4[4] = {4, 6, 8, 16};
+  size_t off = 0;
+  for (int k = 0; k < 4; k++)
+    for (int i = 0; i < dk; i++) {
+      if (nb[i] != W4[k]) continue;
+      int n = nb[i];
+      for (int m = 0; m < dv / 4; m++) group_dec(n, tile + off + (size_t)m * n / 2, Q + (size_t)i * dv + 4 * m);
+      off += (size_t)dv * n / 8;
+    }
+  for (int i = 0; i < dk; i++) sig[i] = (uint16_t)(tile[off + 2 * i] | (tile[off + 2 * i + 1] << 8));
+  off += 2 * (size_t)dk;
+  for (int j = 0; j < dv; j++) cst[j] = (uint16_t)(tile[off + 2 * j] | (tile[off + 2 * j + 1] << 8));
+}
+
 /* ------------------------------------------------------------------ */
 /* pool image                                                          */
 /* ------------------------------------------------------------------ */
-typedef struct {
-  int n_slots, H, dk, dv, gate, unit, W;
-  const int32_t* bits;   /* [H] */
-  const float* wt;       /* [H*dk] */
-} orc_desc;
 
 static size_t ru256(size_t x) { return (x + 255) / 256 * 256; }
+static size_t woff_of(const orc_desc* d) { return ru256(64 + 8 * (size_t)d->H); }
+static size_t roff_of(const orc_desc* d) { return ru256(woff_of(d) + 4 * (size_t)d->H * d->dk); }
 static size_t hdr_bytes(const orc_desc* d) {
-  size_t woff = ru256(64 + 8 * (size_t)d->H);
-  return ru256(woff + 4 * (size_t)d->H * d->dk);
+  if (d->unit == 1) return ru256(roff_of(d) + 2 * (size_t)d->H * d->dk + 16 * (size_t)d->H);
+  return roff_of(d);
+}
+/* per-row units: a tile holds each row as a record of dv codes at the row's
+ * width (dv*n/8 bytes), rows sorted by width, then sigma[dk], c[dv]. */
+static size_t row_tile_bytes(const orc_desc* d, int h) {
+  size_t b = 0;
+  for (int i = 0; i < d->dk; i++) b += (size_t)d->dv * d->bits[(size_t)h * d->dk + i] / 8;
+  return b + 2 * (size_t)(d->dk + d->dv);
+}
+static size_t tile_stride_h(const orc_desc* d, int h) {
+  return d->unit == 1 ? ru256(row_tile_bytes(d, h)) : orc_tile_stride(d->bits[h], d->dk, d->dv);
 }
 static size_t slot_bytes(const orc_desc* d) {
   size_t s = 0;
-  for (int h = 0; h < d->H; h++) s += orc_tile_stride(d->bits[h], d->dk, d->dv);
+  for (int h = 0; h < d->H; h++) s += tile_stride_h(d, h);
   return s;
 }
 static size_t head_off(const orc_desc* d, int h) {
   size_t s = 0;
-  for (int g = 0; g < h; g++) s += orc_tile_stride(d->bits[g], d->dk, d->dv);
+  for (int g = 0; g < h; g++) s += tile_stride_h(d, g);
   return s;
+}
+/* physical row order of a per-row head: rows sorted by width (4, 6, 8, 16),
+ * original order kept inside a width; perm[p] = original row of record p. */
+static void row_order(const orc_desc* d, int h, int* perm, int* cnt) {
+  static const int W4[4] = {4, 6, 8, 16};
+  int p = 0;
+  for (int k = 0; k < 4; k++) {
+    cnt[k] = 0;
+    for (int i = 0; i < d->dk; i++)
+      if (d->bits[(size_t)h * d->dk + i] == W4[k]) { perm[p++] = i; cnt[k]++; }
+  }
 }
 static size_t cache_stride(const orc_desc* d) {
   return d->W ? 256 + 4 * (size_t)d->W * (d->dk + d->dv) : 0;
@@ -368,11 +452,23 @@ void orc_pool_init(int n_slots, int H, int dk, int dv, int gate, int unit, int W
   put64(img + 32, slot_bytes(&d)); put64(img + 40, hdr_bytes(&d));
   put64(img + 48, cache_off(&d)); put64(img + 56, cache_stride(&d));
   for (int h = 0; h < H; h++) {
-    put32(img + 64 + 4 * h, bits[h]);
+    put32(img + 64 + 4 * h, unit == 1 ? 0 : bits[h]);
     put32(img + 64 + 4 * H + 4 * h, (uint32_t)head_off(&d, h));
   }
-  size_t woff = ru256(64 + 8 * (size_t)H);
-  memcpy(img + woff, wt, 4 * (size_t)H * dk);
+  memcpy(img + woff_of(&d), wt, 4 * (size_t)H * dk);
+  if (unit == 1) {
+    uint8_t* wr = img + roff_of(&d);                 /* widths [H][dk], original order */
+    uint8_t* pr = wr + (size_t)H * dk;               /* perm [H][dk]: record p -> row */
+    uint8_t* cr = pr + (size_t)H * dk;               /* int32 counts [H][4] of 4/6/8/16 */
+    int perm[256], cnt[4];
+    for (int h = 0; h < H; h++) {
+      put32(img + 64 + 4 * h, 0);
+      for (int i = 0; i < dk; i++) wr[(size_t)h * dk + i] = (uint8_t)bits[(size_t)h * dk + i];
+      row_order(&d, h, perm, cnt);
+      for (int p = 0; p < dk; p++) pr[(size_t)h * dk + p] = (uint8_t)perm[p];
+      for (int k = 0; k < 4; k++) put32(cr + 16 * (size_t)h + 4 * k, cnt[k]);
+    }
+  }
   /* zero state: Q = 0 (field 2^(n-1)), scales 1.0; pivot: +0.0 */
   int32_t* Q = (int32_t*)calloc((size_t)dk * dv, sizeof(int32_t));
   uint16_t* sg = (uint16_t*)malloc(2 * dk);
@@ -380,8 +476,11 @@ void orc_pool_init(int n_slots, int H, int dk, int dv, int gate, int unit, int W
   for (int i = 0; i < dk; i++) sg[i] = 0x3F80;
   for (int j = 0; j < dv; j++) cs[j] = 0x3F80;
   for (int s = 0; s < n_slots; s++)
-    for (int h = 0; h < H; h++)
-      orc_pack(bits[h], dk, dv, Q, sg, cs, img + hdr_bytes(&d) + (size_t)s * slot_bytes(&d) + head_off(&d, h));
+    for (int h = 0; h < H; h++) {
+      uint8_t* t = img + hdr_bytes(&d) + (size_t)s * slot_bytes(&d) + head_off(&d, h);
+      if (unit == 1) orc_pack_rows(dk, dv, bits + (size_t)h * dk, Q, sg, cs, t);
+      else orc_pack(bits[h], dk, dv, Q, sg, cs, t);
+    }
   free(Q); free(sg); free(cs);
 }
 
@@ -407,22 +506,27 @@ static scratch_t scratch_new(int dk, int dv) {
 }
 static void scratch_free(scratch_t* t) { free(t->Q); free(t->sg); free(t->cs); free(t->nb); free(t->S); free(t->A); }
 
+static void set_widths(const orc_desc* d, int h, scratch_t* t) {
+  for (int i = 0; i < d->dk; i++) t->nb[i] = d->unit == 1 ? d->bits[(size_t)h * d->dk + i] : d->bits[h];
+}
 static void tile_decode(const orc_desc* d, int h, const uint8_t* tile, scratch_t* t) {
-  int n = d->bits[h];
-  for (int i = 0; i < d->dk; i++) t->nb[i] = n;
-  orc_unpack(n, d->dk, d->dv, tile, t->Q, t->sg, t->cs);
+  set_widths(d, h, t);
+  if (d->unit == 1) orc_unpack_rows(d->dk, d->dv, t->nb, tile, t->Q, t->sg, t->cs);
+  else orc_unpack(d->bits[h], d->dk, d->dv, tile, t->Q, t->sg, t->cs);
   orc_dequant(d->dk, d->dv, t->sg, t->cs, t->Q, t->nb, t->S);
 }
+static void tile_pack(const orc_desc* d, int h, uint8_t* tile, scratch_t* t) {
+  if (d->unit == 1) orc_pack_rows(d->dk, d->dv, t->nb, t->Q, t->sg, t->cs, tile);
+  else orc_pack(d->bits[h], d->dk, d->dv, t->Q, t->sg, t->cs, tile);
+}
 static void tile_encode(const orc_desc* d, int h, const float* S, const float* w, uint8_t* tile, scratch_t* t) {
-  int n = d->bits[h];
-  for (int i = 0; i < d->dk; i++) t->nb[i] = n;
+  set_widths(d, h, t);
   orc_refit(d->dk, d->dv, S, w, t->nb, t->sg, t->cs, t->Q, NULL);
-  orc_pack(n, d->dk, d->dv, t->Q, t->sg, t->cs, tile);
+  tile_pack(d, h, tile, t);
 }
 
 static const float* row_w(const orc_desc* d, const uint8_t* img, int h) {
-  size_t woff = ru256(64 + 8 * (size_t)d->H);
-  return (const float*)(img + woff) + (size_t)h * d->dk;
+  return (const float*)(img + woff_of(d)) + (size_t)h * d->dk;
 }
 #define DESC_ARGS int n_slots, int H, int dk, int dv, int gate, int unit, int W, const int32_t* bits
 #define MKDESC orc_desc d = {n_slots, H, dk, dv, gate, unit, W, bits, NULL}
@@ -470,7 +574,7 @@ void orc_pool_requant_fixed(DESC_ARGS, uint8_t* img, const int32_t* slots, int n
       uint8_t* tp = tile_ptr(&d, img, slots[c], h);
       tile_decode(&d, h, tp, &t);
       orc_requant_fixed(dk, dv, t.S, t.sg, t.cs, t.nb, t.Q);
-      orc_pack(bits[h], dk, dv, t.Q, t.sg, t.cs, tp);
+      tile_pack(&d, h, tp, &t);
     }
     scratch_free(&t);
   }
