@@ -74,6 +74,14 @@
  * k of lane l of wave w sits at code-region offset 16*((w*K + k)*64 + l), so
  * that one 16-byte load per lane reads 1 KiB contiguous per wave.
  *
+ * PER-ROW WIDTHS (unit_kind ROW, the KDA allocation unit = key row, [P4]
+ * "Las dos ideas"): a tile is a list of ROW RECORDS, one per key row, each
+ * the row's d_v codes in column order as 4-code groups of the encoding
+ * above (d_v*n/8 bytes; a binary16 pivot row is d_v binary16 values),
+ * records sorted by width (4, 6, 8, then 16; original order kept within a
+ * width), then sigma[d_k] in original row order and c[d_v].  Pivot rows are
+ * excluded from both scale fits (R2, R5).  Window mode is per-head only.
+ *
  * TILE BYTES: codes (d_k*d_v*n/8 bytes), then for n != 16 the row scales
  * sigma[d_k] and column scales c[d_v] as bf16 little-endian.  Tile stride =
  * tile bytes rounded up to a multiple of 256.  (6-bit, 128x128: 12288 + 512
@@ -134,10 +142,14 @@
  *    [12,16) d_k  [16,20) d_v  [20,24) gate_kind  [24,28) unit_kind
  *    [28,32) window  [32,40) slot_bytes  [40,48) slots_off  [48,56) cache_off
  *    [56,64) cache_stride   (integers little-endian, u64 for the last four)
- *    [64, 64+4H)    int32 width of head h
+ *    [64, 64+4H)    int32 width of head h (0 for per-row units)
  *    [64+4H, 64+8H) uint32 byte offset of head h's tile inside a slot
  *    [WOFF, WOFF+4*H*d_k) fp32 row weights [H][d_k], WOFF = roundup(64+8H,256)
- *    HDR = roundup(WOFF + 4*H*d_k, 256)
+ *    ROFF = roundup(WOFF + 4*H*d_k, 256); per-row units only:
+ *    [ROFF, +H*d_k) uint8 width of row i of head h (original order),
+ *    [+H*d_k, +2H*d_k) uint8 original row of record p, then int32 [H][4]
+ *    counts of rows of width 4, 6, 8, 16;
+ *    HDR = ROFF (per-head units) or roundup(ROFF + 2*H*d_k + 16*H, 256)
  *  slots: slots_off = HDR, slot s at slots_off + s*slot_bytes; head h's tile
  *    at + head_off[h]; head_off = running sum of tile strides.
  *  window caches (window > 0): cache_off = slots_off + n_slots*slot_bytes,
@@ -185,7 +197,7 @@ typedef struct stq_pool_desc {
   int32_t gate_kind;    /* STQ_GATE_HEAD or STQ_GATE_CHANNEL                */
   int32_t unit_kind;    /* STQ_UNIT_HEAD (this build) or STQ_UNIT_ROW       */
   int32_t window;       /* 0 = requantize every token; W in [1,32] = window */
-  const int32_t* unit_bits;  /* [H] widths, each 4, 6, 8 or 16                */
+  const int32_t* unit_bits;  /* [H] (HEAD) or [H][d_k] (ROW): 4, 6, 8 or 16   */
   const float* row_weight;   /* [H][d_k] row-impact weights, finite and > 0   */
 } stq_pool_desc;
 

@@ -31,6 +31,8 @@ struct KArgs {
   const int32_t* head_bits;  // device: header tables
   const uint32_t* head_off;
   const float* weights;      // [H][d_k]
+  const uint8_t* row_perm;   // per-row units: [H][d_k] record -> original row
+  const int32_t* row_cnt;    // per-row units: [H][4] rows of width 4, 6, 8, 16
   const float *q, *k, *v, *a, *b;
   float* o;
   const float* S_in;         // store: [n][H][d_k][d_v] (nullptr: zeros)
@@ -534,6 +536,360 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_window(KArgs A) {
 }
 
 // ------------------------------------------------------------------------
+// Per-key-row widths (unit = key row, KDA).  A tile is a list of row
+// records (d_v codes at the row's width, 4-code groups), sorted by width,
+// then sigma[d_k] (original row order) and c[d_v].  The code region is
+// staged through LDS with 16-byte accesses, so every lane can read its rows'
+// groups whatever the width mix; lanes keep the 16 x 4 ownership of the
+// per-head kernel, over the records' (physical) row order.
+// ------------------------------------------------------------------------
+enum { RMODE_STEP = 0, RMODE_STORE = 1, RMODE_FETCH = 2, RMODE_REQUANT = 3 };
+
+template <int DK, int DV>
+struct RSmem {
+  uint32_t codes[DK * DV / 2];        // staged code region (all-binary16 upper bound)
+  uint32_t rinfo[DK];                 // [rb][r]: record offset << 8 | width
+};
+
+__device__ __forceinline__ void rec_of(int p, const int* cnt, int dv, int& n, int& off) {
+  const int r4 = dv / 2, r6 = 3 * dv / 4, r8 = dv, r16 = 2 * dv;
+  if (p < cnt[0]) { n = 4; off = p * r4; return; }
+  p -= cnt[0];
+  int base = cnt[0] * r4;
+  if (p < cnt[1]) { n = 6; off = base + p * r6; return; }
+  p -= cnt[1]; base += cnt[1] * r6;
+  if (p < cnt[2]) { n = 8; off = base + p * r8; return; }
+  p -= cnt[2]; base += cnt[2] * r8;
+  n = 16; off = base + p * r16;
+}
+
+// 4 codes of one row as two exact fp16 pairs (c0, c1), (c2, c3)
+__device__ __forceinline__ void group_load(const uint8_t* lds, int n, f16x2& p0, f16x2& p1) {
+  const uint32_t k64 = 0x64006400u;
+  if (n == 8) {
+    const uint32_t d = *(const uint32_t*)lds;
+    p0 = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04010400u)) + f16x2{(f16)-1152.f, (f16)-1152.f};
+    p1 = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04030402u)) + f16x2{(f16)-1152.f, (f16)-1152.f};
+  } else if (n == 4) {
+    const uint32_t h = *(const uint16_t*)lds;
+    u16x2 a = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, h, 0x0C000C00u));   // (b0, b0)
+    u16x2 b = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, h, 0x0C010C01u));   // (b1, b1)
+    a = a >> (u16x2){0, 4};
+    b = b >> (u16x2){0, 4};
+    p0 = as_h2((__builtin_bit_cast(uint32_t, a) & 0x000F000Fu) | k64) + f16x2{(f16)-1032.f, (f16)-1032.f};
+    p1 = as_h2((__builtin_bit_cast(uint32_t, b) & 0x000F000Fu) | k64) + f16x2{(f16)-1032.f, (f16)-1032.f};
+  } else if (n == 6) {
+    const uint32_t g = (uint32_t)lds[0] | ((uint32_t)lds[1] << 8) | ((uint32_t)lds[2] << 16);
+    u16x2 a = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, g, 0x01000100u));   // (g[0:16], g[0:16])
+    u16x2 b = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, g, 0x02010201u));   // (g[8:24], g[8:24])
+    a = a >> (u16x2){0, 6};
+    b = b >> (u16x2){4, 10};
+    p0 = as_h2((__builtin_bit_cast(uint32_t, a) & 0x003F003Fu) | k64) + f16x2{(f16)-1056.f, (f16)-1056.f};
+    p1 = as_h2((__builtin_bit_cast(uint32_t, b) & 0x003F003Fu) | k64) + f16x2{(f16)-1056.f, (f16)-1056.f};
+  } else {
+    const u32x2 d = *(const u32x2*)lds;
+    p0 = as_h2(d[0]);
+    p1 = as_h2(d[1]);
+  }
+}
+
+// y[c]: binary32 patterns 2^23 + field (non-pivot) or the binary16 values (pivot)
+__device__ __forceinline__ void group_store(uint8_t* lds, int n, const uint32_t* y, const float* s) {
+  if (n == 8) {
+    const uint32_t t = (y[1] << 8) | y[0], u = (y[3] << 8) | y[2];
+    *(uint32_t*)lds = __builtin_amdgcn_perm(u, t, 0x05040100u);
+  } else if (n == 4) {
+    *(uint16_t*)lds = (uint16_t)(y[0] | (y[1] << 4) | (y[2] << 8) | (y[3] << 12));
+  } else if (n == 6) {
+    const uint32_t g = y[0] | (y[1] << 6) | (y[2] << 12) | (y[3] << 18);
+    lds[0] = (uint8_t)g; lds[1] = (uint8_t)(g >> 8); lds[2] = (uint8_t)(g >> 16);
+  } else {
+    f16x2 a = {(f16)__builtin_fminf(__builtin_fmaxf(s[0], -65504.f), 65504.f),
+               (f16)__builtin_fminf(__builtin_fmaxf(s[1], -65504.f), 65504.f)};
+    f16x2 b = {(f16)__builtin_fminf(__builtin_fmaxf(s[2], -65504.f), 65504.f),
+               (f16)__builtin_fminf(__builtin_fmaxf(s[3], -65504.f), 65504.f)};
+    *(u32x2*)lds = u32x2{h2_bits(a), h2_bits(b)};
+  }
+}
+
+template <int DK, int DV, int MODE>
+__device__ __forceinline__ void rows_body(const KArgs& A, Smem<DK, DV>& sm, RSmem<DK, DV>& rs, uint8_t* tile,
+                                          size_t x, int h) {
+  using G = Geo<DK, DV>;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int rb = l % G::RB, cb = l / G::RB;
+  const int j0 = w * G::CPW + 4 * cb;
+  const int rho = tid / G::TPR, rsub = tid % G::TPR;
+  const int prow = (rho >> 4) + G::RB * (rho & 15);         // physical row of the row stage
+  const uint8_t* perm = A.row_perm + (size_t)h * DK;
+  const int* cntp = A.row_cnt + 4 * h;
+  int cnt[4] = {cntp[0], cntp[1], cntp[2], cntp[3]};
+  const int CB = cnt[0] * (DV / 2) + cnt[1] * (3 * DV / 4) + cnt[2] * DV + cnt[3] * 2 * DV;
+  uint16_t* scl = (uint16_t*)(tile + CB);
+  uint8_t* lds = (uint8_t*)rs.codes;
+  const int irow = perm[prow];                               // original row of the row stage
+  int pn, poff;
+  rec_of(prow, cnt, DV, pn, poff);
+  if (rsub == 0) rs.rinfo[rho] = ((uint32_t)poff << 8) | (uint32_t)pn;
+  if (MODE != RMODE_STORE)
+    for (int off = 16 * tid; off < CB; off += 16 * G::NT) *(u32x4*)(lds + off) = *(const u32x4*)(tile + off);
+
+  float Y[64];
+  float cc[4] = {1.f, 1.f, 1.f, 1.f};
+  uint32_t ri[16];
+  f16x2 P[32];
+  float ka[16];
+  bool vecs_ready = false;
+  if (MODE == RMODE_STEP) {
+    float ai = 1.f, kq = 0.f;
+    if (rsub == 0) {
+      const float kk = A.k[x * DK + irow], qq = A.q[x * DK + irow];
+      ai = A.gate ? A.a[x * DK + irow] : A.a[x];
+      const float sg = pn == 16 ? 1.f : bf16f(scl[irow]);
+      const float g = ai * sg;
+      sm.alpha[rho] = g * kk;
+      sm.beta[rho] = g * qq;
+      sm.kappa[rho] = kk * __builtin_amdgcn_rcpf(g);
+      sm.gg[rho] = g;
+      kq = kk * qq;
+    }
+    kq = wave_sum(kq);
+    const bool ne1 = __ballot(ai != 1.f) != 0;
+    if (l == 0) { sm.kqp[w] = kq; sm.notone[w] = ne1; }
+    vecs_ready = true;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r4 = 0; r4 < 4; r4++) *(u32x4*)&ri[4 * r4] = *(const u32x4*)&rs.rinfo[rb * 16 + 4 * r4];
+  if (MODE != RMODE_STORE) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int n = ri[r] & 0xFF, off = ri[r] >> 8;
+      group_load(lds + off + (j0 / 4) * (n / 2), n, P[2 * r], P[2 * r + 1]);
+    }
+    if (MODE != RMODE_STEP || true) {
+      u32x2 cw = *(const u32x2*)(scl + DK + j0);
+      cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
+      cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
+    }
+  }
+  if (MODE == RMODE_FETCH || MODE == RMODE_REQUANT) {
+    // D: fl(fl(sigma c) Q), pivot rows binary16 -> binary32
+    float* S = A.S_out ? A.S_out + x * DK * DV : nullptr;
+    uint32_t yb[4];
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int n = ri[r] & 0xFF, off = ri[r] >> 8;
+      const int p = rb + G::RB * r;
+      const int i = perm[p];
+      const float sgr = n == 16 ? 1.f : bf16f(scl[i]);
+      float v[4];
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const float qv = (float)P[2 * r + (c >> 1)][c & 1];
+        v[c] = n == 16 ? qv : (sgr * cc[c]) * qv;
+      }
+      if (MODE == RMODE_FETCH) {
+        *(f32x4*)(S + (size_t)i * DV + j0) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        const float rsg = rcp_bf16(sgr);
+        const float mg = n == 4 ? Fmt<4>::MAGIC : n == 6 ? Fmt<6>::MAGIC : Fmt<8>::MAGIC;
+        const float qm = n == 4 ? 7.f : n == 6 ? 31.f : 127.f;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          float q = __builtin_fmaf(v[c] * rsg, rcp_bf16(cc[c]), mg);
+          q = __builtin_fminf(__builtin_fmaxf(q, mg - qm), mg + qm);
+          yb[c] = __float_as_uint(q);
+          sv[c] = v[c];
+        }
+        group_store(lds + off + (j0 / 4) * (n / 2), n, yb, sv);
+      }
+    }
+    if (MODE == RMODE_REQUANT) {
+      __syncthreads();
+      for (int off = 16 * tid; off < CB; off += 16 * G::NT) *(u32x4*)(tile + off) = *(const u32x4*)(lds + off);
+    }
+    return;
+  }
+  if (MODE == RMODE_STEP) {
+    int allone = 1;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) allone &= !sm.notone[ww];
+    float al[16], be[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      *(f32x4*)&al[4 * r4] = *(const f32x4*)&sm.alpha[rb * 16 + 4 * r4];
+      *(f32x4*)&be[4 * r4] = *(const f32x4*)&sm.beta[rb * 16 + 4 * r4];
+    }
+    float U[4] = {0.f, 0.f, 0.f, 0.f}, Wr[4] = {0.f, 0.f, 0.f, 0.f};
+    float Up[4] = {0.f, 0.f, 0.f, 0.f}, Wp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const bool piv = (ri[r] & 0xFF) == 16;
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const float qv = (float)P[2 * r + (c >> 1)][c & 1];
+        if (piv) {
+          Up[c] = __builtin_fmaf(qv, al[r], Up[c]);
+          Wp[c] = __builtin_fmaf(qv, be[r], Wp[c]);
+        } else {
+          U[c] = __builtin_fmaf(qv, al[r], U[c]);
+          Wr[c] = __builtin_fmaf(qv, be[r], Wr[c]);
+        }
+      }
+    }
+    float kqs = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqp[ww];
+    const float bb = A.b[x];
+    const f32x4 vv = *(const f32x4*)(A.v + x * DV + j0);
+    float delta[4];
+    f32x4 ov;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const float u = __builtin_fmaf(cc[c], rb_sum<G::RB>(U[c]), rb_sum<G::RB>(Up[c]));
+      const float wq = __builtin_fmaf(cc[c], rb_sum<G::RB>(Wr[c]), rb_sum<G::RB>(Wp[c]));
+      delta[c] = bb * (vv[c] - u);
+      ov[c] = __builtin_fmaf(delta[c], kqs, wq);
+    }
+    if (rb == 0) *(f32x4*)(A.o + x * DV + j0) = ov;
+    if (bb == 0.f && allone) return;      // identity update: keep the encoding
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&ka[4 * r4] = *(const f32x4*)&sm.kappa[rb * 16 + 4 * r4];
+    opaque(P);
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const bool piv = (ri[r] & 0xFF) == 16;
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        Y[4 * r + c] = __builtin_fmaf((float)P[2 * r + (c >> 1)][c & 1], piv ? 1.f : cc[c], ka[r] * delta[c]);
+    }
+  } else {
+    // store: Y = the given fp32 tile (original row order), g = 1
+    const float* S = A.S_in ? A.S_in + x * DK * DV : nullptr;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int i = perm[rb + G::RB * r];
+      f32x4 s4 = S ? *(const f32x4*)(S + (size_t)i * DV + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; c++) Y[4 * r + c] = s4[c];
+    }
+    if (rsub == 0) sm.gg[rho] = 1.f;
+    if (!A.S_in) {                                          // pool creation: clear the tile padding
+      const int TB = CB + 2 * (DK + DV);
+      const int TS = (TB + 255) / 256 * 256;
+      for (int off = TB + 16 * tid; off < TS; off += 16 * G::NT) *(u32x4*)(tile + off) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  (void)vecs_ready;
+  // ---- refit: pivot rows outside the row and column fits ----
+  float gr[16];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; r4++) {
+    f32x4 m4;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int r = 4 * r4 + q;
+      m4[q] = ((ri[r] & 0xFF) == 16) ? 0.f
+              : __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(Y[4 * r]), __builtin_fabsf(Y[4 * r + 1])),
+                                __builtin_fmaxf(__builtin_fabsf(Y[4 * r + 2]), __builtin_fabsf(Y[4 * r + 3])));
+    }
+    *(f32x4*)&sm.part[(w * G::CBW + cb) * DK + rb * 16 + 4 * r4] = m4;
+  }
+  __syncthreads();
+  uint32_t mxb = 0u;
+#pragma unroll
+  for (int p = 0; p < G::NP / G::TPR; p++)
+    mxb = __builtin_elementwise_max(mxb, __float_as_uint(sm.part[(rsub * (G::NP / G::TPR) + p) * DK + rho]));
+  if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
+  const float g = sm.gg[rho];
+  const float m = g * __uint_as_float(mxb);
+  const float pw = m * A.weights[(size_t)h * DK + irow];
+  uint32_t s = 0x3F80u;
+  int epk = 0;
+  if (pn != 16 && pw > 0.f) {
+    s = bf16_rne(MODE == RMODE_STORE ? __builtin_sqrtf(pw) : __builtin_amdgcn_sqrtf(pw));
+    epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
+  }
+  if (rsub != 0) epk = 0;
+  if (rsub == 0) sm.rowh[rho] = g * rcp_bf16(bf16f(s));
+  epk = wave_sum_i(epk);
+  if (l == 0) { sm.esum[w] = epk >> 8; sm.ecnt[w] = epk & 0xFF; }
+  __syncthreads();
+  int es = 0, ec = 0;
+#pragma unroll
+  for (int ww = 0; ww < G::NW; ww++) { es += sm.esum[ww]; ec += sm.ecnt[ww]; }
+  const int E = ec ? mean_exp(es, ec) : 0;
+  if (rsub == 0) scl[irow] = (uint16_t)bf16_adj(s, -E);
+  float hr[16];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; r4++) {
+    *(f32x4*)&hr[4 * r4] = *(const f32x4*)&sm.rowh[rb * 16 + 4 * r4];
+    *(f32x4*)&gr[4 * r4] = *(const f32x4*)&sm.gg[rb * 16 + 4 * r4];
+  }
+  float cm[4] = {0.f, 0.f, 0.f, 0.f};
+  int nonpiv = 0;
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int n = ri[r] & 0xFF;
+    if (n == 16) continue;
+    nonpiv = 1;
+    const float rq = n == 4 ? 1.0f / 7.0f : n == 6 ? 1.0f / 31.0f : 1.0f / 127.0f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      Y[4 * r + c] = Y[4 * r + c] * hr[r];
+      cm[c] = __builtin_fmaxf(cm[c], __builtin_fabsf(Y[4 * r + c]) * rq);
+    }
+  }
+  // any non-pivot row in the tile?  (count of rows with a width below 16)
+  const int has_np = (cnt[0] + cnt[1] + cnt[2]) > 0;
+  (void)nonpiv;
+#pragma unroll
+  for (int c = 0; c < 4; c++) cm[c] = rb_max_pos<G::RB>(cm[c]);
+  const int qd = l & 3;
+  const float Mq = qd == 0 ? cm[0] : qd == 1 ? cm[1] : qd == 2 ? cm[2] : cm[3];
+  uint32_t t = 0x3F80u;
+  if (has_np && Mq > 0.f) {
+    t = bf16_ru_pos(Mq);
+    if (t < 0x0080u) t = 0x0080u;
+  }
+  const float rcq = rcp_bf16(bf16f(t));
+  if (rb < 4) scl[DK + j0 + qd] = (uint16_t)bf16_adj(t, E);
+  float rc[4] = {quad_bcast<0>(rcq), quad_bcast<1>(rcq), quad_bcast<2>(rcq), quad_bcast<3>(rcq)};
+  __syncthreads();                                  // staged codes are overwritten below
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int n = ri[r] & 0xFF, off = ri[r] >> 8;
+    uint32_t yb[4];
+    float sv[4];
+    const float mg = n == 4 ? Fmt<4>::MAGIC : n == 6 ? Fmt<6>::MAGIC : Fmt<8>::MAGIC;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      yb[c] = __float_as_uint(__builtin_fmaf(Y[4 * r + c], rc[c], mg));
+      sv[c] = gr[r] * Y[4 * r + c];
+    }
+    group_store(lds + off + (j0 / 4) * (n / 2), n, yb, sv);
+  }
+  __syncthreads();
+  for (int off = 16 * tid; off < CB; off += 16 * G::NT) *(u32x4*)(tile + off) = *(const u32x4*)(lds + off);
+}
+
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_rows(KArgs A) {
+  __shared__ Smem<DK, DV> sm;
+  __shared__ RSmem<DK, DV> rs;
+  const int T = A.n * A.H;
+  const int tau = tile_of_block(T);
+  if (tau >= T) return;
+  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int slot = A.slots ? A.slots[ci] : ci;
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+  rows_body<DK, DV, MODE>(A, sm, rs, tile, (size_t)ci * A.H + h, h);
+}
+
+// ------------------------------------------------------------------------
 // Fetch (D) and fixed-scale requantization.
 // ------------------------------------------------------------------------
 template <int DK, int DV, int N, bool REQ>
@@ -623,9 +979,9 @@ __global__ void k_debug_rcp(float* out) {
 // ==========================================================================
 struct stq_pool {
   int32_t n_slots, H, dk, dv, gate, unit, W;
-  std::vector<int32_t> bits;
+  std::vector<int32_t> bits;            // [H] or [H][d_k]
   std::vector<uint32_t> head_off;
-  uint64_t hdr, woff, slot_bytes, slots_off, cache_off, cache_stride, total;
+  uint64_t hdr, woff, roff, slot_bytes, slots_off, cache_off, cache_stride, total;
   uint8_t* dev;
   std::vector<uint8_t> header;  // host staging copy of the header
 };
@@ -660,13 +1016,24 @@ bool desc_ok(const stq_pool_desc* d) {
 void layout(const stq_pool_desc* d, stq_pool* p) {
   p->n_slots = d->n_slots; p->H = d->n_heads; p->dk = d->d_k; p->dv = d->d_v;
   p->gate = d->gate_kind; p->unit = d->unit_kind; p->W = d->window;
-  p->bits.assign(d->unit_bits, d->unit_bits + d->n_heads);
+  const bool rows = p->unit == STQ_UNIT_ROW;
+  p->bits.assign(d->unit_bits, d->unit_bits + (rows ? d->n_heads * d->d_k : d->n_heads));
   p->head_off.resize(d->n_heads);
   uint64_t s = 0;
-  for (int h = 0; h < d->n_heads; h++) { p->head_off[h] = (uint32_t)s; s += tile_stride(p->bits[h], p->dk, p->dv); }
+  for (int h = 0; h < d->n_heads; h++) {
+    p->head_off[h] = (uint32_t)s;
+    if (rows) {
+      uint64_t b = 2ull * (p->dk + p->dv);
+      for (int i = 0; i < p->dk; i++) b += (uint64_t)p->dv * p->bits[(size_t)h * p->dk + i] / 8;
+      s += ru256(b);
+    } else {
+      s += tile_stride(p->bits[h], p->dk, p->dv);
+    }
+  }
   p->slot_bytes = s;
   p->woff = ru256(64 + 8ull * p->H);
-  p->hdr = ru256(p->woff + 4ull * p->H * p->dk);
+  p->roff = ru256(p->woff + 4ull * p->H * p->dk);
+  p->hdr = rows ? ru256(p->roff + 2ull * p->H * p->dk + 16ull * p->H) : p->roff;
   p->slots_off = p->hdr;
   p->cache_off = p->slots_off + (uint64_t)p->n_slots * p->slot_bytes;
   p->cache_stride = p->W ? 256 + 4ull * p->W * (p->dk + p->dv) : 0;
@@ -687,6 +1054,8 @@ KArgs base_args(const stq_pool* p, const int32_t* slots, int n) {
   A.head_bits = (const int32_t*)(p->dev + 64);
   A.head_off = (const uint32_t*)(p->dev + 64 + 4 * p->H);
   A.weights = (const float*)(p->dev + p->woff);
+  A.row_perm = p->dev + p->roff + (size_t)p->H * p->dk;
+  A.row_cnt = (const int32_t*)(p->dev + p->roff + 2ull * p->H * p->dk);
   return A;
 }
 
@@ -711,6 +1080,15 @@ struct LTile {
   struct T {
     static void go(const KArgs& A, unsigned g, hipStream_t st) {
       hipLaunchKernelGGL((k_tile<DK, DV, MODE>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
+    }
+  };
+};
+template <int MODE>
+struct LRows {
+  template <int DK, int DV>
+  struct T {
+    static void go(const KArgs& A, unsigned g, hipStream_t st) {
+      hipLaunchKernelGGL((k_rows<DK, DV, MODE>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
     }
   };
 };
@@ -757,7 +1135,7 @@ const char* stq_status_str(stq_status s) {
 }
 
 size_t stq_pool_bytes(const stq_pool_desc* d) {
-  if (!desc_ok(d) || d->unit_kind != STQ_UNIT_HEAD) return 0;
+  if (!desc_ok(d)) return 0;
   stq_pool p;
   layout(d, &p);
   return (size_t)p.total;
@@ -768,8 +1146,8 @@ stq_status stq_pool_create(const stq_pool_desc* d, void* dev_buf, size_t bytes, 
   if (!out) return STQ_ERR_ARG;
   *out = nullptr;
   if (!desc_ok(d)) return STQ_ERR_ARG;
-  if (d->unit_kind != STQ_UNIT_HEAD) return STQ_ERR_UNSUPPORTED;
-  if (d->window > 0 && d->gate_kind != STQ_GATE_HEAD) return STQ_ERR_UNSUPPORTED;
+  if (d->window > 0 && (d->gate_kind != STQ_GATE_HEAD || d->unit_kind != STQ_UNIT_HEAD))
+    return STQ_ERR_UNSUPPORTED;
   if (!dev_buf || ((uintptr_t)dev_buf & 255u)) return STQ_ERR_LAYOUT;
   stq_pool* p = new (std::nothrow) stq_pool;
   if (!p) return STQ_ERR_ARG;
@@ -783,18 +1161,36 @@ stq_status stq_pool_create(const stq_pool_desc* d, void* dev_buf, size_t bytes, 
   put32(hb + 20, p->gate); put32(hb + 24, p->unit); put32(hb + 28, p->W);
   put64(hb + 32, p->slot_bytes); put64(hb + 40, p->slots_off); put64(hb + 48, p->cache_off);
   put64(hb + 56, p->cache_stride);
+  const bool rows = p->unit == STQ_UNIT_ROW;
   for (int h = 0; h < p->H; h++) {
-    put32(hb + 64 + 4 * h, (uint32_t)p->bits[h]);
+    put32(hb + 64 + 4 * h, rows ? 0u : (uint32_t)p->bits[h]);
     put32(hb + 64 + 4 * p->H + 4 * h, p->head_off[h]);
   }
   memcpy(hb + p->woff, d->row_weight, 4ull * p->H * p->dk);
+  if (rows) {   // widths (original order), record order (sorted by width), counts
+    static const int W4[4] = {4, 6, 8, 16};
+    uint8_t* wr = hb + p->roff;
+    uint8_t* pr = wr + (size_t)p->H * p->dk;
+    uint8_t* cr = pr + (size_t)p->H * p->dk;
+    for (int h = 0; h < p->H; h++) {
+      const int32_t* b = &p->bits[(size_t)h * p->dk];
+      int q = 0;
+      for (int k = 0; k < 4; k++) {
+        int c = 0;
+        for (int i = 0; i < p->dk; i++)
+          if (b[i] == W4[k]) { pr[(size_t)h * p->dk + q++] = (uint8_t)i; c++; }
+        put32(cr + 16 * (size_t)h + 4 * k, (uint32_t)c);
+      }
+      for (int i = 0; i < p->dk; i++) wr[(size_t)h * p->dk + i] = (uint8_t)b[i];
+    }
+  }
   if (hipMemcpyAsync(p->dev, hb, p->hdr, hipMemcpyHostToDevice, stream) != hipSuccess) {
     delete p;
     return STQ_ERR_HIP;
   }
   // zero state in every slot (codes 0, scales 1) and empty windows
   KArgs A = base_args(p, nullptr, p->n_slots);
-  stq_status s = dispatch<LTile<MODE_STORE>::T>(p, A, stream);
+  stq_status s = rows ? dispatch<LRows<RMODE_STORE>::T>(p, A, stream) : dispatch<LTile<MODE_STORE>::T>(p, A, stream);
   if (s != STQ_OK) { delete p; return s; }
   *out = p;
   return STQ_OK;
@@ -813,6 +1209,7 @@ stq_status stq_pool_store(stq_pool* p, const int32_t* slots, int32_t n, const fl
   if (!S) return STQ_ERR_ARG;
   KArgs A = base_args(p, slots, n);
   A.S_in = S;
+  if (p->unit == STQ_UNIT_ROW) return dispatch<LRows<RMODE_STORE>::T>(p, A, st);
   return dispatch<LTile<MODE_STORE>::T>(p, A, st);
 }
 
@@ -823,6 +1220,7 @@ stq_status stq_pool_fetch(const stq_pool* p, const int32_t* slots, int32_t n, fl
   if (!S) return STQ_ERR_ARG;
   KArgs A = base_args(p, slots, n);
   A.S_out = S;
+  if (p->unit == STQ_UNIT_ROW) return dispatch<LRows<RMODE_FETCH>::T>(p, A, st);
   return dispatch<LFetch<false>::T>(p, A, st);
 }
 
@@ -831,6 +1229,7 @@ stq_status stq_requant_fixed_scales(stq_pool* p, const int32_t* slots, int32_t n
   if (s != STQ_OK) return s;
   if (n == 0) return STQ_OK;
   KArgs A = base_args(p, slots, n);
+  if (p->unit == STQ_UNIT_ROW) return dispatch<LRows<RMODE_REQUANT>::T>(p, A, st);
   return dispatch<LFetch<true>::T>(p, A, st);
 }
 
@@ -843,6 +1242,7 @@ stq_status stq_decode_step(stq_pool* p, const int32_t* slots, int32_t n, const f
   KArgs A = base_args(p, slots, n);
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
   if (p->W > 0) return dispatch<LWindow<false>::T>(p, A, st);
+  if (p->unit == STQ_UNIT_ROW) return dispatch<LRows<RMODE_STEP>::T>(p, A, st);
   return dispatch<LTile<MODE_STEP>::T>(p, A, st);
 }
 

@@ -20,13 +20,13 @@ class Pair:
         self.stq, self.orc, self.wl = stq, orc, wl
         self.n_slots = wl.B if n_slots is None else n_slots
         W = wl.cfg.window if window is None else window
-        self.desc = stq.make_desc(self.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight,
-                                  wl.cfg.gate, wl.cfg.unit, W)
+        self.desc = stq.make_desc(self.n_slots, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1),
+                                  wl.row_weight, wl.cfg.gate, wl.cfg.unit, W)
         nbytes = stq.stq_pool_bytes(self.desc)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.pool = stq.stq_pool_create(self.desc, self.buf)
-        self.ref = orc.OraclePool(self.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight,
-                                  wl.cfg.gate, wl.cfg.unit, W)
+        self.ref = orc.OraclePool(self.n_slots, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1),
+                                  wl.row_weight, wl.cfg.gate, wl.cfg.unit, W)
         assert self.ref.nbytes == nbytes
 
     def image(self):
@@ -61,14 +61,12 @@ def compare_codes(orc, ref_pool, img_gpu, img_ref, slots, heads=None):
     res = dict(codes=0, mism=0, maxd=0, scales=0, scale_mism=0, piv=0, piv_bad=0, piv_mism=0)
     for s in slots:
         for h in heads:
-            n = int(ref_pool.bits[h])
-            tg = ref_pool.tile_view(int(s), h, img_gpu)
-            tr = ref_pool.tile_view(int(s), h, img_ref)
-            Qg, sg, cg = orc.unpack(n, ref_pool.dk, ref_pool.dv, tg)
-            Qr, sr, cr = orc.unpack(n, ref_pool.dk, ref_pool.dv, tr)
-            if n == 16:
-                fg = Qg.astype(np.uint16).view(np.float16).astype(np.float64)
-                fr = Qr.astype(np.uint16).view(np.float16).astype(np.float64)
+            Qg, sg, cg, nb = ref_pool.decode_tile(int(s), h, img_gpu)
+            Qr, sr, cr, _ = ref_pool.decode_tile(int(s), h, img_ref)
+            piv = nb == 16
+            if piv.any():
+                fg = Qg[piv].astype(np.uint16).view(np.float16).astype(np.float64)
+                fr = Qr[piv].astype(np.uint16).view(np.float16).astype(np.float64)
                 res["piv"] += fg.size
                 res["piv_mism"] += int(np.count_nonzero(fg != fr))
                 # a mismatch must be one binary16 rounding step of the value, or lie
@@ -76,13 +74,13 @@ def compare_codes(orc, ref_pool, img_gpu, img_ref, slots, heads=None):
                 step = np.maximum(np.abs(fr), np.abs(fg)) * 2.0 ** -10 + 2.0 ** -24
                 floor = 2.0 ** -20 * np.abs(fr).max(axis=1, keepdims=True)
                 res["piv_bad"] += int(np.sum(np.abs(fg - fr) > np.maximum(step, floor)))
-                continue
-            d = np.abs(Qg - Qr)
-            res["codes"] += d.size
-            res["mism"] += int(np.count_nonzero(d))
-            res["maxd"] = max(res["maxd"], int(d.max()))
-            res["scales"] += sg.size + cg.size
-            res["scale_mism"] += int(np.count_nonzero(sg != sr) + np.count_nonzero(cg != cr))
+            if (~piv).any():
+                d = np.abs(Qg[~piv] - Qr[~piv])
+                res["codes"] += d.size
+                res["mism"] += int(np.count_nonzero(d))
+                res["maxd"] = max(res["maxd"], int(d.max()))
+                res["scales"] += sg.size + cg.size
+                res["scale_mism"] += int(np.count_nonzero(sg != sr) + np.count_nonzero(cg != cr))
     return res
 
 

@@ -31,13 +31,14 @@ def test_exports_every_declared_symbol(stq):
         assert hasattr(lib, n), n
 
 
-@pytest.mark.parametrize("key,B", [("C1", 4), ("C2", 64), ("C3", 512), ("C5", 512)])
+@pytest.mark.parametrize("key,B", [("C1", 4), ("C2", 64), ("C3", 512), ("C4", 256), ("C5", 512)])
 def test_pool_bytes_agree_with_oracle(stq, orc, key, B):
     from workloads import Workload
     wl = Workload(key, B=B)
-    d = stq.make_desc(B, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, wl.cfg.gate, wl.cfg.unit,
+    bits = np.asarray(wl.bits).reshape(-1)
+    d = stq.make_desc(B, wl.H, wl.dk, wl.dv, bits, wl.row_weight, wl.cfg.gate, wl.cfg.unit,
                       wl.cfg.window)
-    P = orc.OraclePool(B, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, wl.cfg.gate, wl.cfg.unit,
+    P = orc.OraclePool(B, wl.H, wl.dk, wl.dv, bits, wl.row_weight, wl.cfg.gate, wl.cfg.unit,
                        wl.cfg.window)
     assert stq.stq_pool_bytes(d) == P.nbytes
 

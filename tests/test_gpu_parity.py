@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 MISMATCH_MAX = 1e-4
 
 # (config, B, slot-pool size, slot permutation seed): ragged request counts
-STORE_CASES = [("C1", 4, 4), ("C2", 64, 64), ("C3", 37, 50), ("C5", 21, 24)]
+STORE_CASES = [("C1", 4, 4), ("C2", 64, 64), ("C3", 37, 50), ("C4", 19, 23), ("C5", 21, 24)]
 
 
 @pytest.fixture(scope="module")
@@ -54,7 +54,7 @@ def test_fetch_and_fixed_requant_exact(torch_cuda, orc, key, B, NS):
     np.testing.assert_array_equal(P.image(), before)
 
 
-@pytest.mark.parametrize("key", ["C1", "C2"])
+@pytest.mark.parametrize("key", ["C1", "C2", "C4"])
 def test_identity_update_keeps_bytes(torch_cuda, orc, key):
     say("case identity", key)
     wl = Workload(key, B=min(16, Workload(key).B))
@@ -86,8 +86,8 @@ def _teacher_forced(orc, wl, P, slots, T):
     worst = dict(mism=0, codes=0, maxd=0, scale_mism=0, scales=0, piv_bad=0, piv=0, piv_mism=0, o=0.0)
     for t in range(T):
         img = P.image()
-        ref = orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight,
-                             wl.cfg.gate, wl.cfg.unit, wl.cfg.window, image=img)
+        ref = orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1),
+                             wl.row_weight, wl.cfg.gate, wl.cfg.unit, wl.cfg.window, image=img)
         q, k, v, a, b = wl.token(t, len(slots))
         o = P.gpu_step(slots, q, k, v, a, b)
         o_ref = ref.step(slots, q, k, v, a, b)
@@ -99,7 +99,7 @@ def _teacher_forced(orc, wl, P, slots, T):
     return worst
 
 
-@pytest.mark.parametrize("key,B,T", [("C1", 4, 32), ("C2", 64, 1), ("C3", 40, 4)])
+@pytest.mark.parametrize("key,B,T", [("C1", 4, 32), ("C2", 64, 1), ("C3", 40, 4), ("C4", 24, 4)])
 def test_fused_step_teacher_forced(torch_cuda, orc, key, B, T):
     say("case step", key, B, T)
     wl = Workload(key, B=B)
