@@ -60,19 +60,23 @@
  * [-qmax, qmax] is stored as the unsigned field Q + 2^(n-1) (offset binary;
  * the all-zero field is never produced).
  *
- * LANE LAYOUT.  Let RB = d_k/16, CPW = 4*(64/RB) (columns per 64-lane wave),
- * NW = d_v/CPW.  Wave w in [0,NW), lane l in [0,64): rb = l % RB,
- * cb = l / RB.  The lane owns the 16x4 block
- *     row i = rb + RB*r   (r in [0,16)),   col j = w*CPW + 4*cb + c (c in [0,4)).
- * Its LANE STREAM is the 16 rows r = 0..15 in order, each row's 4 codes
- * (c = 0..3) packed in n/2 bytes:
+ * LANE LAYOUT.  Let NRC = d_k/32 (32-row chunks), NCC = 8/NRC (16-column
+ * chunks per wave), CPW = 16*NCC (columns per 64-lane wave), NW = d_v/CPW.
+ * Wave w in [0,NW), lane l in [0,64): G = l / 16, n = l % 16.  The lane
+ * owns the 64 elements e = 8b + t (b = cc*NRC + rc in [0,8), t in [0,8)):
+ *     row i = 32*rc + 16*(t/4) + 4*G + t%4,   col j = w*CPW + 16*cc + n.
+ * Its LANE STREAM is the 16 GROUPS q = e/4 = 0..15 in order; group q holds
+ * the codes of elements 4q..4q+3 (four consecutive rows of one column,
+ * f0 = the lowest row) packed in n/2 bytes:
  *     n=4 : 2 bytes, byte0 = f0 | f1<<4, byte1 = f2 | f3<<4
  *     n=6 : 3 bytes, little-endian 24-bit word f0 | f1<<6 | f2<<12 | f3<<18
  *     n=8 : 4 bytes f0, f1, f2, f3
  *     n=16: 8 bytes, four binary16 values, little-endian
  * (f = stored field).  The lane stream has K = n/2 chunks of 16 bytes; chunk
  * k of lane l of wave w sits at code-region offset 16*((w*K + k)*64 + l), so
- * that one 16-byte load per lane reads 1 KiB contiguous per wave.
+ * that one 16-byte load per lane reads 1 KiB contiguous per wave.  (The two
+ * groups of chunk b are the lane's operand of a 32 x 16 block in the gfx950
+ * 16x16x32 fp16 matrix instruction: G picks 8 of the 32 rows, n the column.)
  *
  * PER-ROW WIDTHS (unit_kind ROW, the KDA allocation unit = key row, [P4]
  * "Las dos ideas"): a tile is a list of ROW RECORDS, one per key row, each

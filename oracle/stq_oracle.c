@@ -240,16 +240,27 @@ size_t orc_tile_bytes(int n, int dk, int dv) {
 }
 size_t orc_tile_stride(int n, int dk, int dv) { return (orc_tile_bytes(n, dk, dv) + 255) / 256 * 256; }
 
-/* position of row i, column j: wave w, lane l, lane row r, lane column c */
-static void lane_of(int dk, int i, int j, int* w, int* l, int* r, int* c) {
-  int RB = dk / 16, CPW = 4 * (64 / RB);
-  int rb = i % RB;
-  *r = i / RB;
+/* Lane layout of a per-head tile.  NRC = dk/32 row chunks, NCC = 8/NRC
+ * column chunks of 16 per wave, CPW = 16*NCC columns per wave.  Element e
+ * (0..63) of lane l in wave w: b = e/8 (cc = b/NRC, rc = b%NRC), t = e%8,
+ *   row = 32 rc + 16 (t/4) + 4 (l/16) + t%4,   col = w CPW + 16 cc + l%16.
+ * Group q = e/4 holds 4 consecutive rows of one column. */
+static void lane_of(int dk, int i, int j, int* w, int* l, int* q, int* c) {
+  int NRC = dk / 32, NCC = 8 / NRC, CPW = 16 * NCC;
   *w = j / CPW;
-  int jj = j % CPW;
-  int cb = jj / 4;
-  *c = jj % 4;
-  *l = rb + RB * cb;
+  int jj = j % CPW, cc = jj / 16, n16 = jj % 16;
+  int rc = i / 32, r32 = i % 32, half = r32 / 16, G = (r32 % 16) / 4, ii = r32 % 4;
+  int t = 4 * half + ii;
+  *l = 16 * G + n16;
+  int e = 8 * (cc * NRC + rc) + t;
+  *q = e / 4;
+  *c = e % 4;
+}
+static void elem_of(int dk, int w, int l, int e, int* i, int* j) {
+  int NRC = dk / 32, NCC = 8 / NRC, CPW = 16 * NCC;
+  int b = e / 8, cc = b / NRC, rc = b % NRC, t = e % 8;
+  *i = 32 * rc + 16 * (t / 4) + 4 * (l / 16) + (t % 4);
+  *j = w * CPW + 16 * cc + (l % 16);
 }
 /* code-region byte offset of byte b of the lane stream of (w, l) */
 static size_t stream_off(int n, int w, int l, int b) {
@@ -260,17 +271,16 @@ static size_t stream_off(int n, int w, int l, int b) {
 /* Pack one uniform-width tile: codes Q (pivot: binary16 bits), scales. */
 void orc_pack(int n, int dk, int dv, const int32_t* Q, const uint16_t* sig, const uint16_t* cst,
               uint8_t* tile) {
-  int NW = dv / (4 * (64 / (dk / 16)));
-  int bpr = n / 2;                       /* bytes per lane row (4 codes) */
+  int NW = dv / (16 * (8 / (dk / 32)));
+  int bpr = n / 2;                       /* bytes per group (4 codes) */
   int32_t f[4];
   for (int w = 0; w < NW; w++)
     for (int l = 0; l < 64; l++)
-      for (int r = 0; r < 16; r++) {
-        int RB = dk / 16, CPW = 4 * (64 / RB);
-        int i = (l % RB) + RB * r;
-        int j0 = w * CPW + 4 * (l / RB);
+      for (int r = 0; r < 16; r++) {     /* group r of the lane stream */
         for (int c = 0; c < 4; c++) {
-          int32_t q = Q[(size_t)i * dv + j0 + c];
+          int i, j;
+          elem_of(dk, w, l, 4 * r + c, &i, &j);
+          int32_t q = Q[(size_t)i * dv + j];
           f[c] = (n == 16) ? q : q + (1 << (n - 1));
         }
         uint8_t bytes[8];

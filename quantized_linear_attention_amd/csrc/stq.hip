@@ -1,12 +1,14 @@
 // stq.hip — gfx950 kernels and C ABI of the low-bit recurrent-state pool
 // (contract: include/stq.h).
 //
-// One workgroup per (request, head) tile.  Each 64-lane wave owns all d_k
-// rows of CPW value columns; each lane owns a 16 x 4 block, so every column
-// reduction (the two matvecs u = A^T k, w = A^T q and the column absmax of
-// the refit) closes inside a wave with three DPP steps, and only the row
-// absmax crosses waves (through LDS).  Codes are loaded and stored with one
-// 16-byte access per lane per chunk (1 KiB contiguous per wave).
+// One workgroup per (request, head) tile.  Per-head tiles: each 64-lane wave
+// owns all d_k rows of CPW value columns; the two matvecs run on
+// v_mfma_f32_16x16x32_f16 straight from the unpacked fp16 codes and the
+// rank-one update on v_mfma_f32_16x16x4_f32, so the vector ALUs only unpack,
+// refit and pack.  Per-key-row tiles (mixed widths inside a tile) stage their
+// row records through LDS and run on the vector ALUs.  Codes are loaded and
+// stored with one 16-byte access per lane per chunk (1 KiB contiguous per
+// wave).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -39,6 +41,7 @@ struct KArgs {
   float* S_out;              // fetch
 };
 
+// LDS of the per-key-row kernel
 template <int DK, int DV>
 struct Smem {
   float alpha[DK] __attribute__((aligned(16)));   // [rb][r]: g k
@@ -62,55 +65,183 @@ __device__ __forceinline__ int tile_of_block(int T) {
 }
 
 // ------------------------------------------------------------------------
-// Shared refit + store stage.  Y[4r+c] holds S'_ij / g_i for the lane's
-// elements (g_i in sm.gg, visible after the next barrier); for a binary16
-// pivot tile Y holds S' itself.  Writes codes, row and column scales.
+// Per-head tiles on the matrix cores.
+//
+// Lane l of wave w (G = l/16, n = l%16) owns the elements e = 8b + t,
+// b = cc*NRC + rc, t in [0, 8):
+//     row 32 rc + 16 (t/4) + 4 G + t%4,   column w CPW + 16 cc + n,
+// and group q = e/4 (4 rows of one column) is the q-th group of its lane
+// stream.  The two matvecs u = A^T k and w = A^T q run as
+// v_mfma_f32_16x16x32_f16: B is a 32-row x 16-column chunk of the exact fp16
+// codes (the lane's fragment is its two groups of that chunk), A is
+// (g k, g q) split into fp16 hi + lo parts, replicated over the four output
+// row quads, so every lane receives the four partial sums of its own column.
+// The rank-one update C + kappa delta^T runs as v_mfma_f32_16x16x4_f32 with
+// C = c Q, whose output fragment is exactly the lane's four rows of a
+// 16 x 16 block.  Column reductions close inside a wave (one permlane swap
+// pair); row reductions cross lanes and waves through LDS.
+// ------------------------------------------------------------------------
+template <int DK, int DV>
+struct GeoM {
+  static constexpr int NRC = DK / 32;       // 32-row chunks
+  static constexpr int NCC = 8 / NRC;       // 16-column chunks per wave
+  static constexpr int CPW = 16 * NCC;      // columns per wave
+  static constexpr int NW = DV / CPW;       // waves per tile
+  static constexpr int NT = 64 * NW;
+  static constexpr int TPR = NT / DK;       // threads per row in the row stage
+  static constexpr int NP = NW * 16;        // partial row maxima per row
+  static constexpr int PSTR = DK + 4;       // LDS stride of one partial set
+  static_assert(DK == 64 || DK == 128, "d_k");
+  static_assert(NW >= 1 && DV % CPW == 0, "d_v");
+  static_assert(TPR == 1 || TPR == 2, "threads per row");
+};
+
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <int DK, int DV>
+struct SmemM {
+  f16 afr[DK / 32][4][4][8] __attribute__((aligned(16)));   // [rc][G][v][k]: matvec A fragments
+  float kappa[DK] __attribute__((aligned(16)));             // natural row order
+  float gg[DK] __attribute__((aligned(16)));
+  float rowh[DK] __attribute__((aligned(16)));
+  float part[GeoM<DK, DV>::NP * GeoM<DK, DV>::PSTR] __attribute__((aligned(16)));
+  float kqp[GeoM<DK, DV>::NW];
+  int notone[GeoM<DK, DV>::NW];
+  int esum[GeoM<DK, DV>::NW];
+  int ecnt[GeoM<DK, DV>::NW];
+};
+
+// element t (0..7) of the lane's two groups of a chunk -> k index of its
+// MFMA fragment, given where unpack<N> leaves each code (see preg/phalf)
+template <int N> __device__ __forceinline__ constexpr int t_to_kk(int t) {
+  return N == 4 ? 2 * (t & 3) + (t >> 2) : (N == 6 ? (t & 4) | ((t & 1) << 1) | ((t >> 1) & 1) : t);
+}
+__device__ __forceinline__ constexpr int erow(int rc, int t, int G) {
+  return 32 * rc + 16 * (t >> 2) + 4 * G + (t & 3);
+}
+
+// wave-uniform max of non-negative floats
+__device__ __forceinline__ float wave_max_pos(float v) {
+  int x = __float_as_int(v);
+  x = __builtin_elementwise_max(x, dppi<0xB1>(x));
+  x = __builtin_elementwise_max(x, dppi<0x4E>(x));
+  x = __builtin_elementwise_max(x, dppi<0x141>(x));
+  x = __builtin_elementwise_max(x, dppi<0x140>(x));
+  int a = __builtin_elementwise_max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+  int b = __builtin_elementwise_max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+  return __int_as_float(__builtin_elementwise_max(a, b));
+}
+// max over the four lanes n, n+16, n+32, n+48 of non-negative floats
+__device__ __forceinline__ float g4_max_pos(float v) {
+  uint32_t x = __float_as_uint(v);
+  auto p16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = __builtin_elementwise_max((uint32_t)p16[0], (uint32_t)p16[1]);
+  auto p32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = __builtin_elementwise_max((uint32_t)p32[0], (uint32_t)p32[1]);
+  return __uint_as_float(x);
+}
+// power of two sc that puts m into [2^14, 2^15) (clamped to normal range),
+// and 1/sc: keeps the matvec operand inside binary16's range
+__device__ __forceinline__ void fp16_scale(float m, float& sc, float& inv) {
+  int e = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127;
+  int s = 14 - e;
+  s = s < -113 ? -113 : (s > 126 ? 126 : s);
+  sc = __builtin_ldexpf(1.0f, s);
+  inv = __builtin_ldexpf(1.0f, -s);
+}
+
+// matvec A fragments of row i: fp16 hi/lo of the scaled (g k, g q)
+template <int DK, int DV, int N>
+__device__ __forceinline__ void put_afr(SmemM<DK, DV>& sm, int i, float al, float be) {
+  const int rc = i >> 5, G = (i >> 2) & 3, t = 4 * ((i >> 4) & 1) + (i & 3);
+  const int k = t_to_kk<N>(t);
+  const f16 ah = (f16)al, bh = (f16)be;
+  sm.afr[rc][G][0][k] = ah;
+  sm.afr[rc][G][1][k] = (f16)(al - (float)ah);
+  sm.afr[rc][G][2][k] = bh;
+  sm.afr[rc][G][3][k] = (f16)(be - (float)bh);
+}
+
+// D[cc] = (alpha_hi, alpha_lo, beta_hi, beta_lo) . Q over all rows, for the
+// lane's column of chunk cc
+template <int DK, int DV>
+__device__ __forceinline__ void matvec(const SmemM<DK, DV>& sm, const f16x2* P, f32x4* D) {
+  using G = GeoM<DK, DV>;
+  const int l = threadIdx.x & 63;
+  f16x8 af[G::NRC];
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++) af[rc] = *(const f16x8*)&sm.afr[rc][l >> 4][l & 3][0];
+#pragma unroll
+  for (int cc = 0; cc < G::NCC; cc++) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++) {
+      const int b = cc * G::NRC + rc;
+      const f16x8 bf = __builtin_shufflevector(__builtin_shufflevector(P[4 * b], P[4 * b + 1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(P[4 * b + 2], P[4 * b + 3], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rc], bf, acc, 0, 0, 0);
+    }
+    D[cc] = acc;
+  }
+}
+template <int N>
+__device__ __forceinline__ float code_e(const f16x2* P, int e) { return code_at<N>(P, e >> 2, e & 3); }
+// materialise a value in a VGPR at this point of the program
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// ------------------------------------------------------------------------
+// Refit + store.  Y[e] holds S'_ij / g_i for the lane's elements (g_i in
+// sm.gg, visible after the next barrier); for a binary16 pivot tile Y holds
+// S' itself.  Writes codes, row and column scales.
 // ------------------------------------------------------------------------
 template <int DK, int DV, int N, bool EXACT>
-__device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, float* Y, uint8_t* tile, int h) {
-  using G = Geo<DK, DV>;
+__device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t* tile, float wgt) {
+  using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int rb = l % G::RB, cb = l / G::RB;
-  const int j0 = w * G::CPW + 4 * cb;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
   uint8_t* codes = tile;
   uint16_t* scl = (uint16_t*)(tile + DK * DV * N / 8);
   uint32_t raw[2 * N];
   if constexpr (N == 16) {
     // binary16 pivot tile: saturate, round to nearest even
 #pragma unroll
-    for (int r = 0; r < 16; r++)
+    for (int q = 0; q < 16; q++)
 #pragma unroll
       for (int h2 = 0; h2 < 2; h2++) {
-        float s0 = __builtin_fminf(__builtin_fmaxf(Y[4 * r + 2 * h2], -65504.f), 65504.f);
-        float s1 = __builtin_fminf(__builtin_fmaxf(Y[4 * r + 2 * h2 + 1], -65504.f), 65504.f);
-        raw[2 * r + h2] = h2_bits(f16x2{(f16)s0, (f16)s1});
+        float s0 = __builtin_fminf(__builtin_fmaxf(Y[4 * q + 2 * h2], -65504.f), 65504.f);
+        float s1 = __builtin_fminf(__builtin_fmaxf(Y[4 * q + 2 * h2 + 1], -65504.f), 65504.f);
+        raw[2 * q + h2] = h2_bits(f16x2{(f16)s0, (f16)s1});
       }
   } else {
-    const int rho = tid / G::TPR, rsub = tid % G::TPR;
-    const int irow = (rho >> 4) + G::RB * (rho & 15);
-    // ---- row refit: partial row absmax -> LDS -> one thread (pair) per row ----
+    const int rho = tid / G::TPR, rsub = tid % G::TPR;      // row stage: row rho
+    // ---- row refit: partial row absmax over the lane's columns -> LDS ----
 #pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) {
-      f32x4 m4;
+    for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        int r = 4 * r4 + q;
-        m4[q] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(Y[4 * r]), __builtin_fabsf(Y[4 * r + 1])),
-                                __builtin_fmaxf(__builtin_fabsf(Y[4 * r + 2]), __builtin_fabsf(Y[4 * r + 3])));
+      for (int hf = 0; hf < 2; hf++) {
+        f32x4 m4;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float m = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < G::NCC; cc++)
+            m = __builtin_fmaxf(m, __builtin_fabsf(Y[8 * (cc * G::NRC + rc) + 4 * hf + i]));
+          m4[i] = m;
+        }
+        *(f32x4*)&sm.part[(w * 16 + n16) * G::PSTR + erow(rc, 4 * hf, Gq)] = m4;
       }
-      *(f32x4*)&sm.part[(w * G::CBW + cb) * DK + rb * 16 + 4 * r4] = m4;
-    }
     __syncthreads();
     uint32_t mxb = 0u;                              // non-negative: compare bit patterns
 #pragma unroll
-    for (int p = 0; p < G::NP / G::TPR; p++)
-      mxb = __builtin_elementwise_max(mxb, __float_as_uint(sm.part[(rsub * (G::NP / G::TPR) + p) * DK + rho]));
-    if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
-    const float mx = __uint_as_float(mxb);
+    for (int p = 0; p < G::NP / G::TPR; p++) {
+      const int pp = 4 * (G::TPR * (p >> 2) + rsub) + (p & 3);
+      mxb = __builtin_elementwise_max(mxb, __float_as_uint(sm.part[pp * G::PSTR + rho]));
+    }
+    if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)dppi<0xB1>((int)mxb));
     const float g = sm.gg[rho];
-    const float m = g * mx;                        // row absmax of S'
-    const float pw = m * A.weights[(size_t)h * DK + irow];
+    const float m = g * __uint_as_float(mxb);      // row absmax of S'
+    const float pw = m * wgt;                      // wgt: weight of row rho
     uint32_t s = 0x3F80u;
     int epk = 0;                                   // exponent sum * 256 + row count
     if (pw > 0.f) {
@@ -120,8 +251,7 @@ __device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, fl
       epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
     }
     if (rsub != 0) epk = 0;
-    const float rs = rcp_bf16(bf16f(s));          // correctly rounded
-    if (rsub == 0) sm.rowh[rho] = g * rs;
+    if (rsub == 0) sm.rowh[rho] = g * rcp_bf16(bf16f(s));
     epk = wave_sum_i(epk);
     if (l == 0) { sm.esum[w] = epk >> 8; sm.ecnt[w] = epk & 0xFF; }
     __syncthreads();
@@ -129,45 +259,41 @@ __device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, fl
 #pragma unroll
     for (int ww = 0; ww < G::NW; ww++) { es += sm.esum[ww]; ec += sm.ecnt[ww]; }
     const int E = ec ? mean_exp(es, ec) : 0;
-    if (rsub == 0) scl[irow] = (uint16_t)bf16_adj(s, -E);
-    // ---- column refit ----
-    float hr[16];
+    if (rsub == 0) scl[rho] = (uint16_t)bf16_adj(s, -E);
+    // ---- column refit: X = Y h, column absmax over the wave's 4 row quads ----
+    float hr[8 * G::NRC];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&hr[4 * r4] = *(const f32x4*)&sm.rowh[rb * 16 + 4 * r4];
-    float cm[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
-    for (int r = 0; r < 16; r++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        Y[4 * r + c] = Y[4 * r + c] * hr[r];
-        cm[c] = __builtin_fmaxf(cm[c], __builtin_fabsf(Y[4 * r + c]));
-      }
-    // column scales: lane q of every quad fits column q of its block, then
-    // the four reciprocals are broadcast inside the quad
+      for (int hf = 0; hf < 2; hf++)
+        *(f32x4*)&hr[8 * rc + 4 * hf] = *(const f32x4*)&sm.rowh[erow(rc, 4 * hf, Gq)];
     constexpr float RQ = 1.0f / (float)Fmt<N>::QMAX;
+    float rq[G::NCC];
 #pragma unroll
-    for (int c = 0; c < 4; c++) cm[c] = rb_max_pos<G::RB>(cm[c]);
-    const int qd = l & 3;
-    const float Mq = (qd == 0 ? cm[0] : qd == 1 ? cm[1] : qd == 2 ? cm[2] : cm[3]) * RQ;
-    uint32_t t = 0x3F80u;
-    if (Mq > 0.f) {
-      t = bf16_ru_pos(Mq);
-      if (t < 0x0080u) t = 0x0080u;              // at least 2^-126
+    for (int cc = 0; cc < G::NCC; cc++) {
+      float cm = 0.f;
+#pragma unroll
+      for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          const int e = 8 * (cc * G::NRC + rc) + t;
+          Y[e] = Y[e] * hr[8 * rc + t];
+          cm = __builtin_fmaxf(cm, __builtin_fabsf(Y[e]));
+        }
+      const float M = g4_max_pos(cm) * RQ;
+      uint32_t tt = 0x3F80u;
+      if (M > 0.f) {
+        tt = bf16_ru_pos(M);
+        if (tt < 0x0080u) tt = 0x0080u;            // at least 2^-126
+      }
+      rq[cc] = rcp_bf16(bf16f(tt));
+      if (Gq == 0) scl[DK + w * G::CPW + 16 * cc + n16] = (uint16_t)bf16_adj(tt, E);
     }
-    const float rcq = rcp_bf16(bf16f(t));
-    if (rb < 4) scl[DK + j0 + qd] = (uint16_t)bf16_adj(t, E);
-    float rc[4];
-    rc[0] = quad_bcast<0>(rcq);
-    rc[1] = quad_bcast<1>(rcq);
-    rc[2] = quad_bcast<2>(rcq);
-    rc[3] = quad_bcast<3>(rcq);
     // ---- requantize: nearest code of the exact product, field in the low bits ----
     uint32_t yb[64];
 #pragma unroll
-    for (int r = 0; r < 16; r++)
-#pragma unroll
-      for (int c = 0; c < 4; c++)
-        yb[4 * r + c] = __float_as_uint(__builtin_fmaf(Y[4 * r + c], rc[c], Fmt<N>::MAGIC));
+    for (int e = 0; e < 64; e++)
+      yb[e] = __float_as_uint(__builtin_fmaf(Y[e], rq[e / (8 * G::NRC)], Fmt<N>::MAGIC));
     pack<N>(yb, raw);
   }
 #pragma unroll
@@ -179,116 +305,119 @@ __device__ __forceinline__ void refit_store(const KArgs& A, Smem<DK, DV>& sm, fl
 // then refit_store); MODE_STORE = refit_store of a given fp32 tile.
 // ------------------------------------------------------------------------
 template <int DK, int DV, int MODE, int N>
-__device__ __forceinline__ void tile_body(const KArgs& A, Smem<DK, DV>& sm, uint8_t* tile,
-                                          size_t x, int h, uint8_t* cache) {
-  using G = Geo<DK, DV>;
+__device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uint8_t* tile, size_t x, int h,
+                                          uint8_t* cache) {
+  using G = GeoM<DK, DV>;
   constexpr int K = N / 2;                 // 16-byte chunks per lane stream
   constexpr bool PIV = (N == 16);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int rb = l % G::RB, cb = l / G::RB;
-  const int j0 = w * G::CPW + 4 * cb;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
   uint8_t* codes = tile;
   uint16_t* scl = (uint16_t*)(tile + DK * DV * N / 8);   // sigma[DK], c[DV]
-  // row-stage assignment: slot rho of the [rb][r] order, row irow
   const int rho = tid / G::TPR, rsub = tid % G::TPR;
-  const int irow = (rho >> 4) + G::RB * (rho & 15);
   float Y[64];
 
   if constexpr (MODE == MODE_STEP) {
+    // ---- every global load of the tile first: one memory latency per tile ----
     uint32_t raw[2 * N];
     f16x2 P[32];
-    float cc[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-    for (int k = 0; k < K; k++)
-      *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+    for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+    constexpr int NS = DK / 64;
+    float sa[NS], ss[NS];                  // gate and row scale of rows l + 64 s
+#pragma unroll
+    for (int q = 0; q < NS; q++) {
+      sa[q] = A.gate ? A.a[x * DK + l + 64 * q] : 1.f;
+      ss[q] = PIV ? 1.f : bf16f(scl[l + 64 * q]);
+    }
+    const float a_h = A.gate ? 1.f : A.a[x];
+    float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
+    float ar = A.gate ? A.a[x * DK + rho] : a_h;
+    float sr = PIV ? 1.f : bf16f(scl[rho]);
+    float wgt = A.weights[(size_t)h * DK + rho];
+    const float bb = A.b[x];
+    float vv[G::NCC], cc[G::NCC];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) {
+      const int j = w * G::CPW + 16 * c + n16;
+      vv[c] = A.v[x * DV + j];
+      cc[c] = PIV ? 1.f : bf16f(scl[DK + j]);
+    }
+    // Keep every loaded value here: no load may sink past this point into a
+    // branch (a late wait there would stall on the tile's stores, which share
+    // the vector memory counter)
+    pin(kk); pin(qq); pin(ar); pin(sr); pin(wgt);
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) { pin(vv[c]); pin(cc[c]); }
+    // binary16 range of the matvec operand: scale by the tile's largest g = a sigma
+    float gl = 0.f;
+#pragma unroll
+    for (int q = 0; q < NS; q++) gl = __builtin_fmaxf(gl, (sa[q] * a_h) * ss[q]);
+    float sc, inv;
+    fp16_scale(wave_max_pos(gl), sc, inv);
     // ---- per-row factors (once per row) ----
-    float ai = 1.f, kq = 0.f;
+    const float g = ar * sr;
+    float kq = 0.f;
     if (rsub == 0) {
-      float kk = A.k[x * DK + irow], qq = A.q[x * DK + irow];
-      ai = A.gate ? A.a[x * DK + irow] : A.a[x];
-      float sg = PIV ? 1.f : bf16f(scl[irow]);
-      float g = ai * sg;
-      sm.alpha[rho] = g * kk;
-      sm.beta[rho] = g * qq;
+      const float gs = g * sc;
+      put_afr<DK, DV, N>(sm, rho, gs * kk, gs * qq);
       sm.kappa[rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(g);   // pivots update S' directly
       sm.gg[rho] = g;
       kq = kk * qq;
     }
     kq = wave_sum(kq);
-    const bool ne1 = __ballot(ai != 1.f) != 0;
+    const bool ne1 = __ballot(ar != 1.f) != 0;
     if (l == 0) { sm.kqp[w] = kq; sm.notone[w] = ne1; }
     __syncthreads();
     int allone = 1;
-#pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) allone &= !sm.notone[ww];
-    // ---- u = A^T k, w = A^T q ----
-    unpack<N>(raw, P);
-    float al[16], be[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) {
-      *(f32x4*)&al[4 * r4] = *(const f32x4*)&sm.alpha[rb * 16 + 4 * r4];
-      *(f32x4*)&be[4 * r4] = *(const f32x4*)&sm.beta[rb * 16 + 4 * r4];
-    }
-    float U[4] = {0.f, 0.f, 0.f, 0.f}, Wr[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        float qv = code_at<N>(P, r, c);
-        U[c] = __builtin_fmaf(qv, al[r], U[c]);
-        Wr[c] = __builtin_fmaf(qv, be[r], Wr[c]);
-      }
-    if constexpr (!PIV) {
-      u32x2 cw = *(const u32x2*)(scl + DK + j0);
-      cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
-      cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
-    }
     float kqs = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqp[ww];
-    const float bb = A.b[x];
-    const f32x4 vv = *(const f32x4*)(A.v + x * DV + j0);
-    float delta[4];
-    f32x4 ov;
+    for (int ww = 0; ww < G::NW; ww++) { allone &= !sm.notone[ww]; kqs += sm.kqp[ww]; }
+    // ---- u = A^T k, w = A^T q on the matrix cores; readout ----
+    unpack<N>(raw, P);
+    f32x4 D[G::NCC];
+    matvec<DK, DV>(sm, P, D);
+    float delta[G::NCC];
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      float u = cc[c] * rb_sum<G::RB>(U[c]);
-      float wq = cc[c] * rb_sum<G::RB>(Wr[c]);
+    for (int c = 0; c < G::NCC; c++) {
+      const int j = w * G::CPW + 16 * c + n16;
+      const float u = cc[c] * ((D[c][0] + D[c][1]) * inv);
+      const float wq = cc[c] * ((D[c][2] + D[c][3]) * inv);
       delta[c] = bb * (vv[c] - u);
-      ov[c] = __builtin_fmaf(delta[c], kqs, wq);
+      if (Gq == 0) A.o[x * DV + j] = __builtin_fmaf(delta[c], kqs, wq);
     }
-    if (rb == 0) *(f32x4*)(A.o + x * DV + j0) = ov;
     if (bb == 0.f && allone) return;      // identity update: keep the encoding
-    float ka[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&ka[4 * r4] = *(const f32x4*)&sm.kappa[rb * 16 + 4 * r4];
     opaque(P);
-    if constexpr (PIV) {
-      // S' = fma(k, delta, g H): two roundings on the way to binary16
-      float gr[16];
+    // ---- Y = C + kappa delta^T, C = c Q (pivot tile: C = g H, kappa = k) ----
 #pragma unroll
-      for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&gr[4 * r4] = *(const f32x4*)&sm.gg[rb * 16 + 4 * r4];
+    for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
-      for (int r = 0; r < 16; r++)
+      for (int hf = 0; hf < 2; hf++) {
+        const float kr = sm.kappa[32 * rc + 16 * hf + n16];
+        const float kv = Gq == 0 ? kr : 0.f;
+        f32x4 gr4 = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (PIV) gr4 = *(const f32x4*)&sm.gg[erow(rc, 4 * hf, Gq)];
 #pragma unroll
-        for (int c = 0; c < 4; c++)
-          Y[4 * r + c] = __builtin_fmaf(ka[r], delta[c], gr[r] * code_at<N>(P, r, c));
-    } else {
-      // S' / g in registers: Y = c Q + (k / g) delta
+        for (int c = 0; c < G::NCC; c++) {
+          const int e0 = 8 * (c * G::NRC + rc) + 4 * hf;
+          // fma with a +0 addend: one v_fma_mix_f32 per code, straight from fp16
+          f32x4 C;
 #pragma unroll
-      for (int r = 0; r < 16; r++)
+          for (int i = 0; i < 4; i++) C[i] = __builtin_fmaf(code_e<N>(P, e0 + i), PIV ? gr4[i] : cc[c], 0.0f);
+          C = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, Gq == 0 ? delta[c] : 0.f, C, 0, 0, 0);
 #pragma unroll
-        for (int c = 0; c < 4; c++)
-          Y[4 * r + c] = __builtin_fmaf(code_at<N>(P, r, c), cc[c], ka[r] * delta[c]);
-    }
+          for (int i = 0; i < 4; i++) Y[e0 + i] = C[i];
+        }
+      }
+    refit_store<DK, DV, N, false>(sm, Y, tile, wgt);
   } else {
     // ---- store: Y = the given fp32 tile, g = 1 ----
     const float* S = A.S_in ? A.S_in + x * DK * DV : nullptr;
+    const float wgt = A.weights[(size_t)h * DK + rho];
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      f32x4 s4 = S ? *(const f32x4*)(S + (size_t)(rb + G::RB * r) * DV + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; c++) Y[4 * r + c] = s4[c];
+    for (int e = 0; e < 64; e++) {
+      const int b = e >> 3, t = e & 7;
+      const int i = erow(b % G::NRC, t, Gq), j = w * G::CPW + 16 * (b / G::NRC) + n16;
+      Y[e] = S ? S[(size_t)i * DV + j] : 0.f;
     }
     if (rsub == 0) sm.gg[rho] = 1.f;
     if (cache) {
@@ -304,13 +433,13 @@ __device__ __forceinline__ void tile_body(const KArgs& A, Smem<DK, DV>& sm, uint
       constexpr int TS = (TB + 255) / 256 * 256;
       for (int off = TB + 16 * tid; off < TS; off += 16 * G::NT) *(u32x4*)(tile + off) = u32x4{0u, 0u, 0u, 0u};
     }
+    refit_store<DK, DV, N, true>(sm, Y, tile, wgt);
   }
-  refit_store<DK, DV, N, MODE == MODE_STORE>(A, sm, Y, tile, h);
 }
 
 template <int DK, int DV, int MODE>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_tile(KArgs A) {
-  __shared__ Smem<DK, DV> sm;
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_tile(KArgs A) {
+  __shared__ SmemM<DK, DV> sm;
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
@@ -338,22 +467,19 @@ constexpr int WMAX = 32;
 
 template <int DK>
 struct WSmem {
-  float kap[WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i), [s][rb][r]
+  float kap[WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i), natural row order
   float cfk[WMAX];                                        // (G_t/G_s) k_s.k_t
   float cfq[WMAX];                                        // (G_t/G_s) k_s.q_t
 };
 
 template <int DK, int DV, int N, bool FLUSH>
-__device__ __forceinline__ void window_body(const KArgs& A, Smem<DK, DV>& sm, WSmem<DK>& ws, uint8_t* tile,
+__device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK>& ws, uint8_t* tile,
                                             uint8_t* cache, size_t x, int h) {
-  using G = Geo<DK, DV>;
+  using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
   constexpr bool PIV = (N == 16);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int rb = l % G::RB, cb = l / G::RB;
-  const int j0 = w * G::CPW + 4 * cb;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
   const int rho = tid / G::TPR, rsub = tid % G::TPR;
-  const int irow = (rho >> 4) + G::RB * (rho & 15);
   uint8_t* codes = tile;
   const uint16_t* scl = (const uint16_t*)(tile + DK * DV * N / 8);
   const int W = A.W;
@@ -376,47 +502,49 @@ __device__ __forceinline__ void window_body(const KArgs& A, Smem<DK, DV>& sm, WS
   f16x2 P[32];
 #pragma unroll
   for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
-  float cc[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (!PIV) {
-    u32x2 cw = *(const u32x2*)(scl + DK + j0);
-    cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
-    cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
+  float cc[G::NCC];
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) cc[c] = PIV ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
+  float sc = 1.f, inv = 1.f;
+  if constexpr (!FLUSH) {
+    float gl = 0.f;
+#pragma unroll
+    for (int i = l; i < DK; i += 64) gl = __builtin_fmaxf(gl, PIV ? 1.f : bf16f(scl[i]));
+    fp16_scale(wave_max_pos(gl), sc, inv);
   }
   // ---- per-row work (once per row) ----
   float kq = 0.f;
   if (rsub == 0) {
-    const float sg = PIV ? 1.f : bf16f(scl[irow]);
+    const float sg = PIV ? 1.f : bf16f(scl[rho]);
     if constexpr (!FLUSH) {
-      const float kk = A.k[x * DK + irow], qq = A.q[x * DK + irow];
-      sm.alpha[rho] = sg * kk;
-      sm.beta[rho] = sg * qq;
+      const float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
+      put_afr<DK, DV, N>(sm, rho, (sg * sc) * kk, (sg * sc) * qq);
       kq = kk * qq;
-      Kc[(size_t)t * DK + irow] = kk;                       // append k_t
+      Kc[(size_t)t * DK + rho] = kk;                       // append k_t
       if (fold) ws.kap[t * DK + rho] = kk / (Gt * sg);
     }
     if (fold) {
-      for (int s = 0; s < t; s++) ws.kap[s * DK + rho] = Kc[(size_t)s * DK + irow] / (Gc[s] * sg);
+      for (int s = 0; s < t; s++) ws.kap[s * DK + rho] = Kc[(size_t)s * DK + rho] / (Gc[s] * sg);
       sm.gg[rho] = Gt * sg;
     }
   }
   if constexpr (!FLUSH) {
     kq = wave_sum(kq);
     if (l == 0) sm.kqp[w] = kq;
-    // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: RB consecutive lanes per dot
-    for (int sd = tid / G::RB; sd < 2 * t; sd += G::NT / G::RB) {
+    // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per dot
+    for (int sd = tid / 8; sd < 2 * t; sd += G::NT / 8) {
       const int s = sd % t;
       const float* vec = (sd < t ? A.k : A.q) + x * DK;
-      const int i0 = 16 * (tid % G::RB);
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i0 + i);
-        f32x4 vv = *(const f32x4*)(vec + i0 + i);
+      for (int i = 4 * (tid % 8); i < DK; i += 32) {
+        const f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i);
+        const f32x4 vv = *(const f32x4*)(vec + i);
         acc = __builtin_fmaf(ks[0], vv[0], acc); acc = __builtin_fmaf(ks[1], vv[1], acc);
         acc = __builtin_fmaf(ks[2], vv[2], acc); acc = __builtin_fmaf(ks[3], vv[3], acc);
       }
-      acc = rb_sum<G::RB>(acc);
-      if (tid % G::RB == 0) {
+      acc = rb_sum<8>(acc);
+      if (tid % 8 == 0) {
         const float f = (Gt / Gc[s]) * acc;
         if (sd < t) ws.cfk[s] = f; else ws.cfq[s] = f;
       }
@@ -424,54 +552,39 @@ __device__ __forceinline__ void window_body(const KArgs& A, Smem<DK, DV>& sm, WS
   }
   __syncthreads();
   unpack<N>(raw, P);
-  float u4[4] = {0.f, 0.f, 0.f, 0.f};
+  float u2[G::NCC];
   if constexpr (!FLUSH) {
     // ---- readout and written vector from the frozen base and the cache ----
-    float al[16], be[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) {
-      *(f32x4*)&al[4 * r4] = *(const f32x4*)&sm.alpha[rb * 16 + 4 * r4];
-      *(f32x4*)&be[4 * r4] = *(const f32x4*)&sm.beta[rb * 16 + 4 * r4];
-    }
-    float U[4] = {0.f, 0.f, 0.f, 0.f}, Wr[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        float qv = code_at<N>(P, r, c);
-        U[c] = __builtin_fmaf(qv, al[r], U[c]);
-        Wr[c] = __builtin_fmaf(qv, be[r], Wr[c]);
-      }
     float kqs = 0.f;
 #pragma unroll
     for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqp[ww];
+    f32x4 D[G::NCC];
+    matvec<DK, DV>(sm, P, D);
     const float bb = A.b[x];
-    const f32x4 vv = *(const f32x4*)(A.v + x * DV + j0);
-    float rr[4], oo[4];
+    float rr[G::NCC], oo[G::NCC];
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      rr[c] = vv[c] - Gt * (cc[c] * rb_sum<G::RB>(U[c]));
-      oo[c] = Gt * (cc[c] * rb_sum<G::RB>(Wr[c]));
+    for (int c = 0; c < G::NCC; c++) {
+      const int j = w * G::CPW + 16 * c + n16;
+      rr[c] = A.v[x * DV + j] - Gt * (cc[c] * ((D[c][0] + D[c][1]) * inv));
+      oo[c] = Gt * (cc[c] * ((D[c][2] + D[c][3]) * inv));
     }
     for (int s = 0; s < t; s++) {
-      const f32x4 us = *(const f32x4*)(Uc + (size_t)s * DV + j0);
       const float fk = ws.cfk[s], fq = ws.cfq[s];
 #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        rr[c] = __builtin_fmaf(-fk, us[c], rr[c]);
-        oo[c] = __builtin_fmaf(fq, us[c], oo[c]);
+      for (int c = 0; c < G::NCC; c++) {
+        const float us = Uc[(size_t)s * DV + w * G::CPW + 16 * c + n16];
+        rr[c] = __builtin_fmaf(-fk, us, rr[c]);
+        oo[c] = __builtin_fmaf(fq, us, oo[c]);
       }
     }
-    f32x4 ov, uv;
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      u4[c] = bb * rr[c];
-      uv[c] = u4[c];
-      ov[c] = __builtin_fmaf(kqs, u4[c], oo[c]);
-    }
-    if (rb == 0) {
-      *(f32x4*)(A.o + x * DV + j0) = ov;
-      *(f32x4*)(Uc + (size_t)t * DV + j0) = uv;           // append u_t
+    for (int c = 0; c < G::NCC; c++) {
+      const int j = w * G::CPW + 16 * c + n16;
+      u2[c] = bb * rr[c];
+      if (Gq == 0) {
+        A.o[x * DV + j] = __builtin_fmaf(kqs, u2[c], oo[c]);
+        Uc[(size_t)t * DV + j] = u2[c];                     // append u_t
+      }
     }
     if (tid == 0) {
       Gc[t] = Gt;
@@ -483,40 +596,42 @@ __device__ __forceinline__ void window_body(const KArgs& A, Smem<DK, DV>& sm, WS
   opaque(P);
   float Y[64];
 #pragma unroll
-  for (int r = 0; r < 64; r++) Y[r] = 0.f;
-  for (int s = 0; s < ns; s++) {
-    f32x4 us;
-    if (!FLUSH && s == t) us = f32x4{u4[0], u4[1], u4[2], u4[3]};
-    else us = *(const f32x4*)(Uc + (size_t)s * DV + j0);
-    float kp[16];
+  for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&kp[4 * r4] = *(const f32x4*)&ws.kap[s * DK + rb * 16 + 4 * r4];
+    for (int hf = 0; hf < 2; hf++) {
+      const int r0 = 32 * rc + 16 * hf;
+      f32x4 C[G::NCC];
 #pragma unroll
-    for (int r = 0; r < 16; r++)
+      for (int c = 0; c < G::NCC; c++) {
+        const int e0 = 8 * (c * G::NRC + rc) + 4 * hf;
 #pragma unroll
-      for (int c = 0; c < 4; c++) Y[4 * r + c] = __builtin_fmaf(kp[r], us[c], Y[4 * r + c]);
-  }
-  if constexpr (PIV) {
-    float gr[16];
+        for (int i = 0; i < 4; i++) C[c][i] = __builtin_fmaf(code_e<N>(P, e0 + i), cc[c], 0.0f);
+      }
+      // four rank-one terms per MFMA: lane quad G carries token s0 + G
+      for (int s0 = 0; s0 < ns; s0 += 4) {
+        const int s = s0 + Gq;
+        const float kv = s < ns ? ws.kap[s * DK + r0 + n16] : 0.f;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&gr[4 * r4] = *(const f32x4*)&sm.gg[rb * 16 + 4 * r4];
+        for (int c = 0; c < G::NCC; c++) {
+          float uv = 0.f;
+          if (s < ns) uv = (!FLUSH && s == t) ? u2[c] : Uc[(size_t)s * DV + w * G::CPW + 16 * c + n16];
+          C[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, uv, C[c], 0, 0, 0);
+        }
+      }
 #pragma unroll
-    for (int r = 0; r < 16; r++)
+      for (int c = 0; c < G::NCC; c++) {
+        const int e0 = 8 * (c * G::NRC + rc) + 4 * hf;
 #pragma unroll
-      for (int c = 0; c < 4; c++) Y[4 * r + c] = gr[r] * (code_at<N>(P, r, c) + Y[4 * r + c]);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) Y[4 * r + c] = __builtin_fmaf(code_at<N>(P, r, c), cc[c], Y[4 * r + c]);
-  }
+        for (int i = 0; i < 4; i++) Y[e0 + i] = PIV ? Gt * C[c][i] : C[c][i];
+      }
+    }
   if (tid == 0) *cntp = 0;
-  refit_store<DK, DV, N, false>(A, sm, Y, tile, h);
+  refit_store<DK, DV, N, false>(sm, Y, tile, A.weights[(size_t)h * DK + rho]);
 }
 
 template <int DK, int DV, bool FLUSH>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_window(KArgs A) {
-  __shared__ Smem<DK, DV> sm;
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) void k_window(KArgs A) {
+  __shared__ SmemM<DK, DV> sm;
   __shared__ WSmem<DK> ws;
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
@@ -890,15 +1005,13 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_rows(KArgs A) {
 }
 
 // ------------------------------------------------------------------------
-// Fetch (D) and fixed-scale requantization.
+// Fetch (D) and fixed-scale requantization of per-head tiles.
 // ------------------------------------------------------------------------
 template <int DK, int DV, int N, bool REQ>
 __device__ __forceinline__ void fetch_body(const KArgs& A, uint8_t* tile, size_t x) {
-  using G = Geo<DK, DV>;
+  using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int rb = l % G::RB, cb = l / G::RB;
-  const int j0 = w * G::CPW + 4 * cb;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
   uint8_t* codes = tile;
   const uint16_t* scl = (const uint16_t*)(tile + DK * DV * N / 8);
   uint32_t raw[2 * N];
@@ -906,43 +1019,26 @@ __device__ __forceinline__ void fetch_body(const KArgs& A, uint8_t* tile, size_t
 #pragma unroll
   for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
   unpack<N>(raw, P);
-  float sg[16], cc[4] = {1.f, 1.f, 1.f, 1.f};
+  float cc[G::NCC];
 #pragma unroll
-  for (int r = 0; r < 16; r++) sg[r] = (N == 16) ? 1.f : bf16f(scl[rb + G::RB * r]);
-  if (N != 16) {
-    u32x2 cw = *(const u32x2*)(scl + DK + j0);
-    cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
-    cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
-  }
-  float Y[64];
+  for (int c = 0; c < G::NCC; c++) cc[c] = N == 16 ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
+  uint32_t yb[64];
 #pragma unroll
-  for (int r = 0; r < 16; r++)
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      float qv = code_at<N>(P, r, c);
-      Y[4 * r + c] = (N == 16) ? qv : (sg[r] * cc[c]) * qv;
+  for (int e = 0; e < 64; e++) {
+    const int b = e >> 3, t = e & 7, c = b / G::NRC;
+    const int i = erow(b % G::NRC, t, Gq), j = w * G::CPW + 16 * c + n16;
+    const float qv = code_e<N>(P, e);
+    const float sg = N == 16 ? 1.f : bf16f(scl[i]);
+    const float v = N == 16 ? qv : (sg * cc[c]) * qv;        // D: fl(fl(sigma c) Q)
+    if constexpr (!REQ) {
+      A.S_out[x * DK * DV + (size_t)i * DV + j] = v;
+    } else if constexpr (N != 16) {
+      float q = __builtin_fmaf(v * rcp_bf16(sg), rcp_bf16(cc[c]), Fmt<N>::MAGIC);
+      q = __builtin_fminf(__builtin_fmaxf(q, Fmt<N>::MAGIC - Fmt<N>::QMAX), Fmt<N>::MAGIC + Fmt<N>::QMAX);
+      yb[e] = __float_as_uint(q);
     }
-  if constexpr (!REQ) {
-    float* S = A.S_out + x * DK * DV;
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-      *(f32x4*)(S + (size_t)(rb + G::RB * r) * DV + j0) = f32x4{Y[4 * r], Y[4 * r + 1], Y[4 * r + 2], Y[4 * r + 3]};
-  } else if constexpr (N != 16) {
-    float rs[16], rc[4];
-#pragma unroll
-    for (int r = 0; r < 16; r++) rs[r] = rcp_bf16(sg[r]);
-#pragma unroll
-    for (int c = 0; c < 4; c++) rc[c] = rcp_bf16(cc[c]);
-    uint32_t yb[64];
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        float X = Y[4 * r + c] * rs[r];
-        float q = __builtin_fmaf(X, rc[c], Fmt<N>::MAGIC);
-        q = __builtin_fminf(__builtin_fmaxf(q, Fmt<N>::MAGIC - Fmt<N>::QMAX), Fmt<N>::MAGIC + Fmt<N>::QMAX);
-        yb[4 * r + c] = __float_as_uint(q);
-      }
+  }
+  if constexpr (REQ && N != 16) {
     pack<N>(yb, raw);
 #pragma unroll
     for (int k = 0; k < K; k++) *(u32x4*)(codes + 16 * ((w * K + k) * 64 + l)) = *(const u32x4*)&raw[4 * k];
@@ -950,7 +1046,7 @@ __device__ __forceinline__ void fetch_body(const KArgs& A, uint8_t* tile, size_t
 }
 
 template <int DK, int DV, bool REQ>
-__global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_fetch(KArgs A) {
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) void k_fetch(KArgs A) {
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
@@ -1079,7 +1175,7 @@ struct LTile {
   template <int DK, int DV>
   struct T {
     static void go(const KArgs& A, unsigned g, hipStream_t st) {
-      hipLaunchKernelGGL((k_tile<DK, DV, MODE>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
+      hipLaunchKernelGGL((k_tile<DK, DV, MODE>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
     }
   };
 };
@@ -1097,7 +1193,7 @@ struct LWindow {
   template <int DK, int DV>
   struct T {
     static void go(const KArgs& A, unsigned g, hipStream_t st) {
-      hipLaunchKernelGGL((k_window<DK, DV, FLUSH>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
+      hipLaunchKernelGGL((k_window<DK, DV, FLUSH>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
     }
   };
 };
@@ -1106,7 +1202,7 @@ struct LFetch {
   template <int DK, int DV>
   struct T {
     static void go(const KArgs& A, unsigned g, hipStream_t st) {
-      hipLaunchKernelGGL((k_fetch<DK, DV, REQ>), dim3(g), dim3(Geo<DK, DV>::NT), 0, st, A);
+      hipLaunchKernelGGL((k_fetch<DK, DV, REQ>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
     }
   };
 };
