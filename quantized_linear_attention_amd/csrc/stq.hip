@@ -90,7 +90,7 @@ struct GeoM {
   static constexpr int NT = 64 * NW;
   static constexpr int TPR = NT / DK;       // threads per row in the row stage
   static constexpr int NP = NW * 16;        // partial row maxima per row
-  static constexpr int PSTR = DK + 4;       // LDS stride of one partial set
+  static constexpr int PSTR = NP + 4;       // LDS row stride of the partials (2-way optimal writes)
   static_assert(DK == 64 || DK == 128, "d_k");
   static_assert(NW >= 1 && DV % CPW == 0, "d_v");
   static_assert(TPR == 1 || TPR == 2, "threads per row");
@@ -101,14 +101,12 @@ typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 template <int DK, int DV>
 struct SmemM {
   f16 afr[DK / 32][4][4][8] __attribute__((aligned(16)));   // [rc][G][v][k]: matvec A fragments
-  float kappa[DK] __attribute__((aligned(16)));             // natural row order
+  float kappa[2][DK] __attribute__((aligned(16)));          // natural row order; [1]: zeros
   float gg[DK] __attribute__((aligned(16)));
   float rowh[DK] __attribute__((aligned(16)));
-  float part[GeoM<DK, DV>::NP * GeoM<DK, DV>::PSTR] __attribute__((aligned(16)));
-  float kqp[GeoM<DK, DV>::NW];
-  int notone[GeoM<DK, DV>::NW];
-  int esum[GeoM<DK, DV>::NW];
-  int ecnt[GeoM<DK, DV>::NW];
+  float part[DK * GeoM<DK, DV>::PSTR] __attribute__((aligned(16)));   // [row][partial]
+  f32x2 kqn[GeoM<DK, DV>::NW];   // per wave: k.q partial sum, 1 if some gate differs from 1
+  int epk[GeoM<DK, DV>::NW];     // per wave: sum of row exponents * 256 + row count
 };
 
 // element t (0..7) of the lane's two groups of a chunk -> k index of its
@@ -220,23 +218,24 @@ __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t
     for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
       for (int hf = 0; hf < 2; hf++) {
-        f32x4 m4;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           float m = 0.f;
 #pragma unroll
           for (int cc = 0; cc < G::NCC; cc++)
             m = __builtin_fmaxf(m, __builtin_fabsf(Y[8 * (cc * G::NRC + rc) + 4 * hf + i]));
-          m4[i] = m;
+          sm.part[(erow(rc, 4 * hf, Gq) + i) * G::PSTR + w * 16 + n16] = m;
         }
-        *(f32x4*)&sm.part[(w * 16 + n16) * G::PSTR + erow(rc, 4 * hf, Gq)] = m4;
       }
-    __syncthreads();
+    lds_barrier();
+    // row stage: each of the TPR threads of row rho reduces a contiguous run
     uint32_t mxb = 0u;                              // non-negative: compare bit patterns
+    const float* pr = &sm.part[rho * G::PSTR + rsub * (G::NP / G::TPR)];
 #pragma unroll
-    for (int p = 0; p < G::NP / G::TPR; p++) {
-      const int pp = 4 * (G::TPR * (p >> 2) + rsub) + (p & 3);
-      mxb = __builtin_elementwise_max(mxb, __float_as_uint(sm.part[pp * G::PSTR + rho]));
+    for (int p = 0; p < G::NP / G::TPR; p += 4) {
+      const u32x4 v4 = *(const u32x4*)(pr + p);
+      mxb = __builtin_elementwise_max(mxb, __builtin_elementwise_max(__builtin_elementwise_max(v4[0], v4[1]),
+                                                                     __builtin_elementwise_max(v4[2], v4[3])));
     }
     if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)dppi<0xB1>((int)mxb));
     const float g = sm.gg[rho];
@@ -253,11 +252,13 @@ __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t
     if (rsub != 0) epk = 0;
     if (rsub == 0) sm.rowh[rho] = g * rcp_bf16(bf16f(s));
     epk = wave_sum_i(epk);
-    if (l == 0) { sm.esum[w] = epk >> 8; sm.ecnt[w] = epk & 0xFF; }
-    __syncthreads();
-    int es = 0, ec = 0;
+    if (l == 0) sm.epk[w] = epk;
+    lds_barrier();
+    int et = 0;                                    // packed sums add up: count < 256
 #pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) { es += sm.esum[ww]; ec += sm.ecnt[ww]; }
+    for (int ww = 0; ww < G::NW; ww++) et += sm.epk[ww];
+    et = __builtin_amdgcn_readfirstlane(et);
+    const int es = et >> 8, ec = et & 0xFF;
     const int E = ec ? mean_exp(es, ec) : 0;
     if (rsub == 0) scl[rho] = (uint16_t)bf16_adj(s, -E);
     // ---- column refit: X = Y h, column absmax over the wave's 4 row quads ----
@@ -360,18 +361,19 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     if (rsub == 0) {
       const float gs = g * sc;
       put_afr<DK, DV, N>(sm, rho, gs * kk, gs * qq);
-      sm.kappa[rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(g);   // pivots update S' directly
+      sm.kappa[0][rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(g);   // pivots update S' directly
+      sm.kappa[1][rho] = 0.f;
       sm.gg[rho] = g;
       kq = kk * qq;
     }
     kq = wave_sum(kq);
     const bool ne1 = __ballot(ar != 1.f) != 0;
-    if (l == 0) { sm.kqp[w] = kq; sm.notone[w] = ne1; }
-    __syncthreads();
-    int allone = 1;
-    float kqs = 0.f;
+    if (l == 0) sm.kqn[w] = f32x2{kq, ne1 ? 1.f : 0.f};
+    lds_barrier();
+    float kqs = 0.f, nes = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) { allone &= !sm.notone[ww]; kqs += sm.kqp[ww]; }
+    for (int ww = 0; ww < G::NW; ww++) { const f32x2 t = sm.kqn[ww]; kqs += t[0]; nes += t[1]; }
+    const bool allone = nes == 0.f;
     // ---- u = A^T k, w = A^T q on the matrix cores; readout ----
     unpack<N>(raw, P);
     f32x4 D[G::NCC];
@@ -388,12 +390,17 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     if (bb == 0.f && allone) return;      // identity update: keep the encoding
     opaque(P);
     // ---- Y = C + kappa delta^T, C = c Q (pivot tile: C = g H, kappa = k) ----
+    // One rank-one term per MFMA: lane quad G = 0 carries kappa and delta,
+    // the other quads zeros (their kappa row in LDS is zero).
+    const float* kap = sm.kappa[Gq == 0 ? 0 : 1];
+    float db[G::NCC];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) db[c] = Gq == 0 ? delta[c] : 0.f;
 #pragma unroll
     for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
       for (int hf = 0; hf < 2; hf++) {
-        const float kr = sm.kappa[32 * rc + 16 * hf + n16];
-        const float kv = Gq == 0 ? kr : 0.f;
+        const float kv = kap[32 * rc + 16 * hf + n16];
         f32x4 gr4 = {1.f, 1.f, 1.f, 1.f};
         if constexpr (PIV) gr4 = *(const f32x4*)&sm.gg[erow(rc, 4 * hf, Gq)];
 #pragma unroll
@@ -403,7 +410,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
           f32x4 C;
 #pragma unroll
           for (int i = 0; i < 4; i++) C[i] = __builtin_fmaf(code_e<N>(P, e0 + i), PIV ? gr4[i] : cc[c], 0.0f);
-          C = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, Gq == 0 ? delta[c] : 0.f, C, 0, 0, 0);
+          C = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, db[c], C, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; i++) Y[e0 + i] = C[i];
         }
@@ -444,12 +451,12 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   const int tau = tile_of_block(T);
   if (tau >= T) return;
   const int ci = tau / A.H, h = tau - ci * A.H;
-  const int slot = A.slots ? A.slots[ci] : ci;
+  const int slot = A.slots ? ld_const(A.slots + ci) : ci;
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
-  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + ld_const(A.head_off + h);
   uint8_t* cache = A.W ? A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride : nullptr;
   const size_t x = (size_t)ci * A.H + h;
-  switch (A.head_bits[h]) {
+  switch (ld_const(A.head_bits + h)) {
     case 4: tile_body<DK, DV, MODE, 4>(A, sm, tile, x, h, cache); break;
     case 6: tile_body<DK, DV, MODE, 6>(A, sm, tile, x, h, cache); break;
     case 8: tile_body<DK, DV, MODE, 8>(A, sm, tile, x, h, cache); break;
@@ -530,7 +537,7 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
   }
   if constexpr (!FLUSH) {
     kq = wave_sum(kq);
-    if (l == 0) sm.kqp[w] = kq;
+    if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
     // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per dot
     for (int sd = tid / 8; sd < 2 * t; sd += G::NT / 8) {
       const int s = sd % t;
@@ -557,7 +564,7 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
     // ---- readout and written vector from the frozen base and the cache ----
     float kqs = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqp[ww];
+    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
     f32x4 D[G::NCC];
     matvec<DK, DV>(sm, P, D);
     const float bb = A.b[x];

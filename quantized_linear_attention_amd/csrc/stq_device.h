@@ -11,6 +11,7 @@ typedef _Float16 f16;
 typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -74,6 +75,18 @@ template <> struct Fmt<4>  { static constexpr int QMAX = 7;   static constexpr f
 template <> struct Fmt<6>  { static constexpr int QMAX = 31;  static constexpr float MAGIC = 8388640.0f; };   // 2^23 + 32
 template <> struct Fmt<8>  { static constexpr int QMAX = 127; static constexpr float MAGIC = 8388736.0f; };   // 2^23 + 128
 template <> struct Fmt<16> { static constexpr int QMAX = 0;   static constexpr float MAGIC = 0.0f; };
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its vector-memory ones (stores in flight stay in
+// flight; a fenced __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Load from memory that no kernel writes while it runs (call tables, pool
+// header): the constant address space lets it go through the scalar cache.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
 
 // --------------------------------------------------------------- DPP
 template <int CTRL>
