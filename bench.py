@@ -12,8 +12,10 @@ Prints one JSON line with throughput, the dominant kernel's roofline figure
 stream) and the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,6 +35,32 @@ def algorithmic_bytes(bits, H, dk, dv, B, gate_per_row=False):
         tile += 2 * (dk * dv * n // 8 + (0 if n == 16 else 2 * (dk + dv)))
     io = 4 * (2 * dk + dv) + 4 * (dk if gate_per_row else 1) + 4 + 4 * dv
     return B * (tile + H * io)
+
+
+def kernel_source_hash():
+    """sha256[:16] of the decode-step kernel sources, as the profile summaries record it."""
+    h = hashlib.sha256()
+    for f in ("stq.hip", "stq_device.h"):
+        with open(os.path.join(ROOT, "quantized_linear_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per step launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (counters scaled by a plain-copy calibration), or None when the kernel
+    sources differ from the ones that were measured."""
+    path = os.path.join(ROOT, "profiles", "k_tile_step_C3_hbm_traffic.txt")
+    try:
+        with open(path) as fh:
+            txt = fh.read()
+    except OSError:
+        return None
+    h = re.search(r"kernel source sha256\[:16\] \(stq.hip \+ stq_device.h\): (\w+)", txt)
+    t = re.search(r"traffic_bytes_per_launch: (\d+)", txt)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
 
 
 def main():
@@ -140,6 +168,7 @@ def main():
                "sample": "%d calls x %d tiles of the same workload (B=%d slots, all 32 heads), %.1f s"
                          % (calls, ns * H, ns, el)}
 
+    traffic = measured_traffic()
     line = {
         "metric": "request-head decode steps/s (B=512, H=32, d=128, 6-bit nominal GDN pool)",
         "value": T * K / (total_ms * 1e-3),
@@ -154,7 +183,9 @@ def main():
                    "global_batch": B, "heads": H, "d_k": dk, "d_v": dv, "layers": L},
         "hbm_gbs": achieved, "hbm_frac": achieved / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "traffic_gbs": None if traffic is None else traffic / (avg_ms * 1e-3) / 1e9,
                      "kernel": "k_tile<128,128,step>", "bytes_per_launch": bytes_step,
                      "avg_launch_ms": avg_ms, "p10_ms": float(np.percentile(per, 10)),
                      "p90_ms": float(np.percentile(per, 90))},
