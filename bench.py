@@ -1,11 +1,13 @@
 """Benchmark of the quantized gated Delta-rule decode step on one MI355X.
 
-Workload: GDN serving pool, B=512 requests x H=32 heads, d_k=d_v=128, the
-6-bit nominal mix {4-bit: 9, 6-bit: 16, 8-bit: 6, FP16 pivot: 1 head} of
-heads, state resident in HBM.  One step = one decode token of one layer
-(stq_decode_step over all 16,384 (request, head) tiles).  L independent
-layer pools are stepped round-robin, as a model does, so the working set
-(L x 214 MB) exceeds the 256 MB Infinity Cache and the timing is HBM-bound.
+Default workload (C3): GDN serving pool, B=512 requests x H=32 heads,
+d_k=d_v=128, the 6-bit nominal mix {4-bit: 9, 6-bit: 16, 8-bit: 6, FP16
+pivot: 1 head} of heads, state resident in HBM.  One step = one decode token
+of one layer (stq_decode_step over all 16,384 (request, head) tiles).  L
+independent layer pools are stepped round-robin, as a model does, so the
+working set exceeds the 256 MB Infinity Cache and the timing is HBM-bound.
+`--workload C4` times the per-channel-gate, per-key-row-width pool (B=256)
+and `--workload C5` the windowed 4-bit pool (W=16, whole windows timed).
 
 Prints one JSON line with throughput, the dominant kernel's roofline figure
 (algorithmic bytes / average kernel duration, from HIP events on the launch
@@ -27,14 +29,42 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
-def algorithmic_bytes(bits, H, dk, dv, B, gate_per_row=False):
-    """Bytes the method must move per step: packed state read + write, the
-    q/k/v/a/b inputs and the readout.  Per-head metadata is excluded."""
-    tile = 0
-    for n in bits:
-        tile += 2 * (dk * dv * n // 8 + (0 if n == 16 else 2 * (dk + dv)))
-    io = 4 * (2 * dk + dv) + 4 * (dk if gate_per_row else 1) + 4 + 4 * dv
-    return B * (tile + H * io)
+def tile_bytes(bits, dk, dv):
+    """Packed bytes of one tile: codes, then the bf16 row and column scales.
+    `bits` is the tile's width (unit = head) or its per-key-row widths (unit =
+    key row); a binary16 pivot head carries no scales."""
+    b = np.atleast_1d(np.asarray(bits, np.int64))
+    if b.size == 1:
+        n = int(b[0])
+        return dk * dv * n // 8 + (0 if n == 16 else 2 * (dk + dv))
+    return int((dv * b // 8).sum()) + 2 * (dk + dv)
+
+
+def io_bytes(dk, dv, gate_per_row):
+    """q, k, v, a, b read and o written, per tile and token (binary32)."""
+    return 4 * (2 * dk + dv) + 4 * (dk if gate_per_row else 1) + 4 + 4 * dv
+
+
+def algorithmic_bytes(wl, pos=0):
+    """Bytes the method must move in one launch over all B x H tiles.
+
+    Per-head and per-key-row modes: the packed state read and written once,
+    plus the per-token inputs and readout.  Window mode at window position
+    `pos` (tokens already cached): the frozen base read, the pos cached
+    (Gamma, k, u) entries read, the new entry and the count written, the
+    inputs and readout, and at the window's last token the base written by
+    the fold.  Per-head metadata is excluded."""
+    c, H, dk, dv = wl.cfg, wl.H, wl.dk, wl.dv
+    per_row = wl.bits.ndim == 2
+    tiles = [tile_bytes(wl.bits[h], dk, dv) for h in range(H)]
+    io = io_bytes(dk, dv, c.gate == 1)
+    if c.window == 0:
+        return wl.B * sum(2 * t + io for t in tiles)
+    ent = 4 * (dk + dv + 1)
+    fold = pos + 1 == c.window
+    per = [t + 8 + pos * ent + ent + io + (t if fold else 0) for t in tiles]
+    assert not per_row
+    return wl.B * sum(per)
 
 
 def kernel_source_hash():
@@ -46,11 +76,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(key):
     """HBM bytes per step launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary (counters scaled by a plain-copy calibration), or None when the kernel
-    sources differ from the ones that were measured."""
-    path = os.path.join(ROOT, "profiles", "k_tile_step_C3_hbm_traffic.txt")
+    summary of the workload's step kernel (counters scaled by a plain-copy
+    calibration), or None when there is none or the kernel sources differ from
+    the ones that were measured."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.txt" % (BENCH[key]["prof"], key))
     try:
         with open(path) as fh:
             txt = fh.read()
@@ -63,12 +94,37 @@ def measured_traffic():
     return int(t.group(1))
 
 
+# Timed workloads.  C3 is the headline line; C4 (per-channel gate, per-key-row
+# widths) and C5 (windowed 4-bit) time the other step kernels the same way.
+# `layers` independent pools are stepped round-robin so that the working set
+# exceeds the 256 MB Infinity Cache (one layer's pool: C3 214 MB, C4 103 MB,
+# C5 415 MB with its window caches).
+BENCH = {
+    "C3": {"layers": 4, "kernel": "k_tile<128, 128, 0>", "prof": "k_tile_step",
+           "metric": "request-head decode steps/s (B=512, H=32, d=128, 6-bit nominal GDN pool)",
+           "workload": "GDN serving pool B=512 H=32 d_k=d_v=128, heads {4b:9, 6b:16, 8b:6, fp16:1}",
+           "dtype": "f32 update, 4/6/8-bit + f16 state"},
+    "C4": {"layers": 8, "kernel": "k_rows<128, 128, 0>", "prof": "k_rows_step",
+           "metric": "request-head decode steps/s (B=256, H=32, d=128, KDA per-channel gate, "
+                     "per-key-row widths)",
+           "workload": "KDA pool B=256 H=32 d_k=d_v=128, per-channel gate, key rows "
+                       "{4b:30%, 6b:50%, 8b:19%, fp16:1%}",
+           "dtype": "f32 update, per-key-row 4/6/8-bit + f16 state"},
+    "C5": {"layers": 2, "kernel": "k_window<128, 128, false>", "prof": "k_window_step",
+           "metric": "request-head decode steps/s (B=512, H=32, d=128, 4-bit GDN, window W=16)",
+           "workload": "windowed GDN pool B=512 H=32 d_k=d_v=128, all heads 4-bit, W=16 "
+                       "(binary32 window caches, one fold per 16 tokens)",
+           "dtype": "f32 update and window cache, 4-bit base state"},
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--workload", choices=sorted(BENCH), default="C3")
+    ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -93,12 +149,22 @@ def main():
     import quantized_linear_attention_amd as stq
     from workloads import Workload
 
+    key = args.workload
+    spec = BENCH[key]
     dev = torch.device("cuda:0")
-    wl = Workload("C3")
+    wl = Workload(key)
+    c = wl.cfg
     B, H, dk, dv = wl.B, wl.H, wl.dk, wl.dv
     T = B * H
-    L = args.layers
-    desc = stq.make_desc(B, H, dk, dv, wl.bits, wl.row_weight)
+    L = spec["layers"] if args.layers is None else args.layers
+    K, Wu = args.steps, args.warmup
+    if c.window:
+        # whole windows in the warm-up and in the timed region, so every pool
+        # enters the timed region with an empty window
+        span = L * c.window
+        K = max(span, -(-K // span) * span)
+        Wu = -(-Wu // span) * span
+    desc = stq.make_desc(B, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window)
     nbytes = stq.stq_pool_bytes(desc)
     slots = torch.arange(B, dtype=torch.int32, device=dev)
     gen = torch.Generator(device=dev)
@@ -110,9 +176,10 @@ def main():
         pool = stq.stq_pool_create(desc, buf)
         gen.manual_seed(wl.seed * 100 + layer)
         for c0 in range(0, B, 64):     # same recipe as workloads.Workload.state, drawn on the GPU
-            z = torch.randn((64, H, dk, dv), generator=gen, device=dev)
+            n = min(64, B - c0)
+            z = torch.randn((n, H, dk, dv), generator=gen, device=dev)
             S0 = (0.1 * z * r_prof[None, :, :, None] * c_prof[None, :, None, :]).contiguous()
-            stq.stq_pool_store(pool, slots[c0:c0 + 64].contiguous(), S0)
+            stq.stq_pool_store(pool, slots[c0:c0 + n].contiguous(), S0)
         pools.append(pool)
         bufs.append(buf)
     NTOK = 8
@@ -127,10 +194,9 @@ def main():
         q, k, v, a, b = toks[(s // L) % NTOK]
         stq.stq_decode_step(pools[s % L], slots, q, k, v, a, b, o)
 
-    for s in range(args.warmup):
+    for s in range(Wu):
         step(s)
     torch.cuda.synchronize()
-    K = args.steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -138,55 +204,59 @@ def main():
     start.record()
     for s in range(K):
         ev[s].record()
-        step(args.warmup + s)
+        step(Wu + s)
     ev[K].record()
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(K)])
     avg_ms = float(per.mean())
-    bytes_step = int(algorithmic_bytes([int(n) for n in wl.bits], H, dk, dv, B))
+    if c.window:
+        # launch s is token (Wu + s) // L of its pool: window position that mod W
+        pos = [((Wu + s) // L) % c.window for s in range(K)]
+        bytes_step = float(np.mean([algorithmic_bytes(wl, p) for p in pos]))
+    else:
+        bytes_step = float(algorithmic_bytes(wl))
     achieved = bytes_step / (avg_ms * 1e-3) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         oracle.build()
-        ns = 32                                    # slots per oracle call (1,024 tiles)
-        P = oracle.OraclePool(ns, H, dk, dv, wl.bits, wl.row_weight)
+        ns = 32 if key != "C4" else 16             # slots per oracle call
+        P = oracle.OraclePool(ns, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window)
         sl = np.arange(ns)
         P.store(sl, wl.state(sl))
-        q, k, v, a, b = wl.token(0, ns)
+        tk = [wl.token(t, ns) for t in range(NTOK)]
         calls = 0
         t0 = time.perf_counter()
-        while time.perf_counter() - t0 < args.cpu_seconds:
-            P.step(sl, q, k, v, a, b)
+        while time.perf_counter() - t0 < args.cpu_seconds or (c.window and calls % c.window):
+            P.step(sl, *tk[calls % NTOK])
             calls += 1
         el = time.perf_counter() - t0
         cpu = {"value": calls * ns * H / el, "unit": "request-head steps/s",
                "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": "%d calls x %d tiles of the same workload (B=%d slots, all 32 heads), %.1f s"
-                         % (calls, ns * H, ns, el)}
+               "sample": "%d calls x %d tiles of the same workload (B=%d slots, all %d heads%s), %.1f s"
+                         % (calls, ns * H, ns, H, ", whole windows" if c.window else "", el)}
 
-    traffic = measured_traffic()
+    traffic = measured_traffic(key)
     line = {
-        "metric": "request-head decode steps/s (B=512, H=32, d=128, 6-bit nominal GDN pool)",
+        "metric": spec["metric"],
         "value": T * K / (total_ms * 1e-3),
         "unit": "request-head steps/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "n_gpus": 1, "steps": K, "warmup": Wu,
         "ms_per_step": total_ms / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32 update, 4/6/8-bit + f16 state",
+        "dtype": spec["dtype"],
         "data": "synthetic (seeded; pool states drawn on the GPU with the workload recipe)",
-        "config": {"workload": "GDN serving pool B=512 H=32 d_k=d_v=128, heads {4b:9, 6b:16, 8b:6, "
-                               "fp16:1}, %d layer pools round-robin" % L,
+        "config": {"workload": spec["workload"] + ", %d layer pools round-robin" % L,
                    "global_batch": B, "heads": H, "d_k": dk, "d_v": dv, "layers": L},
         "hbm_gbs": achieved, "hbm_frac": achieved / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "traffic_gbs": None if traffic is None else traffic / (avg_ms * 1e-3) / 1e9,
-                     "kernel": "k_tile<128,128,step>", "bytes_per_launch": bytes_step,
+                     "kernel": spec["kernel"], "bytes_per_launch": bytes_step,
                      "avg_launch_ms": avg_ms, "p10_ms": float(np.percentile(per, 10)),
                      "p90_ms": float(np.percentile(per, 90))},
         "cpu_baseline": cpu,
