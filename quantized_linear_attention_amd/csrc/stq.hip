@@ -471,16 +471,28 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
 // all binary32.  FLUSH = fold the open window now (no new token).
 // ------------------------------------------------------------------------
 constexpr int WMAX = 32;
+constexpr int UQ = WMAX / 4;     // cached tokens per lane quad (quad G holds s = 4i + G)
 
-template <int DK>
+// sum over the four lanes n, n+16, n+32, n+48; every lane gets the same bits
+__device__ __forceinline__ float g4_sum(float v) {
+  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
+template <int DK, int DV>
 struct WSmem {
-  float kap[WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i), natural row order
+  // the fold's kappa table [s][row] lives in the refit partials, which are
+  // not written before the fold's last read, whenever it fits there
+  static constexpr bool IN_PART = WMAX * DK <= DK * GeoM<DK, DV>::PSTR;
+  float kap[IN_PART ? 4 : WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i)
   float cfk[WMAX];                                        // (G_t/G_s) k_s.k_t
   float cfq[WMAX];                                        // (G_t/G_s) k_s.q_t
 };
 
 template <int DK, int DV, int N, bool FLUSH>
-__device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK>& ws, uint8_t* tile,
+__device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK, DV>& ws, uint8_t* tile,
                                             uint8_t* cache, size_t x, int h) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
@@ -494,6 +506,7 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
   float* Gc = (float*)(cache + 4);
   float* Kc = (float*)(cache + 256);
   float* Uc = Kc + (size_t)W * DK;
+  float* kap = WSmem<DK, DV>::IN_PART ? sm.part : ws.kap;
   const int t = *cntp;                         // tokens already in the window
   if (FLUSH && t == 0) return;                 // nothing to fold
   const bool fold = FLUSH || (t + 1 == W);
@@ -505,6 +518,7 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
     const float a = A.a[x];
     Gt = t ? Gc[t - 1] * a : a;                // binary32 running product
   }
+  // every global read of the tile and of the lane's cached u entries first
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
@@ -512,6 +526,12 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
   float cc[G::NCC];
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) cc[c] = PIV ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
+  float uq[UQ][G::NCC];
+#pragma unroll
+  for (int i = 0; i < UQ; i++)
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+      uq[i][c] = 4 * i + Gq < t ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
   float sc = 1.f, inv = 1.f;
   if constexpr (!FLUSH) {
     float gl = 0.f;
@@ -528,32 +548,45 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
       put_afr<DK, DV, N>(sm, rho, (sg * sc) * kk, (sg * sc) * qq);
       kq = kk * qq;
       Kc[(size_t)t * DK + rho] = kk;                       // append k_t
-      if (fold) ws.kap[t * DK + rho] = kk / (Gt * sg);
     }
-    if (fold) {
-      for (int s = 0; s < t; s++) ws.kap[s * DK + rho] = Kc[(size_t)s * DK + rho] / (Gc[s] * sg);
-      sm.gg[rho] = Gt * sg;
+    if (fold) sm.gg[rho] = Gt * sg;
+  }
+  if (fold) {
+    // kappa_s,i = k_s,i / (G_s sigma_i) for every token of the fold, 4 rows per item
+    for (int j = tid; j < ns * (DK / 4); j += G::NT) {
+      const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
+      const bool cur = !FLUSH && s == t;
+      const f32x4 kv = *(const f32x4*)((cur ? A.k + x * DK : Kc + (size_t)s * DK) + r0);
+      const float gs = cur ? Gt : Gc[s];
+      f32x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; e++) o4[e] = kv[e] / (gs * (PIV ? 1.f : bf16f(scl[r0 + e])));
+      *(f32x4*)&kap[s * DK + r0] = o4;
     }
   }
   if constexpr (!FLUSH) {
     kq = wave_sum(kq);
     if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
-    // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per dot
-    for (int sd = tid / 8; sd < 2 * t; sd += G::NT / 8) {
-      const int s = sd % t;
-      const float* vec = (sd < t ? A.k : A.q) + x * DK;
-      float acc = 0.f;
+    // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per token
+    for (int s = tid / 8; s < t; s += G::NT / 8) {
+      float ak = 0.f, aq = 0.f;
 #pragma unroll
       for (int i = 4 * (tid % 8); i < DK; i += 32) {
         const f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i);
-        const f32x4 vv = *(const f32x4*)(vec + i);
-        acc = __builtin_fmaf(ks[0], vv[0], acc); acc = __builtin_fmaf(ks[1], vv[1], acc);
-        acc = __builtin_fmaf(ks[2], vv[2], acc); acc = __builtin_fmaf(ks[3], vv[3], acc);
+        const f32x4 kv = *(const f32x4*)(A.k + x * DK + i);
+        const f32x4 qv = *(const f32x4*)(A.q + x * DK + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          ak = __builtin_fmaf(ks[e], kv[e], ak);
+          aq = __builtin_fmaf(ks[e], qv[e], aq);
+        }
       }
-      acc = rb_sum<8>(acc);
+      ak = rb_sum<8>(ak);
+      aq = rb_sum<8>(aq);
       if (tid % 8 == 0) {
-        const float f = (Gt / Gc[s]) * acc;
-        if (sd < t) ws.cfk[s] = f; else ws.cfq[s] = f;
+        const float r = Gt / Gc[s];
+        ws.cfk[s] = r * ak;
+        ws.cfq[s] = r * aq;
       }
     }
   }
@@ -568,28 +601,29 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
     f32x4 D[G::NCC];
     matvec<DK, DV>(sm, P, D);
     const float bb = A.b[x];
-    float rr[G::NCC], oo[G::NCC];
+    // cache terms: quad G sums its tokens s = 4i + G, then the four quads add up
+    float pk[G::NCC], pq[G::NCC];
 #pragma unroll
-    for (int c = 0; c < G::NCC; c++) {
-      const int j = w * G::CPW + 16 * c + n16;
-      rr[c] = A.v[x * DV + j] - Gt * (cc[c] * ((D[c][0] + D[c][1]) * inv));
-      oo[c] = Gt * (cc[c] * ((D[c][2] + D[c][3]) * inv));
-    }
-    for (int s = 0; s < t; s++) {
-      const float fk = ws.cfk[s], fq = ws.cfq[s];
+    for (int c = 0; c < G::NCC; c++) pk[c] = pq[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < UQ; i++) {
+      if (4 * i >= t) break;
+      const int s = 4 * i + Gq;
+      const float fk = s < t ? ws.cfk[s] : 0.f, fq = s < t ? ws.cfq[s] : 0.f;
 #pragma unroll
       for (int c = 0; c < G::NCC; c++) {
-        const float us = Uc[(size_t)s * DV + w * G::CPW + 16 * c + n16];
-        rr[c] = __builtin_fmaf(-fk, us, rr[c]);
-        oo[c] = __builtin_fmaf(fq, us, oo[c]);
+        pk[c] = __builtin_fmaf(fk, uq[i][c], pk[c]);
+        pq[c] = __builtin_fmaf(fq, uq[i][c], pq[c]);
       }
     }
 #pragma unroll
     for (int c = 0; c < G::NCC; c++) {
       const int j = w * G::CPW + 16 * c + n16;
-      u2[c] = bb * rr[c];
+      const float rr = A.v[x * DV + j] - Gt * (cc[c] * ((D[c][0] + D[c][1]) * inv)) - g4_sum(pk[c]);
+      const float oo = Gt * (cc[c] * ((D[c][2] + D[c][3]) * inv)) + g4_sum(pq[c]);
+      u2[c] = bb * rr;
       if (Gq == 0) {
-        A.o[x * DV + j] = __builtin_fmaf(kqs, u2[c], oo[c]);
+        A.o[x * DV + j] = __builtin_fmaf(kqs, u2[c], oo);
         Uc[(size_t)t * DV + j] = u2[c];                     // append u_t
       }
     }
@@ -614,14 +648,15 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
 #pragma unroll
         for (int i = 0; i < 4; i++) C[c][i] = __builtin_fmaf(code_e<N>(P, e0 + i), cc[c], 0.0f);
       }
-      // four rank-one terms per MFMA: lane quad G carries token s0 + G
-      for (int s0 = 0; s0 < ns; s0 += 4) {
-        const int s = s0 + Gq;
-        const float kv = s < ns ? ws.kap[s * DK + r0 + n16] : 0.f;
+      // four rank-one terms per MFMA: lane quad G carries token 4i + G
+#pragma unroll
+      for (int i = 0; i < UQ; i++) {
+        if (4 * i >= ns) break;
+        const int s = 4 * i + Gq;
+        const float kv = s < ns ? kap[s * DK + r0 + n16] : 0.f;
 #pragma unroll
         for (int c = 0; c < G::NCC; c++) {
-          float uv = 0.f;
-          if (s < ns) uv = (!FLUSH && s == t) ? u2[c] : Uc[(size_t)s * DV + w * G::CPW + 16 * c + n16];
+          const float uv = (!FLUSH && s == t) ? u2[c] : uq[i][c];
           C[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, uv, C[c], 0, 0, 0);
         }
       }
@@ -633,13 +668,14 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
       }
     }
   if (tid == 0) *cntp = 0;
+  if constexpr (WSmem<DK, DV>::IN_PART) lds_barrier();     // kappa reads done before the partials
   refit_store<DK, DV, N, false>(sm, Y, tile, A.weights[(size_t)h * DK + rho]);
 }
 
 template <int DK, int DV, bool FLUSH>
-__global__ __launch_bounds__((GeoM<DK, DV>::NT)) void k_window(KArgs A) {
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_window(KArgs A) {
   __shared__ SmemM<DK, DV> sm;
-  __shared__ WSmem<DK> ws;
+  __shared__ WSmem<DK, DV> ws;
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;

@@ -200,12 +200,16 @@ def _cache_view(ref, img, slot, h):
     return cnt, G, K, U
 
 
-@pytest.mark.parametrize("W,T", [(16, 19), (4, 9)])
-def test_window_teacher_forced(torch_cuda, orc, W, T):
-    """Window mode (4-bit base frozen inside the window, fp32 cache, fold after
-    token W): the oracle steps from the GPU's bytes at every token."""
-    say("case window", W, T)
+@pytest.mark.parametrize("W,T,mix", [(16, 19, False), (4, 9, False), (8, 10, True), (32, 33, False)])
+def test_window_teacher_forced(torch_cuda, orc, W, T, mix):
+    """Window mode (base frozen inside the window, fp32 cache, fold after token
+    W): the oracle steps from the GPU's bytes at every token.  The C5 pool is
+    all 4-bit; `mix` gives it the GDN head mix (4/6/8-bit and a binary16 pivot
+    head) so that every width's window path runs; W = 32 is the largest window."""
+    say("case window", W, T, "mix" if mix else "4-bit")
     wl = Workload("C5", B=24)
+    if mix:
+        wl.bits = Workload("C2", H=wl.H).bits
     P = Pair(orc, wl, n_slots=26, window=W)
     slots = np.random.default_rng(3).permutation(26)[:24]
     P.store(slots, wl.state(slots))
