@@ -39,6 +39,7 @@ struct KArgs {
   float* o;
   const float* S_in;         // store: [n][H][d_k][d_v] (nullptr: zeros)
   float* S_out;              // fetch
+  uint32_t stage_bytes;      // per-key-row step: LDS bytes of the staged codes / row partials
 };
 
 // LDS of the per-key-row kernel
@@ -137,6 +138,22 @@ __device__ __forceinline__ float g4_max_pos(float v) {
   auto p32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   x = __builtin_elementwise_max((uint32_t)p32[0], (uint32_t)p32[1]);
   return __uint_as_float(x);
+}
+// sum over the four lanes n, n+16, n+32, n+48; every lane gets the same bits
+__device__ __forceinline__ float g4_sum(float v) {
+  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+// sum and max (non-negative floats) over the lanes l and l ^ 32, same bits in both
+__device__ __forceinline__ float pair32_sum(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float pair32_max_pos(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(__builtin_elementwise_max((uint32_t)p[0], (uint32_t)p[1]));
 }
 // power of two sc that puts m into [2^14, 2^15) (clamped to normal range),
 // and 1/sc: keeps the matvec operand inside binary16's range
@@ -473,13 +490,6 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
 constexpr int WMAX = 32;
 constexpr int UQ = WMAX / 4;     // cached tokens per lane quad (quad G holds s = 4i + G)
 
-// sum over the four lanes n, n+16, n+32, n+48; every lane gets the same bits
-__device__ __forceinline__ float g4_sum(float v) {
-  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
-  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
-}
 
 template <int DK, int DV>
 struct WSmem {
@@ -1048,6 +1058,387 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_rows(KArgs A) {
 }
 
 // ------------------------------------------------------------------------
+// Per-key-row widths: the decode step.  The record rows of a tile are split
+// over the waves in runs of RPW; in step r a wave covers RPI consecutive
+// record rows with CGN lanes per row, one 4-code group (4 adjacent columns)
+// per lane.  Records are sorted by width, so the rows of a step share one
+// width except where a run of one width ends: every step's width and record
+// offset are computed in scalar registers from the head's four counts, and
+// a step whose rows differ in width is run once per row of the step under a
+// lane mask.  The tile's codes travel between HBM and LDS as whole 16-byte
+// chunks; lanes read their groups from LDS (a row's lanes read consecutive
+// bytes) and write the new groups back there before the tile is stored.
+// ------------------------------------------------------------------------
+template <int DK, int DV>
+struct GeoR {
+  static constexpr int NW = DK * DV / 4096;     // 16 rows x 4 codes per lane
+  static constexpr int NT = 64 * NW;
+  static constexpr int CGN = DV / 4;            // lanes (column groups) per row
+  static constexpr int RPI = 64 / CGN;          // record rows per wave and step
+  static constexpr int RPW = DK / NW;           // record rows per wave
+  static constexpr int NR = RPW / RPI;          // rows per lane
+  static constexpr int TPR = NT / DK;           // threads per row in the row stage
+  static constexpr int PSTR = CGN + 4;          // LDS stride of the row partials
+  static constexpr int NCH = DK * DV * 2 / (16 * NT);   // 16-byte chunks per thread, binary16 bound
+  static_assert(NR == 16 && (TPR == 1 || TPR == 2) && CGN * RPI == 64, "row geometry");
+};
+
+template <int DK, int DV>
+struct RSmemS {
+  float red[GeoR<DK, DV>::NW][2][DV] __attribute__((aligned(16)));   // per wave: column partials
+  uint32_t sink[GeoR<DK, DV>::NT] __attribute__((aligned(16)));      // stores of lanes with no group
+  float alpha[DK] __attribute__((aligned(16)));   // by lane slot: g k
+  float beta[DK] __attribute__((aligned(16)));    // g q
+  float kappa[DK] __attribute__((aligned(16)));   // k / g
+  float gg[DK] __attribute__((aligned(16)));      // g = gate * row scale
+  float rowh[DK] __attribute__((aligned(16)));    // new X factor (1 on pivot rows)
+  float rq[DK] __attribute__((aligned(16)));      // 1 / QMAX of the row's width (0 on pivot rows)
+  float kqp[GeoR<DK, DV>::NW];
+  int notone[GeoR<DK, DV>::NW];
+  int esum[GeoR<DK, DV>::NW];
+  int ecnt[GeoR<DK, DV>::NW];
+};
+
+// LDS slot of record row p: the NR rows that one lane visits are contiguous
+template <int DK, int DV>
+__device__ __forceinline__ int rslot(int p) {
+  using G = GeoR<DK, DV>;
+  const int w = p / G::RPW, q = p - w * G::RPW;
+  return w * G::RPW + (q % G::RPI) * G::NR + q / G::RPI;
+}
+
+// width and byte offset of record row p (c4, c6, c8: rows below width 6, 8, 16)
+template <int DV>
+__device__ __forceinline__ void rec_at(int p, int c4, int c6, int c8, int& n, int& off) {
+  if (p < c4) {
+    n = 4; off = p * (DV / 2);
+  } else if (p < c6) {
+    n = 6; off = c4 * (DV / 2) + (p - c4) * (3 * DV / 4);
+  } else if (p < c8) {
+    n = 8; off = c4 * (DV / 2) + (c6 - c4) * (3 * DV / 4) + (p - c6) * DV;
+  } else {
+    n = 16; off = c4 * (DV / 2) + (c6 - c4) * (3 * DV / 4) + (c8 - c6) * DV + (p - c8) * 2 * DV;
+  }
+}
+
+// Per-step table of a wave, one word per step: record offset of the step's
+// first row | width << 16 | bit 31 when the rows of the step differ in width.
+template <int DK, int DV>
+__device__ __forceinline__ void step_table(int ws0, int c4, int c6, int c8, uint32_t* tab) {
+  using G = GeoR<DK, DV>;
+#pragma unroll
+  for (int r = 0; r < G::NR; r++) {
+    const int p0 = ws0 + G::RPI * r;
+    int n0, o0, n1, o1;
+    rec_at<DV>(p0, c4, c6, c8, n0, o0);
+    rec_at<DV>(p0 + G::RPI - 1, c4, c6, c8, n1, o1);
+    tab[r] = (uint32_t)o0 | ((uint32_t)n0 << 16) | (n0 != n1 ? 0x80000000u : 0u);
+  }
+}
+
+// Run body(r, n, offU) for the lane's 16 steps: n is the width of the lane's
+// row in step r and offU + rsl * (record bytes) its record offset; n and
+// offU are wave-uniform.
+template <int DK, int DV, typename F>
+__device__ __forceinline__ void row_steps(const uint32_t* tab, int ws0, int rsl, int c4, int c6, int c8, F&& body) {
+  using G = GeoR<DK, DV>;
+#pragma unroll
+  for (int r = 0; r < G::NR; r++) {
+    const uint32_t t = tab[r];
+    if (!(t & 0x80000000u)) {
+      body(r, (int)((t >> 16) & 31u), (int)(t & 0xFFFFu));
+    } else {
+#pragma unroll 1
+      for (int s = 0; s < G::RPI; s++) {
+        int ns, os;
+        rec_at<DV>(ws0 + G::RPI * r + s, c4, c6, c8, ns, os);
+        if (rsl == s) body(r, ns, os - s * (DV * ns / 8));
+      }
+    }
+  }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_step(KArgs A) {
+  using G = GeoR<DK, DV>;
+  __shared__ RSmemS<DK, DV> rs;
+  extern __shared__ u32x4 stage_[];               // the tile's codes, later the row partials
+  uint8_t* stage = (uint8_t*)stage_;
+  float* part = (float*)stage_;
+  const int T = A.n * A.H;
+  const int tau = tile_of_block(T);
+  if (tau >= T) return;
+  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int slot = A.slots ? A.slots[ci] : ci;
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+  const size_t x = (size_t)ci * A.H + h;
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = l % G::CGN, rsl = l / G::CGN;    // column group; row of the step
+  const int j0 = 4 * cg;
+  const int vb = w * G::RPW + rsl * G::NR;        // LDS slot of the lane's first row
+  const int ws0 = w * G::RPW;                     // first record row of the wave
+  const int* cntp = A.row_cnt + 4 * h;
+  const int c4 = cntp[0], c6 = c4 + cntp[1], c8 = c6 + cntp[2];
+  const int CB = c4 * (DV / 2) + cntp[1] * (3 * DV / 4) + cntp[2] * DV + cntp[3] * 2 * DV;
+  uint16_t* scl = (uint16_t*)(tile + CB);
+
+  // ---- every global read first ----
+  u32x4 chunk[G::NCH];
+#pragma unroll
+  for (int i = 0; i < G::NCH; i++) {
+    const int off = 16 * (tid + i * G::NT);
+    if (off < CB) chunk[i] = *(const u32x4*)(tile + off);
+  }
+  const int rho = tid / G::TPR, rsub = tid % G::TPR;     // row stage: record row rho
+  const int irow = A.row_perm[(size_t)h * DK + rho];
+  int pn, poff;
+  rec_at<DV>(rho, c4, c6, c8, pn, poff);
+  float kk = 0.f, qq = 0.f, ai = 1.f, sgr = 1.f;
+  if (rsub == 0) {
+    kk = A.k[x * DK + irow];
+    qq = A.q[x * DK + irow];
+    ai = A.gate ? A.a[x * DK + irow] : A.a[x];
+    sgr = pn == 16 ? 1.f : bf16f(scl[irow]);
+  }
+  const u32x2 cw = *(const u32x2*)(scl + DK + j0);
+  const f32x4 vv = *(const f32x4*)(A.v + x * DV + j0);
+  const float bb = A.b[x];
+#pragma unroll
+  for (int i = 0; i < G::NCH; i++) {
+    const int off = 16 * (tid + i * G::NT);
+    if (off < CB) *(u32x4*)(stage + off) = chunk[i];
+  }
+  float kq = 0.f;
+  if (rsub == 0) {
+    const float g = ai * sgr;
+    const int sl = rslot<DK, DV>(rho);
+    rs.alpha[sl] = g * kk;
+    rs.beta[sl] = g * qq;
+    rs.kappa[sl] = kk * __builtin_amdgcn_rcpf(g);
+    rs.gg[sl] = g;
+    kq = kk * qq;
+  }
+  kq = wave_sum(kq);
+  const bool ne1 = __ballot(ai != 1.f) != 0;
+  if (l == 0) { rs.kqp[w] = kq; rs.notone[w] = ne1; }
+  float cc[4] = {bf16f(cw[0] & 0xFFFFu), bf16f(cw[0] >> 16), bf16f(cw[1] & 0xFFFFu), bf16f(cw[1] >> 16)};
+  lds_barrier();
+
+  // ---- unpack and the two reductions over the rows: (a S)^T k, (a S)^T q ----
+  uint32_t tab[G::NR];
+  step_table<DK, DV>(ws0, c4, c6, c8, tab);
+  f16x2 P[32];
+  float U[4] = {0.f, 0.f, 0.f, 0.f}, Wr[4] = {0.f, 0.f, 0.f, 0.f};
+  float Up[4] = {0.f, 0.f, 0.f, 0.f}, Wp[4] = {0.f, 0.f, 0.f, 0.f};
+  row_steps<DK, DV>(tab, ws0, rsl, c4, c6, c8, [&](int r, int n, int offU) __attribute__((always_inline)) {
+    const int a = offU + rsl * (DV * n / 8) + cg * (n / 2);
+    if (n == 16) {
+      const u32x2 d = *(const u32x2*)(stage + a);
+      P[2 * r] = as_h2(d[0]);
+      P[2 * r + 1] = as_h2(d[1]);
+    } else {
+      const uint32_t* sw = (const uint32_t*)(stage + (a & ~3));
+      const uint32_t g = __builtin_amdgcn_alignbyte(sw[1], sw[0], (uint32_t)a);
+      const uint32_t f0 = __builtin_amdgcn_ubfe(g, 0, n), f1 = __builtin_amdgcn_ubfe(g, n, n);
+      const uint32_t f2 = __builtin_amdgcn_ubfe(g, 2 * n, n), f3 = __builtin_amdgcn_ubfe(g, 3 * n, n);
+      const uint32_t kb = (0xE400u + (1u << (n - 1))) * 0x10001u;   // -(1024 + 2^(n-1)), both halves
+      P[2 * r] = as_h2(f0 | (f1 << 16) | 0x64006400u) + as_h2(kb);
+      P[2 * r + 1] = as_h2(f2 | (f3 << 16) | 0x64006400u) + as_h2(kb);
+      const float alr = rs.alpha[vb + r], ber = rs.beta[vb + r];
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const float qv = (float)P[2 * r + (c >> 1)][c & 1];
+        U[c] = __builtin_fmaf(qv, alr, U[c]);
+        Wr[c] = __builtin_fmaf(qv, ber, Wr[c]);
+      }
+    }
+  });
+  // binary16 pivot rows (the last records): only the steps that reach them
+#pragma unroll
+  for (int r = 0; r < G::NR; r++) {
+    if (ws0 + G::RPI * r + G::RPI - 1 < c8) continue;
+    const bool piv = ws0 + G::RPI * r + rsl >= c8;
+    const float alr = piv ? rs.alpha[vb + r] : 0.f, ber = piv ? rs.beta[vb + r] : 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const float qv = piv ? (float)P[2 * r + (c >> 1)][c & 1] : 0.f;
+      Up[c] = __builtin_fmaf(qv, alr, Up[c]);
+      Wp[c] = __builtin_fmaf(qv, ber, Wp[c]);
+    }
+  }
+  // partial column sums of the lane's rows, then over the rows of a step, then over waves
+  float us[4], wsum[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    us[c] = __builtin_fmaf(cc[c], U[c], Up[c]);
+    wsum[c] = __builtin_fmaf(cc[c], Wr[c], Wp[c]);
+    if (G::RPI == 2) {
+      us[c] = pair32_sum(us[c]);
+      wsum[c] = pair32_sum(wsum[c]);
+    } else {
+      us[c] = g4_sum(us[c]);
+      wsum[c] = g4_sum(wsum[c]);
+    }
+  }
+  if (rsl == 0) {
+    *(f32x4*)&rs.red[w][0][j0] = f32x4{us[0], us[1], us[2], us[3]};
+    *(f32x4*)&rs.red[w][1][j0] = f32x4{wsum[0], wsum[1], wsum[2], wsum[3]};
+  }
+  lds_barrier();
+  int allone = 1;
+  float kqs = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < G::NW; ww++) { allone &= !rs.notone[ww]; kqs += rs.kqp[ww]; }
+  f32x4 u4 = *(const f32x4*)&rs.red[0][0][j0], w4 = *(const f32x4*)&rs.red[0][1][j0];
+#pragma unroll
+  for (int ww = 1; ww < G::NW; ww++) {
+    u4 += *(const f32x4*)&rs.red[ww][0][j0];
+    w4 += *(const f32x4*)&rs.red[ww][1][j0];
+  }
+  float delta[4];
+  f32x4 ov;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    delta[c] = bb * (vv[c] - u4[c]);
+    ov[c] = __builtin_fmaf(delta[c], kqs, w4[c]);
+  }
+  if (w == 0 && rsl == 0) *(f32x4*)(A.o + x * DV + j0) = ov;
+  if (bb == 0.f && allone) return;      // identity update: keep the encoding
+
+  // ---- rank-one update, Y = S' / g; row partial maxima of the non-pivot rows ----
+  float Y[64];
+  opaque(P);
+  row_steps<DK, DV>(tab, ws0, rsl, c4, c6, c8, [&](int r, int n, int offU) __attribute__((always_inline)) {
+    (void)offU;
+    const float kar = rs.kappa[vb + r];
+    float m = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const float qv = (float)P[2 * r + (c >> 1)][c & 1];
+      Y[4 * r + c] = __builtin_fmaf(qv, n == 16 ? 1.f : cc[c], kar * delta[c]);
+      m = __builtin_fmaxf(m, __builtin_fabsf(Y[4 * r + c]));
+    }
+    part[(ws0 + G::RPI * r + rsl) * G::PSTR + cg] = n == 16 ? 0.f : m;
+  });
+  lds_barrier();
+
+  // ---- row refit (one thread pair per record row) ----
+  {
+    uint32_t mxb = 0u;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; k4++) {
+      const u32x4 m4 = *(const u32x4*)&part[rho * G::PSTR + rsub * 16 + 4 * k4];
+      mxb = __builtin_elementwise_max(mxb, __builtin_elementwise_max(__builtin_elementwise_max(m4[0], m4[1]),
+                                                                     __builtin_elementwise_max(m4[2], m4[3])));
+    }
+    if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
+    const int sl = rslot<DK, DV>(rho);
+    const float g = ai * sgr;
+    const float pw = (g * __uint_as_float(mxb)) * A.weights[(size_t)h * DK + irow];
+    uint32_t s = 0x3F80u;
+    int epk = 0;
+    if (pn != 16 && pw > 0.f) {
+      s = bf16_rne(__builtin_amdgcn_sqrtf(pw));
+      epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
+    }
+    if (rsub != 0) epk = 0;
+    if (rsub == 0) {
+      rs.rowh[sl] = pn == 16 ? 1.f : g * rcp_bf16(bf16f(s));
+      rs.rq[sl] = pn == 4 ? 1.0f / 7.0f : pn == 6 ? 1.0f / 31.0f : pn == 8 ? 1.0f / 127.0f : 0.f;
+    }
+    epk = wave_sum_i(epk);
+    if (l == 0) { rs.esum[w] = epk >> 8; rs.ecnt[w] = epk & 0xFF; }
+    lds_barrier();
+    int es = 0, ec = 0;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) { es += rs.esum[ww]; ec += rs.ecnt[ww]; }
+    const int E = ec ? mean_exp(es, ec) : 0;
+    if (rsub == 0) scl[irow] = (uint16_t)bf16_adj(s, -E);
+
+    // ---- column refit ----
+    float hr[16], rqv[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      *(f32x4*)&hr[4 * r4] = *(const f32x4*)&rs.rowh[vb + 4 * r4];
+      *(f32x4*)&rqv[4 * r4] = *(const f32x4*)&rs.rq[vb + 4 * r4];
+    }
+    float cm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        Y[4 * r + c] = Y[4 * r + c] * hr[r];
+        cm[c] = __builtin_fmaxf(cm[c], __builtin_fabsf(Y[4 * r + c]) * rqv[r]);
+      }
+#pragma unroll
+    for (int c = 0; c < 4; c++) cm[c] = G::RPI == 2 ? pair32_max_pos(cm[c]) : g4_max_pos(cm[c]);
+    if (rsl == 0) *(f32x4*)&rs.red[w][0][j0] = f32x4{cm[0], cm[1], cm[2], cm[3]};
+    lds_barrier();
+    f32x4 M4 = *(const f32x4*)&rs.red[0][0][j0];
+#pragma unroll
+    for (int ww = 1; ww < G::NW; ww++) {
+      const f32x4 o4 = *(const f32x4*)&rs.red[ww][0][j0];
+#pragma unroll
+      for (int c = 0; c < 4; c++) M4[c] = __builtin_fmaxf(M4[c], o4[c]);
+    }
+    float rc[4];
+    uint32_t cb[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      uint32_t t = 0x3F80u;
+      if (c8 > 0 && M4[c] > 0.f) {
+        t = bf16_ru_pos(M4[c]);
+        if (t < 0x0080u) t = 0x0080u;
+      }
+      rc[c] = rcp_bf16(bf16f(t));
+      cb[c] = bf16_adj(t, E);
+    }
+    if (w == 0 && rsl == 0) *(u32x2*)(scl + DK + j0) = u32x2{cb[0] | (cb[1] << 16), cb[2] | (cb[3] << 16)};
+
+    // ---- requantize into the staged records ----
+    const int q4 = cg & 3;
+    const int a6 = 12 * (cg >> 2) + 4 * q4;          // 6-bit: dword q4 of the quad's 12 bytes
+    uint8_t* sink = (uint8_t*)&rs.sink[tid];
+    row_steps<DK, DV>(tab, ws0, rsl, c4, c6, c8, [&](int r, int n, int offU) __attribute__((always_inline)) {
+      uint8_t* rec = stage + offU + rsl * (DV * n / 8);
+      if (n == 16) {
+        const float grr = rs.gg[vb + r];
+        float sv[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) sv[c] = __builtin_fminf(__builtin_fmaxf(grr * Y[4 * r + c], -65504.f), 65504.f);
+        *(u32x2*)(rec + 8 * cg) = u32x2{h2_bits(f16x2{(f16)sv[0], (f16)sv[1]}), h2_bits(f16x2{(f16)sv[2], (f16)sv[3]})};
+        return;
+      }
+      const float mg = __uint_as_float(0x4B000000u + (1u << (n - 1)));   // 2^23 + 2^(n-1)
+      uint32_t y[4];
+#pragma unroll
+      for (int c = 0; c < 4; c++) y[c] = __float_as_uint(__builtin_fmaf(Y[4 * r + c], rc[c], mg));
+      if (n == 4) {
+        const uint32_t g = y[0] | (y[1] << 4) | (y[2] << 8) | (y[3] << 12);
+        *(uint16_t*)(rec + 2 * cg) = (uint16_t)g;
+      } else if (n == 8) {
+        *(uint32_t*)(rec + 4 * cg) = (y[0] & 0xFFu) | (y[1] << 8) | (y[2] << 16) | (y[3] << 24);
+      } else {
+        // 6-bit: the quad's four 3-byte groups form 3 dwords; lane q4 < 3 writes dword q4
+        const uint32_t g = y[0] | (y[1] << 6) | (y[2] << 12) | (y[3] << 18);
+        const uint32_t gn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g, 0xF9, 0xF, 0xF, false);   // lane q4 + 1
+        const uint32_t d = __builtin_amdgcn_alignbyte(gn, g << 8, (uint32_t)(q4 + 1));
+        *(uint32_t*)(q4 == 3 ? sink : rec + a6) = d;
+      }
+    });
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < G::NCH; i++) {
+    const int off = 16 * (tid + i * G::NT);
+    if (off < CB) *(u32x4*)(tile + off) = *(const u32x4*)(stage + off);
+  }
+}
+
+// ------------------------------------------------------------------------
 // Fetch (D) and fixed-scale requantization of per-head tiles.
 // ------------------------------------------------------------------------
 template <int DK, int DV, int N, bool REQ>
@@ -1121,6 +1512,7 @@ struct stq_pool {
   std::vector<int32_t> bits;            // [H] or [H][d_k]
   std::vector<uint32_t> head_off;
   uint64_t hdr, woff, roff, slot_bytes, slots_off, cache_off, cache_stride, total;
+  uint32_t rows_stage;                  // per-key-row units: LDS bytes the step kernel stages
   uint8_t* dev;
   std::vector<uint8_t> header;  // host staging copy of the header
 };
@@ -1158,18 +1550,23 @@ void layout(const stq_pool_desc* d, stq_pool* p) {
   const bool rows = p->unit == STQ_UNIT_ROW;
   p->bits.assign(d->unit_bits, d->unit_bits + (rows ? d->n_heads * d->d_k : d->n_heads));
   p->head_off.resize(d->n_heads);
-  uint64_t s = 0;
+  uint64_t s = 0, cbmax = 0;
   for (int h = 0; h < d->n_heads; h++) {
     p->head_off[h] = (uint32_t)s;
     if (rows) {
-      uint64_t b = 2ull * (p->dk + p->dv);
-      for (int i = 0; i < p->dk; i++) b += (uint64_t)p->dv * p->bits[(size_t)h * p->dk + i] / 8;
-      s += ru256(b);
+      uint64_t cb = 0;
+      for (int i = 0; i < p->dk; i++) cb += (uint64_t)p->dv * p->bits[(size_t)h * p->dk + i] / 8;
+      cbmax = cb > cbmax ? cb : cbmax;
+      s += ru256(cb + 2ull * (p->dk + p->dv));
     } else {
       s += tile_stride(p->bits[h], p->dk, p->dv);
     }
   }
   p->slot_bytes = s;
+  // staged codes plus the word the last group's decode reads past them, or the
+  // row partials [d_k][d_v/4 + 4] floats, whichever is larger
+  const uint64_t partb = 4ull * p->dk * (p->dv / 4 + 4);
+  p->rows_stage = (uint32_t)(((cbmax + 16 > partb ? cbmax + 16 : partb) + 15) / 16 * 16);
   p->woff = ru256(64 + 8ull * p->H);
   p->roff = ru256(p->woff + 4ull * p->H * p->dk);
   p->hdr = rows ? ru256(p->roff + 2ull * p->H * p->dk + 16ull * p->H) : p->roff;
@@ -1195,6 +1592,7 @@ KArgs base_args(const stq_pool* p, const int32_t* slots, int n) {
   A.weights = (const float*)(p->dev + p->woff);
   A.row_perm = p->dev + p->roff + (size_t)p->H * p->dk;
   A.row_cnt = (const int32_t*)(p->dev + p->roff + 2ull * p->H * p->dk);
+  A.stage_bytes = p->rows_stage;
   return A;
 }
 
@@ -1237,6 +1635,14 @@ struct LWindow {
   struct T {
     static void go(const KArgs& A, unsigned g, hipStream_t st) {
       hipLaunchKernelGGL((k_window<DK, DV, FLUSH>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    }
+  };
+};
+struct LRowStep {
+  template <int DK, int DV>
+  struct T {
+    static void go(const KArgs& A, unsigned g, hipStream_t st) {
+      hipLaunchKernelGGL((k_rows_step<DK, DV>), dim3(g), dim3(GeoR<DK, DV>::NT), A.stage_bytes, st, A);
     }
   };
 };
@@ -1381,7 +1787,7 @@ stq_status stq_decode_step(stq_pool* p, const int32_t* slots, int32_t n, const f
   KArgs A = base_args(p, slots, n);
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
   if (p->W > 0) return dispatch<LWindow<false>::T>(p, A, st);
-  if (p->unit == STQ_UNIT_ROW) return dispatch<LRows<RMODE_STEP>::T>(p, A, st);
+  if (p->unit == STQ_UNIT_ROW) return dispatch<LRowStep::T>(p, A, st);
   return dispatch<LTile<MODE_STEP>::T>(p, A, st);
 }
 

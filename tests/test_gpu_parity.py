@@ -169,6 +169,59 @@ def test_other_tile_shapes(torch_cuda, orc, dk, dv):
     assert readout_ok(o, o_ref) <= 1.0
 
 
+def _row_width_patterns(dk, rng):
+    """Per-head key-row widths (original row order) that reach every path of the
+    per-key-row step: one width only, binary16 pivots only, runs of a width that
+    end inside a step of the kernel, a lone quantized row among pivots, a mix in
+    the C4 proportions and a uniform random mix."""
+    from workloads import quotas
+    pats = [np.full(dk, 4), np.full(dk, 6), np.full(dk, 8), np.full(dk, 16),
+            np.repeat([4, 6, 8, 16], [3, 5, dk - 9, 1]),
+            np.repeat([4, 6, 8, 16], quotas([0.30, 0.50, 0.19, 0.01], dk)),
+            np.repeat([8, 16], [1, dk - 1]),
+            rng.choice([4, 6, 8, 16], dk)]
+    return np.stack([rng.permutation(p) for p in pats]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_rows_step_shapes(torch_cuda, orc, dk, dv):
+    """Per-key-row widths with the per-channel gate at every tile shape: two
+    teacher-forced steps (the oracle steps from the GPU's bytes each time)."""
+    from types import SimpleNamespace
+    say("case rows step", dk, dv)
+    rng = np.random.default_rng(100 + dk + dv)
+    H, B = 8, 6
+    cfg = SimpleNamespace(gate=1, unit=1, window=0)
+    wl = SimpleNamespace(B=B, H=H, dk=dk, dv=dv, cfg=cfg, bits=_row_width_patterns(dk, rng),
+                         row_weight=np.clip(np.exp(rng.normal(0, 1.15, (H, dk))), 0.1, 10).astype(np.float32))
+    P = Pair(orc, wl, n_slots=B + 2)
+    slots = rng.permutation(B + 2)[:B]
+    prof = np.exp(rng.normal(0, 1.5, (1, H, dk, 1))) * np.exp(rng.normal(0, 1.5, (1, H, 1, dv)))
+    P.store(slots, (0.1 * rng.standard_normal((B, H, dk, dv)) * prof).astype(np.float32))
+    f = lambda x: x.astype(np.float32)
+    worst = dict(mism=0, codes=0, maxd=0, scale_mism=0, scales=0, piv_bad=0, piv=0, piv_mism=0, o=0.0)
+    for t in range(2):
+        img = P.image()
+        ref = orc.OraclePool(B + 2, H, dk, dv, wl.bits.reshape(-1), wl.row_weight, 1, 1, 0, image=img)
+        q = rng.standard_normal((B, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k = rng.standard_normal((B, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((B, H, dv))
+        a = 2.0 ** (-1.0 / (10.0 ** rng.uniform(0, 4, (B, H, dk))))
+        b = rng.uniform(0.05, 0.95, (B, H))
+        o = P.gpu_step(slots, f(q), f(k), f(v), f(a), f(b))
+        o_ref = ref.step(slots, f(q), f(k), f(v), f(a), f(b))
+        r = compare_codes(orc, ref, P.image(), ref.img, slots)
+        for key in ("mism", "codes", "scale_mism", "scales", "piv_bad", "piv", "piv_mism"):
+            worst[key] += r[key]
+        worst["maxd"] = max(worst["maxd"], r["maxd"])
+        worst["o"] = max(worst["o"], readout_ok(o, o_ref))
+    say("  rows %dx%d: code mismatch %d of %d (max |dQ| %d), scale mismatch %d of %d, pivot mismatch %d of %d, "
+        "readout %.3f" % (dk, dv, worst["mism"], worst["codes"], worst["maxd"], worst["scale_mism"],
+                          worst["scales"], worst["piv_mism"], worst["piv"], worst["o"]))
+    _assert_codes(worst)
+    assert worst["o"] <= 1.0
+
+
 def test_empty_and_out_of_range(torch_cuda, orc):
     say("case edges")
     torch = torch_cuda
