@@ -42,17 +42,12 @@ struct KArgs {
   uint32_t stage_bytes;      // per-key-row step: LDS bytes of the staged codes / row partials
 };
 
-// LDS of the per-key-row kernel
+// LDS of the per-key-row ingest / decode / fixed-scale kernel
 template <int DK, int DV>
 struct Smem {
-  float alpha[DK] __attribute__((aligned(16)));   // [rb][r]: g k
-  float beta[DK] __attribute__((aligned(16)));    // g q
-  float kappa[DK] __attribute__((aligned(16)));   // k / g
-  float gg[DK] __attribute__((aligned(16)));      // g = gate * old row scale
+  float gg[DK] __attribute__((aligned(16)));      // g (1 on ingest)
   float rowh[DK] __attribute__((aligned(16)));    // new X factor per row
   float part[Geo<DK, DV>::NP * DK] __attribute__((aligned(16)));
-  float kqp[Geo<DK, DV>::NW];
-  int notone[Geo<DK, DV>::NW];     // per wave: some gate of the tile differs from 1
   int esum[Geo<DK, DV>::NW];
   int ecnt[Geo<DK, DV>::NW];
 };
@@ -708,10 +703,11 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
 // records (d_v codes at the row's width, 4-code groups), sorted by width,
 // then sigma[d_k] (original row order) and c[d_v].  The code region is
 // staged through LDS with 16-byte accesses, so every lane can read its rows'
-// groups whatever the width mix; lanes keep the 16 x 4 ownership of the
-// per-head kernel, over the records' (physical) row order.
+// groups whatever the width mix; lanes own 16 record rows x 4 columns.  This
+// kernel ingests (R of a given tile), decodes (D) and requantizes at fixed
+// scales; the decode step has its own kernel, k_rows_step, below.
 // ------------------------------------------------------------------------
-enum { RMODE_STEP = 0, RMODE_STORE = 1, RMODE_FETCH = 2, RMODE_REQUANT = 3 };
+enum { RMODE_STORE = 1, RMODE_FETCH = 2, RMODE_REQUANT = 3 };
 
 template <int DK, int DV>
 struct RSmem {
@@ -806,26 +802,6 @@ __device__ __forceinline__ void rows_body(const KArgs& A, Smem<DK, DV>& sm, RSme
   float cc[4] = {1.f, 1.f, 1.f, 1.f};
   uint32_t ri[16];
   f16x2 P[32];
-  float ka[16];
-  bool vecs_ready = false;
-  if (MODE == RMODE_STEP) {
-    float ai = 1.f, kq = 0.f;
-    if (rsub == 0) {
-      const float kk = A.k[x * DK + irow], qq = A.q[x * DK + irow];
-      ai = A.gate ? A.a[x * DK + irow] : A.a[x];
-      const float sg = pn == 16 ? 1.f : bf16f(scl[irow]);
-      const float g = ai * sg;
-      sm.alpha[rho] = g * kk;
-      sm.beta[rho] = g * qq;
-      sm.kappa[rho] = kk * __builtin_amdgcn_rcpf(g);
-      sm.gg[rho] = g;
-      kq = kk * qq;
-    }
-    kq = wave_sum(kq);
-    const bool ne1 = __ballot(ai != 1.f) != 0;
-    if (l == 0) { sm.kqp[w] = kq; sm.notone[w] = ne1; }
-    vecs_ready = true;
-  }
   __syncthreads();
 #pragma unroll
   for (int r4 = 0; r4 < 4; r4++) *(u32x4*)&ri[4 * r4] = *(const u32x4*)&rs.rinfo[rb * 16 + 4 * r4];
@@ -835,11 +811,9 @@ __device__ __forceinline__ void rows_body(const KArgs& A, Smem<DK, DV>& sm, RSme
       const int n = ri[r] & 0xFF, off = ri[r] >> 8;
       group_load(lds + off + (j0 / 4) * (n / 2), n, P[2 * r], P[2 * r + 1]);
     }
-    if (MODE != RMODE_STEP || true) {
-      u32x2 cw = *(const u32x2*)(scl + DK + j0);
-      cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
-      cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
-    }
+    u32x2 cw = *(const u32x2*)(scl + DK + j0);
+    cc[0] = bf16f(cw[0] & 0xFFFFu); cc[1] = bf16f(cw[0] >> 16);
+    cc[2] = bf16f(cw[1] & 0xFFFFu); cc[3] = bf16f(cw[1] >> 16);
   }
   if (MODE == RMODE_FETCH || MODE == RMODE_REQUANT) {
     // D: fl(fl(sigma c) Q), pivot rows binary16 -> binary32
@@ -880,60 +854,7 @@ __device__ __forceinline__ void rows_body(const KArgs& A, Smem<DK, DV>& sm, RSme
     }
     return;
   }
-  if (MODE == RMODE_STEP) {
-    int allone = 1;
-#pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) allone &= !sm.notone[ww];
-    float al[16], be[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) {
-      *(f32x4*)&al[4 * r4] = *(const f32x4*)&sm.alpha[rb * 16 + 4 * r4];
-      *(f32x4*)&be[4 * r4] = *(const f32x4*)&sm.beta[rb * 16 + 4 * r4];
-    }
-    float U[4] = {0.f, 0.f, 0.f, 0.f}, Wr[4] = {0.f, 0.f, 0.f, 0.f};
-    float Up[4] = {0.f, 0.f, 0.f, 0.f}, Wp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const bool piv = (ri[r] & 0xFF) == 16;
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const float qv = (float)P[2 * r + (c >> 1)][c & 1];
-        if (piv) {
-          Up[c] = __builtin_fmaf(qv, al[r], Up[c]);
-          Wp[c] = __builtin_fmaf(qv, be[r], Wp[c]);
-        } else {
-          U[c] = __builtin_fmaf(qv, al[r], U[c]);
-          Wr[c] = __builtin_fmaf(qv, be[r], Wr[c]);
-        }
-      }
-    }
-    float kqs = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqp[ww];
-    const float bb = A.b[x];
-    const f32x4 vv = *(const f32x4*)(A.v + x * DV + j0);
-    float delta[4];
-    f32x4 ov;
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const float u = __builtin_fmaf(cc[c], rb_sum<G::RB>(U[c]), rb_sum<G::RB>(Up[c]));
-      const float wq = __builtin_fmaf(cc[c], rb_sum<G::RB>(Wr[c]), rb_sum<G::RB>(Wp[c]));
-      delta[c] = bb * (vv[c] - u);
-      ov[c] = __builtin_fmaf(delta[c], kqs, wq);
-    }
-    if (rb == 0) *(f32x4*)(A.o + x * DV + j0) = ov;
-    if (bb == 0.f && allone) return;      // identity update: keep the encoding
-#pragma unroll
-    for (int r4 = 0; r4 < 4; r4++) *(f32x4*)&ka[4 * r4] = *(const f32x4*)&sm.kappa[rb * 16 + 4 * r4];
-    opaque(P);
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const bool piv = (ri[r] & 0xFF) == 16;
-#pragma unroll
-      for (int c = 0; c < 4; c++)
-        Y[4 * r + c] = __builtin_fmaf((float)P[2 * r + (c >> 1)][c & 1], piv ? 1.f : cc[c], ka[r] * delta[c]);
-    }
-  } else {
+  {
     // store: Y = the given fp32 tile (original row order), g = 1
     const float* S = A.S_in ? A.S_in + x * DK * DV : nullptr;
 #pragma unroll
@@ -950,7 +871,6 @@ __device__ __forceinline__ void rows_body(const KArgs& A, Smem<DK, DV>& sm, RSme
       for (int off = TB + 16 * tid; off < TS; off += 16 * G::NT) *(u32x4*)(tile + off) = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  (void)vecs_ready;
   // ---- refit: pivot rows outside the row and column fits ----
   float gr[16];
 #pragma unroll
@@ -977,7 +897,7 @@ __device__ __forceinline__ void rows_body(const KArgs& A, Smem<DK, DV>& sm, RSme
   uint32_t s = 0x3F80u;
   int epk = 0;
   if (pn != 16 && pw > 0.f) {
-    s = bf16_rne(MODE == RMODE_STORE ? __builtin_sqrtf(pw) : __builtin_amdgcn_sqrtf(pw));
+    s = bf16_rne(__builtin_sqrtf(pw));
     epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
   }
   if (rsub != 0) epk = 0;
