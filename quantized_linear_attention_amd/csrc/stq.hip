@@ -1359,6 +1359,291 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
 }
 
 // ------------------------------------------------------------------------
+// Per-key-row widths with d_v = 128: the 64 lanes of a wave span one record
+// row (columns 2l, 2l+1), so each step of the loops below is one row whose
+// width and record offset are wave-uniform values.  A wave owns 32
+// consecutive record rows.  The binary16 pivot rows, the last records,
+// leave the unrolled loops: their readout terms and their update run row by
+// row at the end of the first and the last phase.
+// ------------------------------------------------------------------------
+template <int DK>
+struct GeoW {
+  static constexpr int DV = 128;
+  static constexpr int NW = DK / 32;        // waves, 32 record rows each
+  static constexpr int NT = 64 * NW;
+  static constexpr int NR = 32;             // steps (rows) per wave
+  static constexpr int TPR = NT / DK;       // threads per row in the row stage
+  static constexpr int PSTR = 36;           // row partials: 32 lane pairs per row, padded
+  static constexpr int NCH = DK * DV * 2 / (16 * NT);   // 16-byte chunks per thread, binary16 bound
+  static_assert(TPR == 2, "row stage");
+};
+
+template <int DK>
+struct WRSmem {
+  float red[GeoW<DK>::NW][2][128] __attribute__((aligned(16)));   // per wave: column partials
+  f32x2 ab[DK] __attribute__((aligned(16)));      // by record row: (g k, g q); 0 on pivot rows
+  f32x2 abp[DK] __attribute__((aligned(16)));     // (g k, g q) of the pivot rows
+  float kappa[DK] __attribute__((aligned(16)));   // k / g
+  float gg[DK] __attribute__((aligned(16)));      // g = gate * row scale
+  float rowh[DK] __attribute__((aligned(16)));    // new X factor
+  float rq[DK] __attribute__((aligned(16)));      // 1 / QMAX of the row's width
+  float kqp[GeoW<DK>::NW];
+  int notone[GeoW<DK>::NW];
+  int esum[GeoW<DK>::NW];
+  int ecnt[GeoW<DK>::NW];
+};
+
+template <int DK>
+__global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_wide(KArgs A) {
+  using G = GeoW<DK>;
+  constexpr int DV = 128;
+  __shared__ WRSmem<DK> rs;
+  extern __shared__ u32x4 stage_[];               // the tile's codes, later the row partials
+  uint8_t* stage = (uint8_t*)stage_;
+  float* part = (float*)stage_;
+  const int T = A.n * A.H;
+  const int tau = tile_of_block(T);
+  if (tau >= T) return;
+  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int slot = A.slots ? A.slots[ci] : ci;
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+  const size_t x = (size_t)ci * A.H + h;
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ws0 = 32 * w;                          // first record row of the wave
+  const int* cntp = A.row_cnt + 4 * h;
+  const int c4 = cntp[0], c6 = c4 + cntp[1], c8 = c6 + cntp[2];
+  const int CB = c4 * 64 + cntp[1] * 96 + cntp[2] * 128 + cntp[3] * 256;
+  const int o6 = -32 * c4, o8 = -32 * (c4 + c6), o16 = -32 * (c4 + c6) - 128 * c8;   // record offset - width * 16 * p
+  uint16_t* scl = (uint16_t*)(tile + CB);
+
+  // ---- every global read first ----
+  u32x4 chunk[G::NCH];
+#pragma unroll
+  for (int i = 0; i < G::NCH; i++) {
+    const int off = 16 * (tid + i * G::NT);
+    if (off < CB) chunk[i] = *(const u32x4*)(tile + off);
+  }
+  const int rho = tid >> 1, rsub = tid & 1;        // row stage: record row rho
+  const int irow = A.row_perm[(size_t)h * DK + rho];
+  const int pn = rho < c4 ? 4 : (rho < c6 ? 6 : (rho < c8 ? 8 : 16));
+  float kk = 0.f, qq = 0.f, ai = 1.f, sgr = 1.f;
+  if (rsub == 0) {
+    kk = A.k[x * DK + irow];
+    qq = A.q[x * DK + irow];
+    ai = A.gate ? A.a[x * DK + irow] : A.a[x];
+    sgr = pn == 16 ? 1.f : bf16f(scl[irow]);
+  }
+  const uint32_t cw = *(const uint32_t*)(scl + DK + 2 * l);
+  const f32x2 vv = *(const f32x2*)(A.v + x * DV + 2 * l);
+  const float bb = A.b[x];
+#pragma unroll
+  for (int i = 0; i < G::NCH; i++) {
+    const int off = 16 * (tid + i * G::NT);
+    if (off < CB) *(u32x4*)(stage + off) = chunk[i];
+  }
+  float kq = 0.f;
+  if (rsub == 0) {
+    const float g = ai * sgr;
+    rs.ab[rho] = pn == 16 ? f32x2{0.f, 0.f} : f32x2{g * kk, g * qq};
+    rs.abp[rho] = f32x2{g * kk, g * qq};
+    rs.kappa[rho] = kk * __builtin_amdgcn_rcpf(g);
+    rs.gg[rho] = g;
+    kq = kk * qq;
+  }
+  kq = wave_sum(kq);
+  const bool ne1 = __ballot(ai != 1.f) != 0;
+  if (l == 0) { rs.kqp[w] = kq; rs.notone[w] = ne1; }
+  const float cc0 = bf16f(cw & 0xFFFFu), cc1 = bf16f(cw >> 16);
+  lds_barrier();
+
+  // ---- unpack and the two reductions over the rows: (a S)^T k, (a S)^T q ----
+  // Record rows from c8 on are binary16 pivots: the unrolled loops run them as
+  // 8-bit rows with zero weights (ab, rq) and a store sink, and the row loops
+  // after them do their real work.
+  const int rN = __builtin_amdgcn_readfirstlane(min(max(c8 - ws0, 0), G::NR));   // quantized rows of the wave
+  f16x2 P[G::NR];
+  float U0 = 0.f, U1 = 0.f, W0 = 0.f, W1 = 0.f;
+  {
+    int k4 = c4, k6 = c6, k8 = c8;
+    asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));   // per-phase scalar run bounds
+    uint32_t sbase = (uint32_t)(uintptr_t)stage;      // LDS address of the staged codes
+#pragma unroll
+    for (int r = 0; r < G::NR; r++) {
+      // the lane's two codes start at bit 2 n l of the record: one 64-bit window, two fields
+      const int p = ws0 + r;
+      const int n = 4 + (p >= k4 ? 2 : 0) + (p >= k6 ? 2 : 0);
+      const int rec = 64 * p + 32 * max(p - k4, 0) + 32 * max(p - k6, 0);
+      const uint32_t bit = (uint32_t)(2 * n) * (uint32_t)l;
+      const uint32_t* sw = (const uint32_t*)(stage + ((sbase + rec + 4 * (bit >> 5)) - (uint32_t)(uintptr_t)stage));
+      const uint32_t g = __builtin_amdgcn_alignbit(sw[1], sw[0], bit);
+      const uint32_t f0 = __builtin_amdgcn_ubfe(g, 0, n), f1 = __builtin_amdgcn_ubfe(g, n, n);
+      const uint32_t kb = (0xE400u + (1u << (n - 1))) * 0x10001u;   // -(1024 + 2^(n-1)), both halves
+      P[r] = as_h2(f0 | (f1 << 16) | 0x64006400u) + as_h2(kb);
+      const f32x2 abr = rs.ab[p];
+      const float q0 = (float)P[r][0], q1 = (float)P[r][1];
+      U0 = __builtin_fmaf(q0, abr[0], U0);
+      U1 = __builtin_fmaf(q1, abr[0], U1);
+      W0 = __builtin_fmaf(q0, abr[1], W0);
+      W1 = __builtin_fmaf(q1, abr[1], W1);
+      // one step at a time (the next loads wait for this step's sums): other
+      // resident waves cover the LDS latency, and registers stay few
+      asm volatile("" : "+v"(sbase) : "v"(U0), "v"(U1), "v"(W0), "v"(W1));
+    }
+  }
+  float Up0 = 0.f, Up1 = 0.f, Wp0 = 0.f, Wp1 = 0.f;
+  for (int r = rN; r < G::NR; r++) {               // binary16 pivot rows
+    const int p = ws0 + r;
+    const f16x2 v2 = as_h2(*(const uint32_t*)(stage + 256 * p + o16 + 4 * l));
+    const f32x2 abr = rs.abp[p];
+    Up0 = __builtin_fmaf((float)v2[0], abr[0], Up0);
+    Up1 = __builtin_fmaf((float)v2[1], abr[0], Up1);
+    Wp0 = __builtin_fmaf((float)v2[0], abr[1], Wp0);
+    Wp1 = __builtin_fmaf((float)v2[1], abr[1], Wp1);
+  }
+  *(f32x2*)&rs.red[w][0][2 * l] = f32x2{__builtin_fmaf(cc0, U0, Up0), __builtin_fmaf(cc1, U1, Up1)};
+  *(f32x2*)&rs.red[w][1][2 * l] = f32x2{__builtin_fmaf(cc0, W0, Wp0), __builtin_fmaf(cc1, W1, Wp1)};
+  lds_barrier();
+  int allone = 1;
+  float kqs = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < G::NW; ww++) { allone &= !rs.notone[ww]; kqs += rs.kqp[ww]; }
+  f32x2 u2 = *(const f32x2*)&rs.red[0][0][2 * l], w2 = *(const f32x2*)&rs.red[0][1][2 * l];
+#pragma unroll
+  for (int ww = 1; ww < G::NW; ww++) {
+    u2 += *(const f32x2*)&rs.red[ww][0][2 * l];
+    w2 += *(const f32x2*)&rs.red[ww][1][2 * l];
+  }
+  const float d0 = bb * (vv[0] - u2[0]), d1 = bb * (vv[1] - u2[1]);
+  if (w == 0) *(f32x2*)(A.o + x * DV + 2 * l) = f32x2{__builtin_fmaf(d0, kqs, w2[0]), __builtin_fmaf(d1, kqs, w2[1])};
+  if (bb == 0.f && allone) return;      // identity update: keep the encoding
+
+  // ---- rank-one update, Y = S' / g; row partial maxima over lane pairs ----
+  float Y[2 * G::NR];
+  float* partl = part + ws0 * G::PSTR + (l >> 1);
+#pragma unroll
+  for (int r = 0; r < G::NR; r++) {
+    const float kr = rs.kappa[ws0 + r];
+    Y[2 * r] = __builtin_fmaf((float)P[r][0], cc0, kr * d0);
+    Y[2 * r + 1] = __builtin_fmaf((float)P[r][1], cc1, kr * d1);
+    uint32_t m = __float_as_uint(__builtin_fmaxf(__builtin_fabsf(Y[2 * r]), __builtin_fabsf(Y[2 * r + 1])));
+    m = __builtin_elementwise_max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    partl[r * G::PSTR] = __uint_as_float(m);
+  }
+  lds_barrier();
+
+  // ---- row refit (one thread pair per record row) ----
+  uint32_t mxb = 0u;
+#pragma unroll
+  for (int k4 = 0; k4 < 4; k4++) {
+    const u32x4 m4 = *(const u32x4*)&part[rho * G::PSTR + rsub * 16 + 4 * k4];
+    mxb = __builtin_elementwise_max(mxb, __builtin_elementwise_max(__builtin_elementwise_max(m4[0], m4[1]),
+                                                                   __builtin_elementwise_max(m4[2], m4[3])));
+  }
+  mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
+  const float g = ai * sgr;
+  const float pw = (g * __uint_as_float(mxb)) * A.weights[(size_t)h * DK + irow];
+  uint32_t s = 0x3F80u;
+  int epk = 0;
+  if (pn != 16 && pw > 0.f) {
+    s = bf16_rne(__builtin_amdgcn_sqrtf(pw));
+    epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
+  }
+  if (rsub != 0) epk = 0;
+  if (rsub == 0) {
+    rs.rowh[rho] = g * rcp_bf16(bf16f(s));
+    rs.rq[rho] = pn == 4 ? 1.0f / 7.0f : pn == 6 ? 1.0f / 31.0f : pn == 8 ? 1.0f / 127.0f : 0.f;
+  }
+  epk = wave_sum_i(epk);
+  if (l == 0) { rs.esum[w] = epk >> 8; rs.ecnt[w] = epk & 0xFF; }
+  lds_barrier();
+  int es = 0, ec = 0;
+#pragma unroll
+  for (int ww = 0; ww < G::NW; ww++) { es += rs.esum[ww]; ec += rs.ecnt[ww]; }
+  const int E = ec ? mean_exp(es, ec) : 0;
+  if (rsub == 0) scl[irow] = (uint16_t)bf16_adj(s, -E);
+
+  // ---- column refit ----
+  float cm0 = 0.f, cm1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < G::NR; r++) {
+    const float hr = rs.rowh[ws0 + r], rq = rs.rq[ws0 + r];
+    Y[2 * r] = Y[2 * r] * hr;
+    Y[2 * r + 1] = Y[2 * r + 1] * hr;
+    cm0 = __builtin_fmaxf(cm0, __builtin_fabsf(Y[2 * r]) * rq);
+    cm1 = __builtin_fmaxf(cm1, __builtin_fabsf(Y[2 * r + 1]) * rq);
+  }
+  *(f32x2*)&rs.red[w][0][2 * l] = f32x2{cm0, cm1};
+  lds_barrier();
+  f32x2 M2 = *(const f32x2*)&rs.red[0][0][2 * l];
+#pragma unroll
+  for (int ww = 1; ww < G::NW; ww++) {
+    const f32x2 o2 = *(const f32x2*)&rs.red[ww][0][2 * l];
+    M2[0] = __builtin_fmaxf(M2[0], o2[0]);
+    M2[1] = __builtin_fmaxf(M2[1], o2[1]);
+  }
+  float rc[2];
+  uint32_t cb[2];
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    uint32_t t = 0x3F80u;
+    if (c8 > 0 && M2[c] > 0.f) {
+      t = bf16_ru_pos(M2[c]);
+      if (t < 0x0080u) t = 0x0080u;
+    }
+    rc[c] = rcp_bf16(bf16f(t));
+    cb[c] = bf16_adj(t, E);
+  }
+  if (w == 0) *(uint32_t*)(scl + DK + 2 * l) = cb[0] | (cb[1] << 16);
+
+  // ---- requantize into the staged records ----
+  const int q4 = l & 3, pq = q4 < 2 ? q4 : 2;      // 6-bit: lane q4 of a quad writes 16-bit piece pq
+  const int L6w = 6 * (l >> 2) + 2 * pq;
+  const uint32_t sh6 = 20 + 4 * pq;
+  const int sink = CB + 16;                        // 128 bytes past the codes: stores of pivot steps
+  int k4 = c4, k6 = c6, k8 = c8;
+  asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));
+#pragma unroll
+  for (int r = 0; r < G::NR; r++) {
+    const int p = ws0 + r;
+    if (p < k4) {
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], Fmt<4>::MAGIC));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], Fmt<4>::MAGIC));
+      stage[64 * p + l] = (uint8_t)(y0 | (y1 << 4));
+    } else if (p < k6) {
+      // a lane quad holds two 3-byte groups: 12 bits per lane, written as three 16-bit pieces
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], Fmt<6>::MAGIC));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], Fmt<6>::MAGIC));
+      const uint32_t g12 = y0 | (y1 << 6);
+      const uint32_t ga = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g12, 0xA4, 0xF, 0xF, false);   // lane pq
+      const uint32_t gb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g12, 0xF9, 0xF, 0xF, false);   // lane pq + 1
+      *(uint16_t*)(stage + 96 * p + o6 + L6w) = (uint16_t)__builtin_amdgcn_alignbit(gb, ga << 20, sh6);
+    } else {
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], Fmt<8>::MAGIC));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], Fmt<8>::MAGIC));
+      *(uint16_t*)(stage + (p < k8 ? 128 * p + o8 : sink) + 2 * l) = (uint16_t)(y0 | (y1 << 8));
+    }
+  }
+  for (int r = rN; r < G::NR; r++) {               // binary16 pivot rows: S' = g (v + kappa delta)
+    const int p = ws0 + r;
+    const int off = 256 * p + o16 + 4 * l;
+    const f16x2 v2 = as_h2(*(const uint32_t*)(tile + off));   // the tile's bytes are unchanged until the store
+    const float kr = rs.kappa[p], gr = rs.gg[p];
+    const float s0 = __builtin_fminf(__builtin_fmaxf(gr * __builtin_fmaf((float)v2[0], 1.f, kr * d0), -65504.f), 65504.f);
+    const float s1 = __builtin_fminf(__builtin_fmaxf(gr * __builtin_fmaf((float)v2[1], 1.f, kr * d1), -65504.f), 65504.f);
+    *(uint32_t*)(stage + off) = h2_bits(f16x2{(f16)s0, (f16)s1});
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < G::NCH; i++) {
+    const int off = 16 * (tid + i * G::NT);
+    if (off < CB) *(u32x4*)(tile + off) = *(const u32x4*)(stage + off);
+  }
+}
+
+// ------------------------------------------------------------------------
 // Fetch (D) and fixed-scale requantization of per-head tiles.
 // ------------------------------------------------------------------------
 template <int DK, int DV, int N, bool REQ>
@@ -1483,10 +1768,11 @@ void layout(const stq_pool_desc* d, stq_pool* p) {
     }
   }
   p->slot_bytes = s;
-  // staged codes plus the word the last group's decode reads past them, or the
-  // row partials [d_k][d_v/4 + 4] floats, whichever is larger
+  // staged codes plus the word the last group's decode reads past them and a
+  // store sink, or the row partials [d_k][d_v/4 + 4] floats, whichever is larger
   const uint64_t partb = 4ull * p->dk * (p->dv / 4 + 4);
-  p->rows_stage = (uint32_t)(((cbmax + 16 > partb ? cbmax + 16 : partb) + 15) / 16 * 16);
+  const uint64_t codeb = cbmax + 16 + 2 * p->dv;   // codes, read-ahead word, store sink of pivot steps
+  p->rows_stage = (uint32_t)(((codeb > partb ? codeb : partb) + 15) / 16 * 16);
   p->woff = ru256(64 + 8ull * p->H);
   p->roff = ru256(p->woff + 4ull * p->H * p->dk);
   p->hdr = rows ? ru256(p->roff + 2ull * p->H * p->dk + 16ull * p->H) : p->roff;
@@ -1558,14 +1844,19 @@ struct LWindow {
     }
   };
 };
-struct LRowStep {
-  template <int DK, int DV>
-  struct T {
-    static void go(const KArgs& A, unsigned g, hipStream_t st) {
-      hipLaunchKernelGGL((k_rows_step<DK, DV>), dim3(g), dim3(GeoR<DK, DV>::NT), A.stage_bytes, st, A);
-    }
-  };
-};
+// per-key-row decode step: whole-row waves for d_v = 128, row-sharing waves for d_v = 64
+stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st) {
+  const unsigned g = grid_of(A.n, A.H);
+  if (p->dv == 128 && p->dk == 128)
+    hipLaunchKernelGGL((k_rows_wide<128>), dim3(g), dim3(GeoW<128>::NT), A.stage_bytes, st, A);
+  else if (p->dv == 128)
+    hipLaunchKernelGGL((k_rows_wide<64>), dim3(g), dim3(GeoW<64>::NT), A.stage_bytes, st, A);
+  else if (p->dk == 128)
+    hipLaunchKernelGGL((k_rows_step<128, 64>), dim3(g), dim3(GeoR<128, 64>::NT), A.stage_bytes, st, A);
+  else
+    hipLaunchKernelGGL((k_rows_step<64, 64>), dim3(g), dim3(GeoR<64, 64>::NT), A.stage_bytes, st, A);
+  return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
+}
 template <bool REQ>
 struct LFetch {
   template <int DK, int DV>
@@ -1707,7 +1998,7 @@ stq_status stq_decode_step(stq_pool* p, const int32_t* slots, int32_t n, const f
   KArgs A = base_args(p, slots, n);
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
   if (p->W > 0) return dispatch<LWindow<false>::T>(p, A, st);
-  if (p->unit == STQ_UNIT_ROW) return dispatch<LRowStep::T>(p, A, st);
+  if (p->unit == STQ_UNIT_ROW) return dispatch_rows_step(p, A, st);
   return dispatch<LTile<MODE_STEP>::T>(p, A, st);
 }
 
