@@ -1529,7 +1529,7 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
     Y[2 * r] = __builtin_fmaf((float)P[r][0], cc0, kr * d0);
     Y[2 * r + 1] = __builtin_fmaf((float)P[r][1], cc1, kr * d1);
     uint32_t m = __float_as_uint(__builtin_fmaxf(__builtin_fabsf(Y[2 * r]), __builtin_fabsf(Y[2 * r + 1])));
-    m = __builtin_elementwise_max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    m = __builtin_elementwise_max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, true));
     partl[r * G::PSTR] = __uint_as_float(m);
   }
   lds_barrier();
@@ -1605,24 +1605,26 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   const int sink = CB + 16;                        // 128 bytes past the codes: stores of pivot steps
   int k4 = c4, k6 = c6, k8 = c8;
   asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));
+  float mg4 = Fmt<4>::MAGIC, mg6 = Fmt<6>::MAGIC, mg8 = Fmt<8>::MAGIC;
+  asm volatile("" : "+s"(mg4), "+s"(mg6), "+s"(mg8));   // scalar operands of the fma
 #pragma unroll
   for (int r = 0; r < G::NR; r++) {
     const int p = ws0 + r;
     if (p < k4) {
-      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], Fmt<4>::MAGIC));
-      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], Fmt<4>::MAGIC));
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], mg4));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], mg4));
       stage[64 * p + l] = (uint8_t)(y0 | (y1 << 4));
     } else if (p < k6) {
       // a lane quad holds two 3-byte groups: 12 bits per lane, written as three 16-bit pieces
-      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], Fmt<6>::MAGIC));
-      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], Fmt<6>::MAGIC));
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], mg6));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], mg6));
       const uint32_t g12 = y0 | (y1 << 6);
-      const uint32_t ga = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g12, 0xA4, 0xF, 0xF, false);   // lane pq
-      const uint32_t gb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g12, 0xF9, 0xF, 0xF, false);   // lane pq + 1
+      const uint32_t ga = (uint32_t)__builtin_amdgcn_mov_dpp((int)g12, 0xA4, 0xF, 0xF, true);   // lane pq
+      const uint32_t gb = (uint32_t)__builtin_amdgcn_mov_dpp((int)g12, 0xF9, 0xF, 0xF, true);   // lane pq + 1
       *(uint16_t*)(stage + 96 * p + o6 + L6w) = (uint16_t)__builtin_amdgcn_alignbit(gb, ga << 20, sh6);
     } else {
-      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], Fmt<8>::MAGIC));
-      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], Fmt<8>::MAGIC));
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], mg8));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], mg8));
       *(uint16_t*)(stage + (p < k8 ? 128 * p + o8 : sink) + 2 * l) = (uint16_t)(y0 | (y1 << 8));
     }
   }
