@@ -161,8 +161,8 @@ __device__ __forceinline__ void fp16_scale(float m, float& sc, float& inv) {
 }
 
 // matvec A fragments of row i: fp16 hi/lo of the scaled (g k, g q)
-template <int DK, int DV, int N>
-__device__ __forceinline__ void put_afr(SmemM<DK, DV>& sm, int i, float al, float be) {
+template <int DK, int DV, int N, class S>
+__device__ __forceinline__ void put_afr(S& sm, int i, float al, float be) {
   const int rc = i >> 5, G = (i >> 2) & 3, t = 4 * ((i >> 4) & 1) + (i & 3);
   const int k = t_to_kk<N>(t);
   const f16 ah = (f16)al, bh = (f16)be;
@@ -174,8 +174,8 @@ __device__ __forceinline__ void put_afr(SmemM<DK, DV>& sm, int i, float al, floa
 
 // D[cc] = (alpha_hi, alpha_lo, beta_hi, beta_lo) . Q over all rows, for the
 // lane's column of chunk cc
-template <int DK, int DV>
-__device__ __forceinline__ void matvec(const SmemM<DK, DV>& sm, const f16x2* P, f32x4* D) {
+template <int DK, int DV, class S>
+__device__ __forceinline__ void matvec(const S& sm, const f16x2* P, f32x4* D) {
   using G = GeoM<DK, DV>;
   const int l = threadIdx.x & 63;
   f16x8 af[G::NRC];
@@ -205,11 +205,13 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 // sm.gg, visible after the next barrier); for a binary16 pivot tile Y holds
 // S' itself.  Writes codes, row and column scales.
 // ------------------------------------------------------------------------
-template <int DK, int DV, int N, bool EXACT>
+template <int DK, int DV, int N, bool EXACT, bool OPQ = false>
 __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t* tile, float wgt) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  int tid = threadIdx.x;
+  if (OPQ) asm volatile("" : "+v"(tid));      // inside a loop: keep lane indices out of its preheader
+  const int w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
   uint8_t* codes = tile;
   uint16_t* scl = (uint16_t*)(tile + DK * DV * N / 8);
   uint32_t raw[2 * N];
@@ -492,13 +494,23 @@ struct WSmem {
   // not written before the fold's last read, whenever it fits there
   static constexpr bool IN_PART = WMAX * DK <= DK * GeoM<DK, DV>::PSTR;
   float kap[IN_PART ? 4 : WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i)
-  float cfk[WMAX];                                        // (G_t/G_s) k_s.k_t
-  float cfq[WMAX];                                        // (G_t/G_s) k_s.q_t
 };
 
-template <int DK, int DV, int N, bool FLUSH>
-__device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK, DV>& ws, uint8_t* tile,
-                                            uint8_t* cache, size_t x, int h) {
+// LDS of the readout-and-append kernel
+template <int DK, int DV>
+struct WRead {
+  f16 afr[DK / 32][4][4][8] __attribute__((aligned(16)));   // matvec A fragments
+  f32x2 kqn[GeoM<DK, DV>::NW];                              // per wave: k.q partial sum
+  float cfk[WMAX];                                          // (G_t/G_s) k_s.k_t
+  float cfq[WMAX];                                          // (G_t/G_s) k_s.q_t
+};
+
+// One token of an open window: readout from the frozen base and the cache,
+// then the token's (G_t, k_t, u_t) appended.  A window that this token fills
+// (t + 1 = W) is left full for the fold kernel that runs next.
+template <int DK, int DV, int N>
+__device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, uint8_t* tile, uint8_t* cache,
+                                            size_t x) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
   constexpr bool PIV = (N == 16);
@@ -511,19 +523,129 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
   float* Gc = (float*)(cache + 4);
   float* Kc = (float*)(cache + 256);
   float* Uc = Kc + (size_t)W * DK;
-  float* kap = WSmem<DK, DV>::IN_PART ? sm.part : ws.kap;
   const int t = *cntp;                         // tokens already in the window
-  if (FLUSH && t == 0) return;                 // nothing to fold
-  const bool fold = FLUSH || (t + 1 == W);
-  const int ns = FLUSH ? t : t + 1;            // tokens in the fold
-  float Gt;
-  if constexpr (FLUSH) {
-    Gt = Gc[t - 1];
-  } else {
-    const float a = A.a[x];
-    Gt = t ? Gc[t - 1] * a : a;                // binary32 running product
+  if (t >= W) return;                          // full: only the fold may touch it
+  const float a = A.a[x];
+  const float Gt = t ? Gc[t - 1] * a : a;      // binary32 running product
+  // the tile's global reads first
+  uint32_t raw[2 * N];
+  f16x2 P[32];
+#pragma unroll
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+  float cc[G::NCC];
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) cc[c] = PIV ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
+  float sc, inv;
+  {
+    float gl = 0.f;
+#pragma unroll
+    for (int i = l; i < DK; i += 64) gl = __builtin_fmaxf(gl, PIV ? 1.f : bf16f(scl[i]));
+    fp16_scale(wave_max_pos(gl), sc, inv);
   }
-  // every global read of the tile and of the lane's cached u entries first
+  // ---- per-row work (once per row) ----
+  float kq = 0.f;
+  if (rsub == 0) {
+    const float sg = PIV ? 1.f : bf16f(scl[rho]);
+    const float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
+    put_afr<DK, DV, N>(sm, rho, (sg * sc) * kk, (sg * sc) * qq);
+    kq = kk * qq;
+    Kc[(size_t)t * DK + rho] = kk;                       // append k_t
+  }
+  kq = wave_sum(kq);
+  if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
+  // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per token
+  for (int s = tid / 8; s < t; s += G::NT / 8) {
+    float ak = 0.f, aq = 0.f;
+#pragma unroll
+    for (int i = 4 * (tid % 8); i < DK; i += 32) {
+      const f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i);
+      const f32x4 kv = *(const f32x4*)(A.k + x * DK + i);
+      const f32x4 qv = *(const f32x4*)(A.q + x * DK + i);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        ak = __builtin_fmaf(ks[e], kv[e], ak);
+        aq = __builtin_fmaf(ks[e], qv[e], aq);
+      }
+    }
+    ak = rb_sum<8>(ak);
+    aq = rb_sum<8>(aq);
+    if (tid % 8 == 0) {
+      const float r = Gt / Gc[s];
+      sm.cfk[s] = r * ak;
+      sm.cfq[s] = r * aq;
+    }
+  }
+  __syncthreads();
+  // the lane quad's cached u entries (s = 4i + Gq), in flight during the matvec
+  float uq[UQ][G::NCC];
+#pragma unroll
+  for (int i = 0; i < UQ; i++)
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+      uq[i][c] = 4 * i + Gq < t ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
+  unpack<N>(raw, P);
+  // ---- readout and written vector from the frozen base and the cache ----
+  float kqs = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
+  f32x4 D[G::NCC];
+  matvec<DK, DV>(sm, P, D);
+  const float bb = A.b[x];
+  // cache terms: quad G sums its tokens s = 4i + G, then the four quads add up
+  float pk[G::NCC], pq[G::NCC];
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) pk[c] = pq[c] = 0.f;
+#pragma unroll
+  for (int i = 0; i < UQ; i++) {
+    if (4 * i >= t) break;
+    const int s = 4 * i + Gq;
+    const float fk = s < t ? sm.cfk[s] : 0.f, fq = s < t ? sm.cfq[s] : 0.f;
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) {
+      pk[c] = __builtin_fmaf(fk, uq[i][c], pk[c]);
+      pq[c] = __builtin_fmaf(fq, uq[i][c], pq[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) {
+    const int j = w * G::CPW + 16 * c + n16;
+    const float rr = A.v[x * DV + j] - Gt * (cc[c] * ((D[c][0] + D[c][1]) * inv)) - g4_sum(pk[c]);
+    const float oo = Gt * (cc[c] * ((D[c][2] + D[c][3]) * inv)) + g4_sum(pq[c]);
+    const float u2 = bb * rr;
+    if (Gq == 0) {
+      A.o[x * DV + j] = __builtin_fmaf(kqs, u2, oo);
+      Uc[(size_t)t * DV + j] = u2;                         // append u_t
+    }
+  }
+  if (tid == 0) {
+    Gc[t] = Gt;
+    *cntp = t + 1;
+  }
+}
+
+// Fold of a tile's open window: S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T, refit,
+// window emptied.  Folds windows holding at least `need` tokens.
+template <int DK, int DV, int N>
+__device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK, DV>& ws, uint8_t* tile,
+                                            uint8_t* cache, int h, int need) {
+  using G = GeoM<DK, DV>;
+  constexpr int K = N / 2;
+  constexpr bool PIV = (N == 16);
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));                // the fold kernel loops over tiles: keep lane indices local
+  const int w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  const int rho = tid / G::TPR, rsub = tid % G::TPR;
+  uint8_t* codes = tile;
+  const uint16_t* scl = (const uint16_t*)(tile + DK * DV * N / 8);
+  const int W = A.W;
+  int32_t* cntp = (int32_t*)cache;
+  float* Gc = (float*)(cache + 4);
+  float* Kc = (float*)(cache + 256);
+  float* Uc = Kc + (size_t)W * DK;
+  float* kap = WSmem<DK, DV>::IN_PART ? sm.part : ws.kap;
+  const int ns = *cntp;                        // tokens in the window
+  if (ns < need || ns == 0) return;
+  const float Gt = Gc[ns - 1];
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
@@ -536,109 +658,20 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
   for (int i = 0; i < UQ; i++)
 #pragma unroll
     for (int c = 0; c < G::NCC; c++)
-      uq[i][c] = 4 * i + Gq < t ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
-  float sc = 1.f, inv = 1.f;
-  if constexpr (!FLUSH) {
-    float gl = 0.f;
+      uq[i][c] = 4 * i + Gq < ns ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
+  if (rsub == 0) sm.gg[rho] = Gt * (PIV ? 1.f : bf16f(scl[rho]));
+  // kappa_s,i = k_s,i / (G_s sigma_i) for every token of the window, 4 rows per item
+  for (int j = tid; j < ns * (DK / 4); j += G::NT) {
+    const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
+    const f32x4 kv = *(const f32x4*)(Kc + (size_t)s * DK + r0);
+    const float gs = Gc[s];
+    f32x4 o4;
 #pragma unroll
-    for (int i = l; i < DK; i += 64) gl = __builtin_fmaxf(gl, PIV ? 1.f : bf16f(scl[i]));
-    fp16_scale(wave_max_pos(gl), sc, inv);
-  }
-  // ---- per-row work (once per row) ----
-  float kq = 0.f;
-  if (rsub == 0) {
-    const float sg = PIV ? 1.f : bf16f(scl[rho]);
-    if constexpr (!FLUSH) {
-      const float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
-      put_afr<DK, DV, N>(sm, rho, (sg * sc) * kk, (sg * sc) * qq);
-      kq = kk * qq;
-      Kc[(size_t)t * DK + rho] = kk;                       // append k_t
-    }
-    if (fold) sm.gg[rho] = Gt * sg;
-  }
-  if (fold) {
-    // kappa_s,i = k_s,i / (G_s sigma_i) for every token of the fold, 4 rows per item
-    for (int j = tid; j < ns * (DK / 4); j += G::NT) {
-      const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
-      const bool cur = !FLUSH && s == t;
-      const f32x4 kv = *(const f32x4*)((cur ? A.k + x * DK : Kc + (size_t)s * DK) + r0);
-      const float gs = cur ? Gt : Gc[s];
-      f32x4 o4;
-#pragma unroll
-      for (int e = 0; e < 4; e++) o4[e] = kv[e] / (gs * (PIV ? 1.f : bf16f(scl[r0 + e])));
-      *(f32x4*)&kap[s * DK + r0] = o4;
-    }
-  }
-  if constexpr (!FLUSH) {
-    kq = wave_sum(kq);
-    if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
-    // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per token
-    for (int s = tid / 8; s < t; s += G::NT / 8) {
-      float ak = 0.f, aq = 0.f;
-#pragma unroll
-      for (int i = 4 * (tid % 8); i < DK; i += 32) {
-        const f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i);
-        const f32x4 kv = *(const f32x4*)(A.k + x * DK + i);
-        const f32x4 qv = *(const f32x4*)(A.q + x * DK + i);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          ak = __builtin_fmaf(ks[e], kv[e], ak);
-          aq = __builtin_fmaf(ks[e], qv[e], aq);
-        }
-      }
-      ak = rb_sum<8>(ak);
-      aq = rb_sum<8>(aq);
-      if (tid % 8 == 0) {
-        const float r = Gt / Gc[s];
-        ws.cfk[s] = r * ak;
-        ws.cfq[s] = r * aq;
-      }
-    }
+    for (int e = 0; e < 4; e++) o4[e] = kv[e] / (gs * (PIV ? 1.f : bf16f(scl[r0 + e])));
+    *(f32x4*)&kap[s * DK + r0] = o4;
   }
   __syncthreads();
   unpack<N>(raw, P);
-  float u2[G::NCC];
-  if constexpr (!FLUSH) {
-    // ---- readout and written vector from the frozen base and the cache ----
-    float kqs = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
-    f32x4 D[G::NCC];
-    matvec<DK, DV>(sm, P, D);
-    const float bb = A.b[x];
-    // cache terms: quad G sums its tokens s = 4i + G, then the four quads add up
-    float pk[G::NCC], pq[G::NCC];
-#pragma unroll
-    for (int c = 0; c < G::NCC; c++) pk[c] = pq[c] = 0.f;
-#pragma unroll
-    for (int i = 0; i < UQ; i++) {
-      if (4 * i >= t) break;
-      const int s = 4 * i + Gq;
-      const float fk = s < t ? ws.cfk[s] : 0.f, fq = s < t ? ws.cfq[s] : 0.f;
-#pragma unroll
-      for (int c = 0; c < G::NCC; c++) {
-        pk[c] = __builtin_fmaf(fk, uq[i][c], pk[c]);
-        pq[c] = __builtin_fmaf(fq, uq[i][c], pq[c]);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < G::NCC; c++) {
-      const int j = w * G::CPW + 16 * c + n16;
-      const float rr = A.v[x * DV + j] - Gt * (cc[c] * ((D[c][0] + D[c][1]) * inv)) - g4_sum(pk[c]);
-      const float oo = Gt * (cc[c] * ((D[c][2] + D[c][3]) * inv)) + g4_sum(pq[c]);
-      u2[c] = bb * rr;
-      if (Gq == 0) {
-        A.o[x * DV + j] = __builtin_fmaf(kqs, u2[c], oo);
-        Uc[(size_t)t * DV + j] = u2[c];                     // append u_t
-      }
-    }
-    if (tid == 0) {
-      Gc[t] = Gt;
-      if (!fold) *cntp = t + 1;
-    }
-    if (!fold) return;
-  }
-  // ---- fold: S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T  ->  refit, window emptied ----
   opaque(P);
   float Y[64];
 #pragma unroll
@@ -660,10 +693,7 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
         const int s = 4 * i + Gq;
         const float kv = s < ns ? kap[s * DK + r0 + n16] : 0.f;
 #pragma unroll
-        for (int c = 0; c < G::NCC; c++) {
-          const float uv = (!FLUSH && s == t) ? u2[c] : uq[i][c];
-          C[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, uv, C[c], 0, 0, 0);
-        }
+        for (int c = 0; c < G::NCC; c++) C[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, uq[i][c], C[c], 0, 0, 0);
       }
 #pragma unroll
       for (int c = 0; c < G::NCC; c++) {
@@ -674,13 +704,13 @@ __device__ __forceinline__ void window_body(const KArgs& A, SmemM<DK, DV>& sm, W
     }
   if (tid == 0) *cntp = 0;
   if constexpr (WSmem<DK, DV>::IN_PART) lds_barrier();     // kappa reads done before the partials
-  refit_store<DK, DV, N, false>(sm, Y, tile, A.weights[(size_t)h * DK + rho]);
+  refit_store<DK, DV, N, false, true>(sm, Y, tile, A.weights[(size_t)h * DK + rho]);
 }
 
-template <int DK, int DV, bool FLUSH>
-__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_window(KArgs A) {
-  __shared__ SmemM<DK, DV> sm;
-  __shared__ WSmem<DK, DV> ws;
+// readout and append of every tile of the call
+template <int DK, int DV>
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(5))) void k_window_read(KArgs A) {
+  __shared__ WRead<DK, DV> sm;
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
@@ -691,10 +721,54 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
   const size_t x = (size_t)ci * A.H + h;
   switch (A.head_bits[h]) {
-    case 4: window_body<DK, DV, 4, FLUSH>(A, sm, ws, tile, cache, x, h); break;
-    case 6: window_body<DK, DV, 6, FLUSH>(A, sm, ws, tile, cache, x, h); break;
-    case 8: window_body<DK, DV, 8, FLUSH>(A, sm, ws, tile, cache, x, h); break;
-    default: window_body<DK, DV, 16, FLUSH>(A, sm, ws, tile, cache, x, h); break;
+    case 4: window_read<DK, DV, 4>(A, sm, tile, cache, x); break;
+    case 6: window_read<DK, DV, 6>(A, sm, tile, cache, x); break;
+    case 8: window_read<DK, DV, 8>(A, sm, tile, cache, x); break;
+    default: window_read<DK, DV, 16>(A, sm, tile, cache, x); break;
+  }
+}
+
+// Fold.  STEP (after a decode step): a workgroup reads the window counts of
+// FPW tiles of the call, one per lane, and folds the full ones in turn; an
+// empty launch costs one wave of small workgroups.  Flush: one tile per
+// workgroup, any non-empty window.
+constexpr int FPW = 16;
+template <int DK, int DV, bool STEP>
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_window_fold(KArgs A) {
+  __shared__ SmemM<DK, DV> sm;
+  __shared__ WSmem<DK, DV> ws;
+  const int T = A.n * A.H;
+  const int t0 = STEP ? (int)blockIdx.x * FPW : tile_of_block(T);
+  const int need = STEP ? A.W : 1;
+  uint64_t mask;
+  {
+    bool due = false;
+    const int i = threadIdx.x & 63, tau = t0 + i;
+    if (i < (STEP ? FPW : 1) && tau < T) {
+      const int ci = tau / A.H, h = tau - ci * A.H;
+      const int slot = A.slots[ci];
+      if ((unsigned)slot < (unsigned)A.n_slots)
+        due = *(const int32_t*)(A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride) >= need;
+    }
+    mask = __ballot(due);
+  }
+  bool first = true;
+  while (mask) {
+    const int i = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const int tau = t0 + i;
+    const int ci = tau / A.H, h = tau - ci * A.H;
+    const int slot = A.slots[ci];
+    uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
+    uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
+    if (!first) __syncthreads();               // the previous fold's LDS reads are done
+    first = false;
+    switch (A.head_bits[h]) {
+      case 4: window_fold<DK, DV, 4>(A, sm, ws, tile, cache, h, need); break;
+      case 6: window_fold<DK, DV, 6>(A, sm, ws, tile, cache, h, need); break;
+      case 8: window_fold<DK, DV, 8>(A, sm, ws, tile, cache, h, need); break;
+      default: window_fold<DK, DV, 16>(A, sm, ws, tile, cache, h, need); break;
+    }
   }
 }
 
@@ -1837,15 +1911,6 @@ struct LRows {
     }
   };
 };
-template <bool FLUSH>
-struct LWindow {
-  template <int DK, int DV>
-  struct T {
-    static void go(const KArgs& A, unsigned g, hipStream_t st) {
-      hipLaunchKernelGGL((k_window<DK, DV, FLUSH>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
-    }
-  };
-};
 // per-key-row decode step: whole-row waves for d_v = 128, row-sharing waves for d_v = 64
 stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st) {
   const unsigned g = grid_of(A.n, A.H);
@@ -1857,6 +1922,24 @@ stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st)
     hipLaunchKernelGGL((k_rows_step<128, 64>), dim3(g), dim3(GeoR<128, 64>::NT), A.stage_bytes, st, A);
   else
     hipLaunchKernelGGL((k_rows_step<64, 64>), dim3(g), dim3(GeoR<64, 64>::NT), A.stage_bytes, st, A);
+  return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
+}
+// window mode: readout and append, then the fold of full windows (or, for a flush, of any open one)
+template <int DK, int DV>
+void launch_window(const KArgs& A, bool step, hipStream_t st) {
+  if (step) {
+    hipLaunchKernelGGL((k_window_read<DK, DV>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    const unsigned T = (unsigned)A.n * (unsigned)A.H;
+    hipLaunchKernelGGL((k_window_fold<DK, DV, true>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
+  } else {
+    hipLaunchKernelGGL((k_window_fold<DK, DV, false>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
+  }
+}
+stq_status dispatch_window(const stq_pool* p, const KArgs& A, bool step, hipStream_t st) {
+  if (p->dk == 128 && p->dv == 128) launch_window<128, 128>(A, step, st);
+  else if (p->dk == 64 && p->dv == 64) launch_window<64, 64>(A, step, st);
+  else if (p->dk == 64 && p->dv == 128) launch_window<64, 128>(A, step, st);
+  else launch_window<128, 64>(A, step, st);
   return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
 }
 template <bool REQ>
@@ -1999,7 +2082,7 @@ stq_status stq_decode_step(stq_pool* p, const int32_t* slots, int32_t n, const f
   if (!q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
   KArgs A = base_args(p, slots, n);
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
-  if (p->W > 0) return dispatch<LWindow<false>::T>(p, A, st);
+  if (p->W > 0) return dispatch_window(p, A, true, st);
   if (p->unit == STQ_UNIT_ROW) return dispatch_rows_step(p, A, st);
   return dispatch<LTile<MODE_STEP>::T>(p, A, st);
 }
@@ -2010,7 +2093,7 @@ stq_status stq_window_flush(stq_pool* p, const int32_t* slots, int32_t n, hipStr
   if (p->W == 0) return STQ_ERR_STATE;
   if (n == 0) return STQ_OK;
   KArgs A = base_args(p, slots, n);
-  return dispatch<LWindow<true>::T>(p, A, st);
+  return dispatch_window(p, A, false, st);
 }
 
 stq_status stq_debug_rcp_bf16(float* out_dev, hipStream_t st) {
