@@ -554,7 +554,11 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   kq = wave_sum(kq);
   if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
   // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per token
-  for (int s = tid / 8; s < t; s += G::NT / 8) {
+  // (a fixed number of passes, so that the loads issue with the tile's)
+#pragma unroll
+  for (int it = 0; it < (WMAX + G::NT / 8 - 1) / (G::NT / 8); it++) {
+    const int s = tid / 8 + it * (G::NT / 8);
+    if (s >= t) continue;
     float ak = 0.f, aq = 0.f;
 #pragma unroll
     for (int i = 4 * (tid % 8); i < DK; i += 32) {

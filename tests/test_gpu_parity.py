@@ -222,6 +222,51 @@ def test_rows_step_shapes(torch_cuda, orc, dk, dv):
     assert worst["o"] <= 1.0
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_kda_gate_per_head_widths(torch_cuda, orc, dk, dv):
+    """Per-channel (KDA) gate on per-head widths: the gate vector scales each
+    key row of the tile before the delta update.  Three teacher-forced steps,
+    then the identity rule with a gate vector of ones."""
+    from types import SimpleNamespace
+    say("case KDA gate, per-head widths", dk, dv)
+    rng = np.random.default_rng(300 + dk)
+    H, B = 8, 6
+    cfg = SimpleNamespace(gate=1, unit=0, window=0)
+    wl = SimpleNamespace(B=B, H=H, dk=dk, dv=dv, cfg=cfg, bits=np.array([4, 6, 8, 16, 6, 4, 8, 6], np.int32),
+                         row_weight=np.clip(np.exp(rng.normal(0, 1.15, (H, dk))), 0.1, 10).astype(np.float32))
+    P = Pair(orc, wl, n_slots=B + 1)
+    slots = rng.permutation(B + 1)[:B]
+    prof = np.exp(rng.normal(0, 1.5, (1, H, dk, 1))) * np.exp(rng.normal(0, 1.5, (1, H, 1, dv)))
+    P.store(slots, (0.1 * rng.standard_normal((B, H, dk, dv)) * prof).astype(np.float32))
+    f = lambda x: x.astype(np.float32)
+    worst = dict(mism=0, codes=0, maxd=0, scale_mism=0, scales=0, piv_bad=0, piv=0, piv_mism=0, o=0.0)
+    for t in range(3):
+        img = P.image()
+        ref = orc.OraclePool(B + 1, H, dk, dv, wl.bits, wl.row_weight, 1, 0, 0, image=img)
+        q = rng.standard_normal((B, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k = rng.standard_normal((B, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((B, H, dv))
+        a = 2.0 ** (-1.0 / (10.0 ** rng.uniform(0, 4, (B, H, dk))))
+        b = rng.uniform(0.05, 0.95, (B, H))
+        o = P.gpu_step(slots, f(q), f(k), f(v), f(a), f(b))
+        o_ref = ref.step(slots, f(q), f(k), f(v), f(a), f(b))
+        r = compare_codes(orc, ref, P.image(), ref.img, slots)
+        for key in ("mism", "codes", "scale_mism", "scales", "piv_bad", "piv", "piv_mism"):
+            worst[key] += r[key]
+        worst["maxd"] = max(worst["maxd"], r["maxd"])
+        worst["o"] = max(worst["o"], readout_ok(o, o_ref))
+    say("  KDA %dx%d: code mismatch %d of %d (max |dQ| %d), pivot mismatch %d of %d, readout %.3f"
+        % (dk, dv, worst["mism"], worst["codes"], worst["maxd"], worst["piv_mism"], worst["piv"], worst["o"]))
+    _assert_codes(worst)
+    assert worst["o"] <= 1.0
+    before = P.image()
+    q = f(rng.standard_normal((B, H, dk)))
+    k = f(rng.standard_normal((B, H, dk)))
+    v = f(rng.standard_normal((B, H, dv)))
+    P.gpu_step(slots, q, k, v, np.ones((B, H, dk), np.float32), np.zeros((B, H), np.float32))
+    np.testing.assert_array_equal(P.image(), before)
+
+
 def test_empty_and_out_of_range(torch_cuda, orc):
     say("case edges")
     torch = torch_cuda
