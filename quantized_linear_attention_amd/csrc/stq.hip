@@ -315,6 +315,28 @@ __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t
   for (int k = 0; k < K; k++) *(u32x4*)(codes + 16 * ((w * K + k) * 64 + l)) = *(const u32x4*)&raw[4 * k];
 }
 
+// Clear the codes of the rows flagged (nonzero) in sm.rowh: their old state
+// is multiplied by a zero gate.
+template <int DK, int DV, int N>
+__device__ __forceinline__ void clear_rows(const SmemM<DK, DV>& sm, f16x2* P) {
+  using G = GeoM<DK, DV>;
+  const int Gq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      const f32x4 f = *(const f32x4*)&sm.rowh[erow(rc, 4 * hf, Gq)];
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int e = 8 * (c * G::NRC + rc) + 4 * hf + i, r = e >> 2, cq = e & 3;
+          f16x2& pr = P[preg<N>(r, cq)];
+          pr[phalf<N>(r, cq)] = f[i] != 0.f ? (f16)0.f : pr[phalf<N>(r, cq)];
+        }
+    }
+}
+
 // ------------------------------------------------------------------------
 // Tile body: MODE_STEP = decode step (unpack, gate, delta update, readout,
 // then refit_store); MODE_STORE = refit_store of a given fp32 tile.
@@ -371,18 +393,24 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     fp16_scale(wave_max_pos(gl), sc, inv);
     // ---- per-row factors (once per row) ----
     const float g = ar * sr;
+    // A zero (or subnormal) gate drops the row's old state, S'_i = k_i delta: the
+    // row is carried with factor 1 and its codes are cleared before the update.
+    const bool zg = !PIV && !(g >= 0x1p-126f);
     float kq = 0.f;
     if (rsub == 0) {
       const float gs = g * sc;
+      const float gf = zg ? 1.f : g;
       put_afr<DK, DV, N>(sm, rho, gs * kk, gs * qq);
-      sm.kappa[0][rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(g);   // pivots update S' directly
+      sm.kappa[0][rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(gf);   // pivots update S' directly
       sm.kappa[1][rho] = 0.f;
-      sm.gg[rho] = g;
+      sm.gg[rho] = gf;
+      sm.rowh[rho] = zg ? 1.f : 0.f;                 // (free until the refit) rows to clear
       kq = kk * qq;
     }
     kq = wave_sum(kq);
     const bool ne1 = __ballot(ar != 1.f) != 0;
-    if (l == 0) sm.kqn[w] = f32x2{kq, ne1 ? 1.f : 0.f};
+    const bool zgw = __ballot(zg) != 0;
+    if (l == 0) sm.kqn[w] = f32x2{kq, (ne1 ? 1.f : 0.f) + (zgw ? 256.f : 0.f)};
     lds_barrier();
     float kqs = 0.f, nes = 0.f;
 #pragma unroll
@@ -402,6 +430,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
       if (Gq == 0) A.o[x * DV + j] = __builtin_fmaf(delta[c], kqs, wq);
     }
     if (bb == 0.f && allone) return;      // identity update: keep the encoding
+    if (nes >= 256.f) clear_rows<DK, DV, N>(sm, P);   // some gate is zero (rare)
     opaque(P);
     // ---- Y = C + kappa delta^T, C = c Q (pivot tile: C = g H, kappa = k) ----
     // One rank-one term per MFMA: lane quad G = 0 carries kappa and delta,
@@ -1091,6 +1120,7 @@ struct RSmemS {
   float gg[DK] __attribute__((aligned(16)));      // g = gate * row scale
   float rowh[DK] __attribute__((aligned(16)));    // new X factor (1 on pivot rows)
   float rq[DK] __attribute__((aligned(16)));      // 1 / QMAX of the row's width (0 on pivot rows)
+  float zf[DK] __attribute__((aligned(16)));      // 1 on rows whose gate is zero
   float kqp[GeoR<DK, DV>::NW];
   int notone[GeoR<DK, DV>::NW];
   int esum[GeoR<DK, DV>::NW];
@@ -1209,19 +1239,25 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     const int off = 16 * (tid + i * G::NT);
     if (off < CB) *(u32x4*)(stage + off) = chunk[i];
   }
+  // A zero (or subnormal) gate drops a row's old state, S'_i = k_i delta: the row
+  // is carried with factor gf = 1 and its codes are cleared before the update.
+  const float g = ai * sgr;
+  const bool zg = rsub == 0 && !(g >= 0x1p-126f);
+  const float gf = zg ? 1.f : g;
   float kq = 0.f;
   if (rsub == 0) {
-    const float g = ai * sgr;
     const int sl = rslot<DK, DV>(rho);
     rs.alpha[sl] = g * kk;
     rs.beta[sl] = g * qq;
-    rs.kappa[sl] = kk * __builtin_amdgcn_rcpf(g);
-    rs.gg[sl] = g;
+    rs.kappa[sl] = kk * __builtin_amdgcn_rcpf(gf);
+    rs.gg[sl] = gf;
+    rs.zf[sl] = zg ? 1.f : 0.f;
     kq = kk * qq;
   }
   kq = wave_sum(kq);
   const bool ne1 = __ballot(ai != 1.f) != 0;
-  if (l == 0) { rs.kqp[w] = kq; rs.notone[w] = ne1; }
+  const bool zgw = __ballot(zg) != 0;
+  if (l == 0) { rs.kqp[w] = kq; rs.notone[w] = (ne1 ? 1 : 0) | (zgw ? 2 : 0); }
   float cc[4] = {bf16f(cw[0] & 0xFFFFu), bf16f(cw[0] >> 16), bf16f(cw[1] & 0xFFFFu), bf16f(cw[1] >> 16)};
   lds_barrier();
 
@@ -1286,10 +1322,11 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     *(f32x4*)&rs.red[w][1][j0] = f32x4{wsum[0], wsum[1], wsum[2], wsum[3]};
   }
   lds_barrier();
-  int allone = 1;
+  int flags = 0;
   float kqs = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < G::NW; ww++) { allone &= !rs.notone[ww]; kqs += rs.kqp[ww]; }
+  for (int ww = 0; ww < G::NW; ww++) { flags |= rs.notone[ww]; kqs += rs.kqp[ww]; }
+  const bool allone = !(flags & 1);
   f32x4 u4 = *(const f32x4*)&rs.red[0][0][j0], w4 = *(const f32x4*)&rs.red[0][1][j0];
 #pragma unroll
   for (int ww = 1; ww < G::NW; ww++) {
@@ -1305,6 +1342,11 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   }
   if (w == 0 && rsl == 0) *(f32x4*)(A.o + x * DV + j0) = ov;
   if (bb == 0.f && allone) return;      // identity update: keep the encoding
+  if (flags & 2) {                       // some gate is zero (rare): clear those rows' codes
+#pragma unroll
+    for (int r = 0; r < G::NR; r++)
+      if (rs.zf[vb + r] != 0.f) P[2 * r] = P[2 * r + 1] = f16x2{(f16)0.f, (f16)0.f};
+  }
 
   // ---- rank-one update, Y = S' / g; row partial maxima of the non-pivot rows ----
   float Y[64];
@@ -1334,8 +1376,7 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     }
     if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
     const int sl = rslot<DK, DV>(rho);
-    const float g = ai * sgr;
-    const float pw = (g * __uint_as_float(mxb)) * A.weights[(size_t)h * DK + irow];
+    const float pw = (gf * __uint_as_float(mxb)) * A.weights[(size_t)h * DK + irow];
     uint32_t s = 0x3F80u;
     int epk = 0;
     if (pn != 16 && pw > 0.f) {
@@ -1344,7 +1385,7 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     }
     if (rsub != 0) epk = 0;
     if (rsub == 0) {
-      rs.rowh[sl] = pn == 16 ? 1.f : g * rcp_bf16(bf16f(s));
+      rs.rowh[sl] = pn == 16 ? 1.f : gf * rcp_bf16(bf16f(s));
       rs.rq[sl] = pn == 4 ? 1.0f / 7.0f : pn == 6 ? 1.0f / 31.0f : pn == 8 ? 1.0f / 127.0f : 0.f;
     }
     epk = wave_sum_i(epk);
@@ -1461,10 +1502,11 @@ struct WRSmem {
   float red[GeoW<DK>::NW][2][128] __attribute__((aligned(16)));   // per wave: column partials
   f32x2 ab[DK] __attribute__((aligned(16)));      // by record row: (g k, g q); 0 on pivot rows
   f32x2 abp[DK] __attribute__((aligned(16)));     // (g k, g q) of the pivot rows
-  float kappa[DK] __attribute__((aligned(16)));   // k / g
-  float gg[DK] __attribute__((aligned(16)));      // g = gate * row scale
+  float kappa[DK] __attribute__((aligned(16)));   // k / g (k on pivot rows)
+  float gg[DK] __attribute__((aligned(16)));      // g = gate * row scale (1 on zero-gate rows)
   float rowh[DK] __attribute__((aligned(16)));    // new X factor
   float rq[DK] __attribute__((aligned(16)));      // 1 / QMAX of the row's width
+  float zf[DK] __attribute__((aligned(16)));      // 1 on quantized rows whose gate is zero
   float kqp[GeoW<DK>::NW];
   int notone[GeoW<DK>::NW];
   int esum[GeoW<DK>::NW];
@@ -1522,18 +1564,25 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
     const int off = 16 * (tid + i * G::NT);
     if (off < CB) *(u32x4*)(stage + off) = chunk[i];
   }
+  // A zero (or subnormal) gate drops a quantized row's old state, S'_i = k_i delta:
+  // the row is carried with factor gf = 1 and its codes are cleared before the
+  // update.  Pivot rows update as S' = g v + k delta (kappa = k, no division).
+  const float g = ai * sgr;
+  const bool zg = rsub == 0 && pn != 16 && !(g >= 0x1p-126f);
+  const float gf = zg ? 1.f : g;
   float kq = 0.f;
   if (rsub == 0) {
-    const float g = ai * sgr;
     rs.ab[rho] = pn == 16 ? f32x2{0.f, 0.f} : f32x2{g * kk, g * qq};
     rs.abp[rho] = f32x2{g * kk, g * qq};
-    rs.kappa[rho] = kk * __builtin_amdgcn_rcpf(g);
-    rs.gg[rho] = g;
+    rs.kappa[rho] = pn == 16 ? kk : kk * __builtin_amdgcn_rcpf(gf);
+    rs.gg[rho] = gf;
+    rs.zf[rho] = zg ? 1.f : 0.f;
     kq = kk * qq;
   }
   kq = wave_sum(kq);
   const bool ne1 = __ballot(ai != 1.f) != 0;
-  if (l == 0) { rs.kqp[w] = kq; rs.notone[w] = ne1; }
+  const bool zgw = __ballot(zg) != 0;
+  if (l == 0) { rs.kqp[w] = kq; rs.notone[w] = (ne1 ? 1 : 0) | (zgw ? 2 : 0); }
   const float cc0 = bf16f(cw & 0xFFFFu), cc1 = bf16f(cw >> 16);
   lds_barrier();
 
@@ -1584,10 +1633,11 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   *(f32x2*)&rs.red[w][0][2 * l] = f32x2{__builtin_fmaf(cc0, U0, Up0), __builtin_fmaf(cc1, U1, Up1)};
   *(f32x2*)&rs.red[w][1][2 * l] = f32x2{__builtin_fmaf(cc0, W0, Wp0), __builtin_fmaf(cc1, W1, Wp1)};
   lds_barrier();
-  int allone = 1;
+  int flags = 0;
   float kqs = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < G::NW; ww++) { allone &= !rs.notone[ww]; kqs += rs.kqp[ww]; }
+  for (int ww = 0; ww < G::NW; ww++) { flags |= rs.notone[ww]; kqs += rs.kqp[ww]; }
+  const bool allone = !(flags & 1);
   f32x2 u2 = *(const f32x2*)&rs.red[0][0][2 * l], w2 = *(const f32x2*)&rs.red[0][1][2 * l];
 #pragma unroll
   for (int ww = 1; ww < G::NW; ww++) {
@@ -1597,6 +1647,11 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   const float d0 = bb * (vv[0] - u2[0]), d1 = bb * (vv[1] - u2[1]);
   if (w == 0) *(f32x2*)(A.o + x * DV + 2 * l) = f32x2{__builtin_fmaf(d0, kqs, w2[0]), __builtin_fmaf(d1, kqs, w2[1])};
   if (bb == 0.f && allone) return;      // identity update: keep the encoding
+  if (flags & 2) {                       // some gate is zero (rare): clear those rows' codes
+#pragma unroll
+    for (int r = 0; r < G::NR; r++)
+      if (rs.zf[ws0 + r] != 0.f) P[r] = f16x2{(f16)0.f, (f16)0.f};
+  }
 
   // ---- rank-one update, Y = S' / g; row partial maxima over lane pairs ----
   float Y[2 * G::NR];
@@ -1621,8 +1676,8 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
                                                                    __builtin_elementwise_max(m4[2], m4[3])));
   }
   mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
-  const float g = ai * sgr;
-  const float pw = (g * __uint_as_float(mxb)) * A.weights[(size_t)h * DK + irow];
+  const float gr = (pn != 16 && !(ai * sgr >= 0x1p-126f)) ? 1.f : ai * sgr;   // the row's factor gf, again
+  const float pw = (gr * __uint_as_float(mxb)) * A.weights[(size_t)h * DK + irow];
   uint32_t s = 0x3F80u;
   int epk = 0;
   if (pn != 16 && pw > 0.f) {
@@ -1631,7 +1686,7 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   }
   if (rsub != 0) epk = 0;
   if (rsub == 0) {
-    rs.rowh[rho] = g * rcp_bf16(bf16f(s));
+    rs.rowh[rho] = gr * rcp_bf16(bf16f(s));
     rs.rq[rho] = pn == 4 ? 1.0f / 7.0f : pn == 6 ? 1.0f / 31.0f : pn == 8 ? 1.0f / 127.0f : 0.f;
   }
   epk = wave_sum_i(epk);
@@ -1706,13 +1761,13 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
       *(uint16_t*)(stage + (p < k8 ? 128 * p + o8 : sink) + 2 * l) = (uint16_t)(y0 | (y1 << 8));
     }
   }
-  for (int r = rN; r < G::NR; r++) {               // binary16 pivot rows: S' = g (v + kappa delta)
+  for (int r = rN; r < G::NR; r++) {               // binary16 pivot rows: S' = g v + k delta
     const int p = ws0 + r;
     const int off = 256 * p + o16 + 4 * l;
     const f16x2 v2 = as_h2(*(const uint32_t*)(tile + off));   // the tile's bytes are unchanged until the store
     const float kr = rs.kappa[p], gr = rs.gg[p];
-    const float s0 = __builtin_fminf(__builtin_fmaxf(gr * __builtin_fmaf((float)v2[0], 1.f, kr * d0), -65504.f), 65504.f);
-    const float s1 = __builtin_fminf(__builtin_fmaxf(gr * __builtin_fmaf((float)v2[1], 1.f, kr * d1), -65504.f), 65504.f);
+    const float s0 = __builtin_fminf(__builtin_fmaxf(__builtin_fmaf((float)v2[0], gr, kr * d0), -65504.f), 65504.f);
+    const float s1 = __builtin_fminf(__builtin_fmaxf(__builtin_fmaf((float)v2[1], gr, kr * d1), -65504.f), 65504.f);
     *(uint32_t*)(stage + off) = h2_bits(f16x2{(f16)s0, (f16)s1});
   }
   lds_barrier();

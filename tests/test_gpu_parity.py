@@ -267,6 +267,62 @@ def test_kda_gate_per_head_widths(torch_cuda, orc, dk, dv):
     np.testing.assert_array_equal(P.image(), before)
 
 
+@pytest.mark.parametrize("dk,dv,gate,unit", [(128, 128, 0, 0), (128, 128, 1, 0), (128, 128, 1, 1), (128, 64, 1, 1)])
+def test_zero_gate(torch_cuda, orc, dk, dv, gate, unit):
+    """A gate of zero (a full forget) on quantized and binary16 pivot units:
+    S' = k delta^T there.  GDN: whole heads at a = 0, one of them with b = 0 too
+    (the state becomes zero: codes 0, scales 1); KDA: zero channels in every
+    width.  Two teacher-forced steps against the oracle."""
+    from types import SimpleNamespace
+    say("case zero gate", dk, dv, "KDA" if gate else "GDN", "rows" if unit else "heads")
+    rng = np.random.default_rng(500 + 10 * gate + unit + dv)
+    H, B = 8, 5
+    cfg = SimpleNamespace(gate=gate, unit=unit, window=0)
+    if unit:
+        bits = _row_width_patterns(dk, rng)
+    else:
+        bits = np.array([4, 6, 8, 16, 6, 4, 8, 6], np.int32)
+    wl = SimpleNamespace(B=B, H=H, dk=dk, dv=dv, cfg=cfg, bits=bits,
+                         row_weight=np.clip(np.exp(rng.normal(0, 1.15, (H, dk))), 0.1, 10).astype(np.float32))
+    P = Pair(orc, wl, n_slots=B)
+    slots = np.arange(B)
+    prof = np.exp(rng.normal(0, 1.5, (1, H, dk, 1))) * np.exp(rng.normal(0, 1.5, (1, H, 1, dv)))
+    P.store(slots, (0.1 * rng.standard_normal((B, H, dk, dv)) * prof).astype(np.float32))
+    f = lambda x: x.astype(np.float32)
+    worst = dict(mism=0, codes=0, maxd=0, scale_mism=0, scales=0, piv_bad=0, piv=0, piv_mism=0, o=0.0)
+    for t in range(2):
+        img = P.image()
+        ref = orc.OraclePool(B, H, dk, dv, np.asarray(bits).reshape(-1), wl.row_weight, gate, unit, 0, image=img)
+        q = rng.standard_normal((B, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k = rng.standard_normal((B, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((B, H, dv))
+        b = rng.uniform(0.05, 0.95, (B, H))
+        if gate:
+            a = 2.0 ** (-1.0 / (10.0 ** rng.uniform(0, 4, (B, H, dk))))
+            a[rng.uniform(size=a.shape) < 0.1] = 0.0
+        else:
+            a = rng.uniform(0.9, 1.0, (B, H))
+            a[:, [1, 3, 6]] = 0.0                       # a 6-bit, the pivot and an 8-bit head
+            b[0, 1] = 0.0                               # a = b = 0: the state becomes zero
+        o = P.gpu_step(slots, f(q), f(k), f(v), f(a), f(b))
+        o_ref = ref.step(slots, f(q), f(k), f(v), f(a), f(b))
+        post = P.image()
+        assert np.isfinite(o).all()
+        r = compare_codes(orc, ref, post, ref.img, slots)
+        for key in ("mism", "codes", "scale_mism", "scales", "piv_bad", "piv", "piv_mism"):
+            worst[key] += r[key]
+        worst["maxd"] = max(worst["maxd"], r["maxd"])
+        worst["o"] = max(worst["o"], readout_ok(o, o_ref))
+        if not gate:                                    # the reset head: every code 0, every scale 1
+            Qg, sg, cg, _ = ref.decode_tile(0, 1, post)
+            assert not np.any(Qg) and np.all(sg == 0x3F80) and np.all(cg == 0x3F80)   # bf16 1.0
+    say("  zero gate: code mismatch %d of %d (max |dQ| %d), scale mismatch %d of %d, pivot mismatch %d of %d, "
+        "readout %.3f" % (worst["mism"], worst["codes"], worst["maxd"], worst["scale_mism"], worst["scales"],
+                          worst["piv_mism"], worst["piv"], worst["o"]))
+    _assert_codes(worst)
+    assert worst["o"] <= 1.0
+
+
 def test_empty_and_out_of_range(torch_cuda, orc):
     say("case edges")
     torch = torch_cuda
