@@ -126,7 +126,8 @@
  *   S' = S^ is already represented exactly and the tile bytes are left
  *   unchanged instead of being refitted.  The fused kernel computes S' in binary32;
  *   its codes agree with R applied to the exactly rounded S' except for rare
- *   one-step rounding flips.
+ *   one-step rounding flips.  Gates lie in [0, 1]; a gate of 0 (or below the
+ *   binary32 normal range) forgets the unit's old state: S'_i = k_i delta.
  *
  * WINDOW MODE (window = W > 0, GDN gate; [P3] per-window quantization and
  * residual smoothing): the quantized base S0 is frozen inside a window.  Per
@@ -137,7 +138,10 @@
  * which is exactly the per-token recurrence started from S0.  After token
  * W's readout (or on stq_window_flush) the window is folded:
  *   S_W = G_W S0 + sum_s (G_W/G_s) k_s u_s^T  ->  R  -> new base, cache cleared.
- * (Use row_weight = 1 for the pages' plain per-row smoothing.)
+ * (Use row_weight = 1 for the pages' plain per-row smoothing.)  The ratios
+ * G_t/G_s need every G of a window to be a normal binary32 number: gates in
+ * (0, 1] whose product over W tokens stays >= 2^-126.  Smaller products are
+ * outside the contract of window mode (the per-token mode accepts any gate).
  *
  * ------------------------------------------------------------------------
  * POOL BUFFER (one caller-owned device buffer of stq_pool_bytes() bytes):
