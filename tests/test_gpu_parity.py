@@ -323,6 +323,56 @@ def test_zero_gate(torch_cuda, orc, dk, dv, gate, unit):
     assert worst["o"] <= 1.0
 
 
+@pytest.mark.parametrize("unit", [0, 1])
+def test_max_heads(torch_cuda, orc, unit):
+    """The largest head count the descriptor accepts (4,096 heads, d = 64):
+    header tables, tile offsets and the grid at their limit.  One step with the
+    KDA gate, checked against the oracle on a sample of heads."""
+    from types import SimpleNamespace
+    say("case max heads", "rows" if unit else "heads")
+    rng = np.random.default_rng(700 + unit)
+    H, B, dk, dv = 4096, 2, 64, 64
+    cfg = SimpleNamespace(gate=1, unit=unit, window=0)
+    bits = rng.choice([4, 6, 8, 16], (H, dk) if unit else H, p=[0.3, 0.5, 0.18, 0.02]).astype(np.int32)
+    wl = SimpleNamespace(B=B, H=H, dk=dk, dv=dv, cfg=cfg, bits=bits,
+                         row_weight=np.clip(np.exp(rng.normal(0, 1.15, (H, dk))), 0.1, 10).astype(np.float32))
+    P = Pair(orc, wl, n_slots=B)
+    slots = np.arange(B)
+    P.store(slots, (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32))
+    np.testing.assert_array_equal(P.image(), P.ref.img)
+    f = lambda x: x.astype(np.float32)
+    q = rng.standard_normal((B, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((B, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, dv))
+    a = rng.uniform(0.5, 1.0, (B, H, dk))
+    b = rng.uniform(0.05, 0.95, (B, H))
+    img = P.image()
+    o = P.gpu_step(slots, f(q), f(k), f(v), f(a), f(b))
+    ref = orc.OraclePool(B, H, dk, dv, np.asarray(bits).reshape(-1), wl.row_weight, 1, unit, 0, image=img)
+    o_ref = ref.step(slots, f(q), f(k), f(v), f(a), f(b))
+    heads = sorted(set(rng.choice(H, 64, replace=False).tolist()) | {0, H - 1})
+    r = compare_codes(orc, ref, P.image(), ref.img, slots, heads=heads)
+    say("  max heads: code mismatch %d of %d (max |dQ| %d), pivot mismatch %d of %d, readout %.3f"
+        % (r["mism"], r["codes"], r["maxd"], r["piv_mism"], r["piv"], readout_ok(o, o_ref)))
+    _assert_codes(r)
+    assert readout_ok(o, o_ref) <= 1.0
+
+
+def test_step_from_fresh_pool(torch_cuda, orc):
+    """A step straight after pool creation (every state zero: codes 0, scales
+    1), GDN head mix, two teacher-forced steps."""
+    say("case fresh pool")
+    wl = Workload("C2", B=8)
+    P = Pair(orc, wl)
+    slots = np.arange(8)
+    np.testing.assert_array_equal(P.image(), P.ref.img)
+    r = _teacher_forced(orc, wl, P, slots, 2)
+    say("  fresh pool: code mismatch %d of %d (max |dQ| %d), pivot mismatch %d of %d, readout %.3f"
+        % (r["mism"], r["codes"], r["maxd"], r["piv_mism"], r["piv"], r["o"]))
+    _assert_codes(r)
+    assert r["o"] <= 1.0
+
+
 def test_empty_and_out_of_range(torch_cuda, orc):
     say("case edges")
     torch = torch_cuda
