@@ -1655,6 +1655,7 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
 
   // ---- rank-one update, Y = S' / g; row partial maxima over lane pairs ----
   float Y[2 * G::NR];
+  opaque(P);                             // each use converts inside its own v_fma_mix_f32
   float* partl = part + ws0 * G::PSTR + (l >> 1);
 #pragma unroll
   for (int r = 0; r < G::NR; r++) {
