@@ -1615,9 +1615,10 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
       U1 = __builtin_fmaf(q1, abr[0], U1);
       W0 = __builtin_fmaf(q0, abr[1], W0);
       W1 = __builtin_fmaf(q1, abr[1], W1);
-      // one step at a time (the next loads wait for this step's sums): other
-      // resident waves cover the LDS latency, and registers stay few
-      asm volatile("" : "+v"(sbase) : "v"(U0), "v"(U1), "v"(W0), "v"(W1));
+      // four steps at a time (the next four steps' loads wait for these sums):
+      // enough LDS reads in flight, and the scheduler cannot hoist all 32
+      // steps' loads (which spills)
+      if ((r & 3) == 3) asm volatile("" : "+v"(sbase) : "v"(U0), "v"(U1), "v"(W0), "v"(W1));
     }
   }
   float Up0 = 0.f, Up1 = 0.f, Wp0 = 0.f, Wp1 = 0.f;
