@@ -110,7 +110,8 @@ BENCH = {
            "workload": "KDA pool B=256 H=32 d_k=d_v=128, per-channel gate, key rows "
                        "{4b:30%, 6b:50%, 8b:19%, fp16:1%}",
            "dtype": "f32 update, per-key-row 4/6/8-bit + f16 state"},
-    "C5": {"layers": 2, "kernel": "k_window<128, 128, false>", "prof": "k_window_step",
+    "C5": {"layers": 2, "kernel": "k_window_read<128, 128> + k_window_fold<128, 128, true>",
+           "regex": "k_window_(read<128, 128>|fold<128, 128, true>)", "prof": "k_window_step",
            "metric": "request-head decode steps/s (B=512, H=32, d=128, 4-bit GDN, window W=16)",
            "workload": "windowed GDN pool B=512 H=32 d_k=d_v=128, all heads 4-bit, W=16 "
                        "(binary32 window caches, one fold per 16 tokens)",
