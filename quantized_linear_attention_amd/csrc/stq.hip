@@ -590,7 +590,8 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
     if (s >= t) continue;
     float ak = 0.f, aq = 0.f;
 #pragma unroll
-    for (int i = 4 * (tid % 8); i < DK; i += 32) {
+    for (int ii = 0; ii < DK / 32; ii++) {
+      const int i = 4 * (tid % 8) + 32 * ii;
       const f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i);
       const f32x4 kv = *(const f32x4*)(A.k + x * DK + i);
       const f32x4 qv = *(const f32x4*)(A.q + x * DK + i);
