@@ -161,10 +161,11 @@ __device__ __forceinline__ void fp16_scale(float m, float& sc, float& inv) {
 }
 
 // matvec A fragments of row i: fp16 hi/lo of the scaled (g k, g q)
-template <int DK, int DV, int N, class S>
+template <int DK, int DV, int N, class S, bool X16 = false>
 __device__ __forceinline__ void put_afr(S& sm, int i, float al, float be) {
   const int rc = i >> 5, G = (i >> 2) & 3, t = 4 * ((i >> 4) & 1) + (i & 3);
   const int k = t_to_kk<N>(t);
+  if (X16 && x16<N>(i & 3)) { al *= 0.0625f; be *= 0.0625f; }   // this row's codes unpack as 16 Q
   const f16 ah = (f16)al, bh = (f16)be;
   sm.afr[rc][G][0][k] = ah;
   sm.afr[rc][G][1][k] = (f16)(al - (float)ah);
@@ -400,7 +401,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     if (rsub == 0) {
       const float gs = g * sc;
       const float gf = zg ? 1.f : g;
-      put_afr<DK, DV, N>(sm, rho, gs * kk, gs * qq);
+      put_afr<DK, DV, N, SmemM<DK, DV>, true>(sm, rho, gs * kk, gs * qq);
       sm.kappa[0][rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(gf);   // pivots update S' directly
       sm.kappa[1][rho] = 0.f;
       sm.gg[rho] = gf;
@@ -417,7 +418,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     for (int ww = 0; ww < G::NW; ww++) { const f32x2 t = sm.kqn[ww]; kqs += t[0]; nes += t[1]; }
     const bool allone = nes == 0.f;
     // ---- u = A^T k, w = A^T q on the matrix cores; readout ----
-    unpack<N>(raw, P);
+    unpack_x16<N>(raw, P);
     f32x4 D[G::NCC];
     matvec<DK, DV>(sm, P, D);
     float delta[G::NCC];
@@ -436,9 +437,9 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     // One rank-one term per MFMA: lane quad G = 0 carries kappa and delta,
     // the other quads zeros (their kappa row in LDS is zero).
     const float* kap = sm.kappa[Gq == 0 ? 0 : 1];
-    float db[G::NCC];
+    float db[G::NCC], c16[G::NCC];
 #pragma unroll
-    for (int c = 0; c < G::NCC; c++) db[c] = Gq == 0 ? delta[c] : 0.f;
+    for (int c = 0; c < G::NCC; c++) { db[c] = Gq == 0 ? delta[c] : 0.f; c16[c] = cc[c] * 0.0625f; }
 #pragma unroll
     for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
@@ -452,7 +453,8 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
           // fma with a +0 addend: one v_fma_mix_f32 per code, straight from fp16
           f32x4 C;
 #pragma unroll
-          for (int i = 0; i < 4; i++) C[i] = __builtin_fmaf(code_e<N>(P, e0 + i), PIV ? gr4[i] : cc[c], 0.0f);
+          for (int i = 0; i < 4; i++)
+            C[i] = __builtin_fmaf(code_e<N>(P, e0 + i), PIV ? gr4[i] : (x16<N>(i) ? c16[c] : cc[c]), 0.0f);
           C = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, db[c], C, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; i++) Y[e0 + i] = C[i];

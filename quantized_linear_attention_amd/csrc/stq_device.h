@@ -210,6 +210,50 @@ __device__ __forceinline__ void unpack(const uint32_t* raw, f16x2* P) {
   }
 }
 
+// Unpack for the decode step: stream codes of column c with x16<N>(c) come out
+// as 16 Q (a field shifted by four bits is still an exact binary16 integer),
+// which saves a shift per pair; the step divides the matvec operand of those
+// rows by 16 and multiplies their column scale by 1/16.
+template <int N> __device__ __forceinline__ constexpr bool x16(int c) {
+  return N == 4 ? (c & 1) != 0 : (N == 6 ? c >= 2 : false);
+}
+template <int N>
+__device__ __forceinline__ void unpack_x16(const uint32_t* raw, f16x2* P) {
+  if constexpr (N == 4) {
+    const f16x2 off = {(f16)-1032.0f, (f16)-1032.0f}, offx = {(f16)-1152.0f, (f16)-1152.0f};
+    const uint32_t k64 = vconst(0x64006400u);
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+      const uint32_t d = raw[m], d8 = d >> 8;
+      P[4 * m] = as_h2((d & 0x000F000Fu) | k64) + off;
+      P[4 * m + 1] = as_h2((d & 0x00F000F0u) | k64) + offx;
+      P[4 * m + 2] = as_h2((d8 & 0x000F000Fu) | k64) + off;
+      P[4 * m + 3] = as_h2((d8 & 0x00F000F0u) | k64) + offx;
+    }
+  } else if constexpr (N == 6) {
+    // high halves hold the codes of columns 2, 3 at bits 4..9: 1024 + 16 field
+    const f16x2 off = {(f16)-1056.0f, (f16)-1536.0f};
+    const uint32_t k64 = vconst(0x64006400u);
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      uint32_t d0 = raw[3 * u], d1 = raw[3 * u + 1], d2 = raw[3 * u + 2];
+      uint32_t x[4];
+      x[0] = __builtin_amdgcn_perm(d0, d0, 0x02010100u);
+      x[1] = __builtin_amdgcn_perm(d1, d0, 0x05040403u);
+      x[2] = __builtin_amdgcn_perm(d2, d1, 0x04030302u);
+      x[3] = __builtin_amdgcn_perm(d2, d2, 0x03020201u);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int r = 4 * u + q;
+        P[2 * r] = as_h2((x[q] & 0x03F0003Fu) | k64) + off;
+        P[2 * r + 1] = as_h2(((x[q] >> 6) & 0x03F0003Fu) | k64) + off;
+      }
+    }
+  } else {
+    unpack<N>(raw, P);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ float code_at(const f16x2* P, int r, int c) {
   return (float)P[preg<N>(r, c)][phalf<N>(r, c)];
@@ -219,6 +263,14 @@ __device__ __forceinline__ float code_at(const f16x2* P, int r, int c) {
 __device__ __forceinline__ void opaque(f16x2* P) {
 #pragma unroll
   for (int k = 0; k < 32; k++) asm volatile("" : "+v"(P[k]));
+}
+
+// (a << s) | b as one v_lshl_or_b32 (a chain of them instead of shifts and
+// three-input ors)
+__device__ __forceinline__ uint32_t lshl_or(uint32_t a, int s, uint32_t b) {
+  uint32_t r = (a << s) | b;
+  asm volatile("" : "+v"(r));
+  return r;
 }
 
 // y[4r+c]: binary32 bit patterns 2^23 + field (field in the low bits, nothing
@@ -235,8 +287,8 @@ __device__ __forceinline__ void pack(const uint32_t* y, uint32_t* raw) {
   } else if constexpr (N == 4) {
 #pragma unroll
     for (int m = 0; m < 8; m++) {
-      uint32_t h0 = y[8 * m] | (y[8 * m + 1] << 4) | (y[8 * m + 2] << 8) | (y[8 * m + 3] << 12);
-      uint32_t h1 = y[8 * m + 4] | (y[8 * m + 5] << 4) | (y[8 * m + 6] << 8) | (y[8 * m + 7] << 12);
+      uint32_t h0 = lshl_or(y[8 * m + 3], 12, lshl_or(y[8 * m + 2], 8, lshl_or(y[8 * m + 1], 4, y[8 * m])));
+      uint32_t h1 = lshl_or(y[8 * m + 7], 12, lshl_or(y[8 * m + 6], 8, lshl_or(y[8 * m + 5], 4, y[8 * m + 4])));
       raw[m] = __builtin_amdgcn_perm(h1, h0, 0x05040100u);
     }
   } else if constexpr (N == 6) {
@@ -246,7 +298,7 @@ __device__ __forceinline__ void pack(const uint32_t* y, uint32_t* raw) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const uint32_t* yy = y + 4 * (4 * u + q);
-        g[q] = yy[0] | (yy[1] << 6) | (yy[2] << 12) | (yy[3] << 18);
+        g[q] = lshl_or(yy[3], 18, lshl_or(yy[2], 12, lshl_or(yy[1], 6, yy[0])));
       }
       raw[3 * u] = __builtin_amdgcn_perm(g[1], g[0], 0x04020100u);
       raw[3 * u + 1] = __builtin_amdgcn_perm(g[2], g[1], 0x05040201u);
