@@ -206,7 +206,10 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 // sm.gg, visible after the next barrier); for a binary16 pivot tile Y holds
 // S' itself.  Writes codes, row and column scales.
 // ------------------------------------------------------------------------
-template <int DK, int DV, int N, bool EXACT, bool OPQ = false>
+// SPLIT: the row stage runs on the second half of the waves, one lane per row
+// (row tid mod d_k, whose weight wgt is); otherwise on every wave, TPR lanes
+// per row (row tid / TPR).
+template <int DK, int DV, int N, bool EXACT, bool OPQ = false, bool SPLIT = false>
 __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t* tile, float wgt) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
@@ -227,7 +230,10 @@ __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t
         raw[2 * q + h2] = h2_bits(f16x2{(f16)s0, (f16)s1});
       }
   } else {
-    const int rho = tid / G::TPR, rsub = tid % G::TPR;      // row stage: row rho
+    const int rho = SPLIT ? (tid & (DK - 1)) : tid / G::TPR;     // row stage: row rho
+    const int rsub = SPLIT ? 0 : tid % G::TPR;
+    constexpr int W0 = SPLIT ? G::NW / 2 : 0;                     // first wave of the row stage
+    constexpr int PPT = SPLIT ? G::NP : G::NP / G::TPR;           // partials per row thread
     // ---- row refit: partial row absmax over the lane's columns -> LDS ----
 #pragma unroll
     for (int rc = 0; rc < G::NRC; rc++)
@@ -243,39 +249,41 @@ __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t
         }
       }
     lds_barrier();
-    // row stage: each of the TPR threads of row rho reduces a contiguous run
-    uint32_t mxb = 0u;                              // non-negative: compare bit patterns
-    const float* pr = &sm.part[rho * G::PSTR + rsub * (G::NP / G::TPR)];
-#pragma unroll
-    for (int p = 0; p < G::NP / G::TPR; p += 4) {
-      const u32x4 v4 = *(const u32x4*)(pr + p);
-      mxb = __builtin_elementwise_max(mxb, __builtin_elementwise_max(__builtin_elementwise_max(v4[0], v4[1]),
-                                                                     __builtin_elementwise_max(v4[2], v4[3])));
-    }
-    if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)dppi<0xB1>((int)mxb));
-    const float g = sm.gg[rho];
-    const float m = g * __uint_as_float(mxb);      // row absmax of S'
-    const float pw = m * wgt;                      // wgt: weight of row rho
     uint32_t s = 0x3F80u;
-    int epk = 0;                                   // exponent sum * 256 + row count
-    if (pw > 0.f) {
-      // ingest: correctly rounded sqrt (bit-exact refit); decode step: v_sqrt
-      // (1 ulp), which can move a row scale by one bf16 step in rare rows
-      s = bf16_rne(EXACT ? __builtin_sqrtf(pw) : __builtin_amdgcn_sqrtf(pw));
-      epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
+    if (w >= W0) {
+      // row stage: each of the TPR threads of row rho reduces a contiguous run
+      uint32_t mxb = 0u;                              // non-negative: compare bit patterns
+      const float* pr = &sm.part[rho * G::PSTR + rsub * PPT];
+#pragma unroll
+      for (int p = 0; p < PPT; p += 4) {
+        const u32x4 v4 = *(const u32x4*)(pr + p);
+        mxb = __builtin_elementwise_max(mxb, __builtin_elementwise_max(__builtin_elementwise_max(v4[0], v4[1]),
+                                                                       __builtin_elementwise_max(v4[2], v4[3])));
+      }
+      if (!SPLIT && G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)dppi<0xB1>((int)mxb));
+      const float g = sm.gg[rho];
+      const float m = g * __uint_as_float(mxb);      // row absmax of S'
+      const float pw = m * wgt;                      // wgt: weight of row rho
+      int epk = 0;                                   // exponent sum * 256 + row count
+      if (pw > 0.f) {
+        // ingest: correctly rounded sqrt (bit-exact refit); decode step: v_sqrt
+        // (1 ulp), which can move a row scale by one bf16 step in rare rows
+        s = bf16_rne(EXACT ? __builtin_sqrtf(pw) : __builtin_amdgcn_sqrtf(pw));
+        epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
+      }
+      if (rsub != 0) epk = 0;
+      if (rsub == 0) sm.rowh[rho] = g * rcp_bf16(bf16f(s));
+      epk = wave_sum_i(epk);
+      if (l == 0) sm.epk[w] = epk;
     }
-    if (rsub != 0) epk = 0;
-    if (rsub == 0) sm.rowh[rho] = g * rcp_bf16(bf16f(s));
-    epk = wave_sum_i(epk);
-    if (l == 0) sm.epk[w] = epk;
     lds_barrier();
     int et = 0;                                    // packed sums add up: count < 256
 #pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) et += sm.epk[ww];
+    for (int ww = W0; ww < G::NW; ww++) et += sm.epk[ww];
     et = __builtin_amdgcn_readfirstlane(et);
     const int es = et >> 8, ec = et & 0xFF;
     const int E = ec ? mean_exp(es, ec) : 0;
-    if (rsub == 0) scl[rho] = (uint16_t)bf16_adj(s, -E);
+    if (w >= W0 && rsub == 0) scl[rho] = (uint16_t)bf16_adj(s, -E);
     // ---- column refit: X = Y h, column absmax over the wave's 4 row quads ----
     float hr[8 * G::NRC];
 #pragma unroll
@@ -368,10 +376,22 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
       ss[q] = PIV ? 1.f : bf16f(scl[l + 64 * q]);
     }
     const float a_h = A.gate ? 1.f : A.a[x];
-    float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
-    float ar = A.gate ? A.a[x * DK + rho] : a_h;
-    float sr = PIV ? 1.f : bf16f(scl[rho]);
-    float wgt = A.weights[(size_t)h * DK + rho];
+    // SPLIT (two threads per row otherwise): row r has one lane, r = tid mod d_k;
+    // the first half of the waves computes the per-row factors, the second half
+    // runs the row stage of the refit
+    constexpr bool SPLIT = G::TPR == 2 && NS == 2;
+    const int rr = SPLIT ? (tid & (DK - 1)) : rho;
+    float kk = A.k[x * DK + rr], qq = A.q[x * DK + rr];
+    float ar, sr;
+    if constexpr (SPLIT) {
+      ar = (w & 1) ? sa[1] : sa[0];
+      sr = (w & 1) ? ss[1] : ss[0];
+      if (!A.gate) ar = a_h;
+    } else {
+      ar = A.gate ? A.a[x * DK + rho] : a_h;
+      sr = PIV ? 1.f : bf16f(scl[rho]);
+    }
+    float wgt = A.weights[(size_t)h * DK + rr];
     const float bb = A.b[x];
     float vv[G::NCC], cc[G::NCC];
 #pragma unroll
@@ -397,25 +417,28 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     // A zero (or subnormal) gate drops the row's old state, S'_i = k_i delta: the
     // row is carried with factor 1 and its codes are cleared before the update.
     const bool zg = !PIV && !(g >= 0x1p-126f);
-    float kq = 0.f;
-    if (rsub == 0) {
-      const float gs = g * sc;
-      const float gf = zg ? 1.f : g;
-      put_afr<DK, DV, N, SmemM<DK, DV>, true>(sm, rho, gs * kk, gs * qq);
-      sm.kappa[0][rho] = PIV ? kk : kk * __builtin_amdgcn_rcpf(gf);   // pivots update S' directly
-      sm.kappa[1][rho] = 0.f;
-      sm.gg[rho] = gf;
-      sm.rowh[rho] = zg ? 1.f : 0.f;                 // (free until the refit) rows to clear
-      kq = kk * qq;
+    constexpr int RW = SPLIT ? G::NW / 2 : G::NW;     // waves that hold the per-row factors
+    if (!SPLIT || w < RW) {
+      float kq = 0.f;
+      if (SPLIT || rsub == 0) {
+        const float gs = g * sc;
+        const float gf = zg ? 1.f : g;
+        put_afr<DK, DV, N, SmemM<DK, DV>, true>(sm, rr, gs * kk, gs * qq);
+        sm.kappa[0][rr] = PIV ? kk : kk * __builtin_amdgcn_rcpf(gf);   // pivots update S' directly
+        sm.kappa[1][rr] = 0.f;
+        sm.gg[rr] = gf;
+        sm.rowh[rr] = zg ? 1.f : 0.f;                 // (free until the refit) rows to clear
+        kq = kk * qq;
+      }
+      kq = wave_sum(kq);
+      const bool ne1 = __ballot(ar != 1.f) != 0;
+      const bool zgw = __ballot(zg) != 0;
+      if (l == 0) sm.kqn[w] = f32x2{kq, (ne1 ? 1.f : 0.f) + (zgw ? 256.f : 0.f)};
     }
-    kq = wave_sum(kq);
-    const bool ne1 = __ballot(ar != 1.f) != 0;
-    const bool zgw = __ballot(zg) != 0;
-    if (l == 0) sm.kqn[w] = f32x2{kq, (ne1 ? 1.f : 0.f) + (zgw ? 256.f : 0.f)};
     lds_barrier();
     float kqs = 0.f, nes = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) { const f32x2 t = sm.kqn[ww]; kqs += t[0]; nes += t[1]; }
+    for (int ww = 0; ww < RW; ww++) { const f32x2 t = sm.kqn[ww]; kqs += t[0]; nes += t[1]; }
     const bool allone = nes == 0.f;
     // ---- u = A^T k, w = A^T q on the matrix cores; readout ----
     unpack_x16<N>(raw, P);
@@ -460,7 +483,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
           for (int i = 0; i < 4; i++) Y[e0 + i] = C[i];
         }
       }
-    refit_store<DK, DV, N, false>(sm, Y, tile, wgt);
+    refit_store<DK, DV, N, false, false, SPLIT>(sm, Y, tile, wgt);
   } else {
     // ---- store: Y = the given fp32 tile, g = 1 ----
     const float* S = A.S_in ? A.S_in + x * DK * DV : nullptr;
