@@ -607,6 +607,14 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   }
   kq = wave_sum(kq);
   if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
+  // the lane quad's cached u entries (s = 4i + Gq): issued with the other reads
+  // that wait for t
+  float uq[UQ][G::NCC];
+#pragma unroll
+  for (int i = 0; i < UQ; i++)
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+      uq[i][c] = 4 * i + Gq < t ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
   // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per token
   // (a fixed number of passes, so that the loads issue with the tile's)
 #pragma unroll
@@ -635,13 +643,6 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
     }
   }
   __syncthreads();
-  // the lane quad's cached u entries (s = 4i + Gq), in flight during the matvec
-  float uq[UQ][G::NCC];
-#pragma unroll
-  for (int i = 0; i < UQ; i++)
-#pragma unroll
-    for (int c = 0; c < G::NCC; c++)
-      uq[i][c] = 4 * i + Gq < t ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
   unpack<N>(raw, P);
   // ---- readout and written vector from the frozen base and the cache ----
   float kqs = 0.f;
