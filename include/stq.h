@@ -241,7 +241,13 @@ stq_status stq_pool_fetch(const stq_pool* pool, const int32_t* slots_dev, int32_
                           float* S_dev, hipStream_t stream);
 
 /* One decode token for n requests and all heads (see DECODE STEP / WINDOW
- * MODE above): reads q, k, v, a, b, writes o and advances the states. */
+ * MODE above): reads q, k, v, a, b, writes o and advances the states.
+ * Range: every entry of q and k must have magnitude below 2 (queries and keys
+ * of the gated delta rule are L2-normalised, so |entry| <= 1).  Per-head
+ * units feed the matrix cores the products gate * row scale * (q or k) as
+ * binary16 pairs scaled so that the largest gate * row scale of the tile sits
+ * in [2^14, 2^15); larger entries overflow binary16 and the results of that
+ * tile are undefined.  Not checked (the vectors live on the device). */
 stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                            const float* q_dev, const float* k_dev, const float* v_dev,
                            const float* a_dev, const float* b_dev, float* o_dev,
