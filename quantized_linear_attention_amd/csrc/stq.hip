@@ -577,11 +577,8 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   float* Gc = (float*)(cache + 4);
   float* Kc = (float*)(cache + 256);
   float* Uc = Kc + (size_t)W * DK;
-  const int t = *cntp;                         // tokens already in the window
-  if (t >= W) return;                          // full: only the fold may touch it
-  const float a = A.a[x];
-  const float Gt = t ? Gc[t - 1] * a : a;      // binary32 running product
-  // the tile's global reads first
+  // every read that does not depend on the window count t, and t itself, in
+  // one round trip; then the reads that do
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
@@ -589,18 +586,32 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   float cc[G::NCC];
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) cc[c] = PIV ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
+  constexpr int NS = DK / 64;
+  float sgl[NS];
+#pragma unroll
+  for (int q = 0; q < NS; q++) sgl[q] = PIV ? 1.f : bf16f(scl[l + 64 * q]);
+  float sg = PIV ? 1.f : bf16f(scl[rho]);
+  float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
+  float a = A.a[x];
+  const int t = *cntp;                         // tokens already in the window
+  pin(a);
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) pin(cc[c]);
+#pragma unroll
+  for (int q = 0; q < NS; q++) pin(sgl[q]);
+  pin(sg); pin(kk); pin(qq);
+  if (t >= W) return;                          // full: only the fold may touch it
+  const float Gt = t ? Gc[t - 1] * a : a;      // binary32 running product
   float sc, inv;
   {
     float gl = 0.f;
 #pragma unroll
-    for (int i = l; i < DK; i += 64) gl = __builtin_fmaxf(gl, PIV ? 1.f : bf16f(scl[i]));
+    for (int q = 0; q < NS; q++) gl = __builtin_fmaxf(gl, sgl[q]);
     fp16_scale(wave_max_pos(gl), sc, inv);
   }
   // ---- per-row work (once per row) ----
   float kq = 0.f;
   if (rsub == 0) {
-    const float sg = PIV ? 1.f : bf16f(scl[rho]);
-    const float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
     put_afr<DK, DV, N>(sm, rho, (sg * sc) * kk, (sg * sc) * qq);
     kq = kk * qq;
     Kc[(size_t)t * DK + rho] = kk;                       // append k_t
