@@ -698,7 +698,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
 // window emptied.  Folds windows holding at least `need` tokens.
 template <int DK, int DV, int N>
 __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK, DV>& ws, uint8_t* tile,
-                                            uint8_t* cache, int h, int need) {
+                                            uint8_t* cache, int h, int ns) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
   constexpr bool PIV = (N == 16);
@@ -714,8 +714,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   float* Kc = (float*)(cache + 256);
   float* Uc = Kc + (size_t)W * DK;
   float* kap = WSmem<DK, DV>::IN_PART ? sm.part : ws.kap;
-  const int ns = *cntp;                        // tokens in the window
-  if (ns < need || ns == 0) return;
+  // ns: tokens in the window (read by the caller), 1 <= ns <= W
   const float Gt = Gc[ns - 1];
   uint32_t raw[2 * N];
   f16x2 P[32];
@@ -730,16 +729,35 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
 #pragma unroll
     for (int c = 0; c < G::NCC; c++)
       uq[i][c] = 4 * i + Gq < ns ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
-  if (rsub == 0) sm.gg[rho] = Gt * (PIV ? 1.f : bf16f(scl[rho]));
-  // kappa_s,i = k_s,i / (G_s sigma_i) for every token of the window, 4 rows per item
-  for (int j = tid; j < ns * (DK / 4); j += G::NT) {
-    const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
-    const f32x4 kv = *(const f32x4*)(Kc + (size_t)s * DK + r0);
-    const float gs = Gc[s];
-    f32x4 o4;
+  const uint32_t sgr = PIV ? 0x3F80u : scl[rho];
+  const float wgt = A.weights[(size_t)h * DK + rho];
+  // kappa_s,i = k_s,i / (G_s sigma_i) for every token of the window, 4 rows per
+  // item; a fixed number of passes whose reads all issue before any is used
+  constexpr int KP = (WMAX * DK / 4 + G::NT - 1) / G::NT;
+  f32x4 kv[KP];
+  float gs[KP];
+  u32x2 sg4[KP];
 #pragma unroll
-    for (int e = 0; e < 4; e++) o4[e] = kv[e] / (gs * (PIV ? 1.f : bf16f(scl[r0 + e])));
-    *(f32x4*)&kap[s * DK + r0] = o4;
+  for (int it = 0; it < KP; it++) {
+    const int j = tid + it * G::NT;
+    const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
+    const bool on = j < ns * (DK / 4);
+    kv[it] = on ? *(const f32x4*)(Kc + (size_t)s * DK + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    gs[it] = on ? Gc[s] : 1.f;
+    sg4[it] = on && !PIV ? *(const u32x2*)(scl + r0) : u32x2{0x3F803F80u, 0x3F803F80u};
+  }
+  if (rsub == 0) sm.gg[rho] = Gt * bf16f(sgr);
+#pragma unroll
+  for (int it = 0; it < KP; it++) {
+    const int j = tid + it * G::NT;
+    if (j < ns * (DK / 4)) {
+      const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
+      f32x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        o4[e] = kv[it][e] / (gs[it] * bf16f((sg4[it][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+      *(f32x4*)&kap[s * DK + r0] = o4;
+    }
   }
   __syncthreads();
   unpack<N>(raw, P);
@@ -775,7 +793,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
     }
   if (tid == 0) *cntp = 0;
   if constexpr (WSmem<DK, DV>::IN_PART) lds_barrier();     // kappa reads done before the partials
-  refit_store<DK, DV, N, false, true>(sm, Y, tile, A.weights[(size_t)h * DK + rho]);
+  refit_store<DK, DV, N, false, true>(sm, Y, tile, wgt);
 }
 
 // readout and append of every tile of the call
@@ -812,16 +830,16 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   const int t0 = STEP ? (int)blockIdx.x * FPW : tile_of_block(T);
   const int need = STEP ? A.W : 1;
   uint64_t mask;
+  int cnt = 0;                                   // lane i: window count of tile t0 + i
   {
-    bool due = false;
     const int i = threadIdx.x & 63, tau = t0 + i;
     if (i < (STEP ? FPW : 1) && tau < T) {
       const int ci = tau / A.H, h = tau - ci * A.H;
       const int slot = A.slots[ci];
       if ((unsigned)slot < (unsigned)A.n_slots)
-        due = *(const int32_t*)(A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride) >= need;
+        cnt = *(const int32_t*)(A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride);
     }
-    mask = __ballot(due);
+    mask = __ballot(cnt >= need && cnt > 0);
   }
   bool first = true;
   while (mask) {
@@ -832,13 +850,14 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     const int slot = A.slots[ci];
     uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
     uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
+    const int ns = __builtin_amdgcn_readlane(cnt, i);
     if (!first) __syncthreads();               // the previous fold's LDS reads are done
     first = false;
     switch (A.head_bits[h]) {
-      case 4: window_fold<DK, DV, 4>(A, sm, ws, tile, cache, h, need); break;
-      case 6: window_fold<DK, DV, 6>(A, sm, ws, tile, cache, h, need); break;
-      case 8: window_fold<DK, DV, 8>(A, sm, ws, tile, cache, h, need); break;
-      default: window_fold<DK, DV, 16>(A, sm, ws, tile, cache, h, need); break;
+      case 4: window_fold<DK, DV, 4>(A, sm, ws, tile, cache, h, ns); break;
+      case 6: window_fold<DK, DV, 6>(A, sm, ws, tile, cache, h, ns); break;
+      case 8: window_fold<DK, DV, 8>(A, sm, ws, tile, cache, h, ns); break;
+      default: window_fold<DK, DV, 16>(A, sm, ws, tile, cache, h, ns); break;
     }
   }
 }
