@@ -196,6 +196,34 @@ __device__ __forceinline__ void matvec(const S& sm, const f16x2* P, f32x4* D) {
     D[cc] = acc;
   }
 }
+// matvec straight from the packed lane stream: each column chunk unpacks its
+// own part just before its MFMAs, so only that part's pairs are live
+template <int DK, int DV, int N, class S>
+__device__ __forceinline__ void matvec_raw(const S& sm, uint32_t* raw, f32x4* D) {
+  using G = GeoM<DK, DV>;
+  const int l = threadIdx.x & 63;
+  f16x8 af[G::NRC];
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++) af[rc] = *(const f16x8*)&sm.afr[rc][l >> 4][l & 3][0];
+  f16x2 P[32];
+#pragma unroll
+  for (int cc = 0; cc < G::NCC; cc++) {
+    unpack_part<N, G::NCC>(raw, P, cc);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++) {
+      const int b = cc * G::NRC + rc;
+      const f16x8 bf = __builtin_shufflevector(__builtin_shufflevector(P[4 * b], P[4 * b + 1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(P[4 * b + 2], P[4 * b + 3], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rc], bf, acc, 0, 0, 0);
+    }
+    D[cc] = acc;
+    // the next part's unpack waits for this chunk's products
+#pragma unroll
+    for (int k = 0; k < 2 * N; k++) asm volatile("" : "+v"(raw[k]) : "v"(acc));
+  }
+}
 template <int N>
 __device__ __forceinline__ float code_e(const f16x2* P, int e) { return code_at<N>(P, e >> 2, e & 3); }
 // materialise a value in a VGPR at this point of the program
@@ -557,6 +585,8 @@ struct WRead {
   f32x2 kqn[GeoM<DK, DV>::NW];                              // per wave: k.q partial sum
   float cfk[WMAX];                                          // (G_t/G_s) k_s.k_t
   float cfq[WMAX];                                          // (G_t/G_s) k_s.q_t
+  float kt[DK] __attribute__((aligned(16)));                // k_t, q_t
+  float qt[DK] __attribute__((aligned(16)));
 };
 
 // One token of an open window: readout from the frozen base and the cache,
@@ -580,7 +610,6 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   // every read that does not depend on the window count t, and t itself, in
   // one round trip; then the reads that do
   uint32_t raw[2 * N];
-  f16x2 P[32];
 #pragma unroll
   for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
   float cc[G::NCC];
@@ -592,9 +621,14 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   for (int q = 0; q < NS; q++) sgl[q] = PIV ? 1.f : bf16f(scl[l + 64 * q]);
   float sg = PIV ? 1.f : bf16f(scl[rho]);
   float kk = A.k[x * DK + rho], qq = A.q[x * DK + rho];
-  float a = A.a[x];
+  float a = A.a[x], bb = A.b[x];
+  float vv[G::NCC];
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) vv[c] = A.v[x * DV + w * G::CPW + 16 * c + n16];
   const int t = *cntp;                         // tokens already in the window
-  pin(a);
+  pin(a); pin(bb);
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) pin(vv[c]);
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) pin(cc[c]);
 #pragma unroll
@@ -614,6 +648,8 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   if (rsub == 0) {
     put_afr<DK, DV, N>(sm, rho, (sg * sc) * kk, (sg * sc) * qq);
     kq = kk * qq;
+    sm.kt[rho] = kk;
+    sm.qt[rho] = qq;
     Kc[(size_t)t * DK + rho] = kk;                       // append k_t
   }
   kq = wave_sum(kq);
@@ -626,42 +662,52 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
 #pragma unroll
     for (int c = 0; c < G::NCC; c++)
       uq[i][c] = 4 * i + Gq < t ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
-  // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t for s < t: 8 consecutive lanes per token
-  // (a fixed number of passes, so that the loads issue with the tile's)
+  // cached keys k_s (s < t) for (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t, 8
+  // consecutive lanes per token: read now, used after the base matvec
+  constexpr int DP = (WMAX + G::NT / 8 - 1) / (G::NT / 8);    // passes
+  f32x4 ks[DP][DK / 32];
+  float gsv[DP];
 #pragma unroll
-  for (int it = 0; it < (WMAX + G::NT / 8 - 1) / (G::NT / 8); it++) {
+  for (int it = 0; it < DP; it++) {
     const int s = tid / 8 + it * (G::NT / 8);
-    if (s >= t) continue;
-    float ak = 0.f, aq = 0.f;
+    const bool on = s < t;
 #pragma unroll
-    for (int ii = 0; ii < DK / 32; ii++) {
-      const int i = 4 * (tid % 8) + 32 * ii;
-      const f32x4 ks = *(const f32x4*)(Kc + (size_t)s * DK + i);
-      const f32x4 kv = *(const f32x4*)(A.k + x * DK + i);
-      const f32x4 qv = *(const f32x4*)(A.q + x * DK + i);
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        ak = __builtin_fmaf(ks[e], kv[e], ak);
-        aq = __builtin_fmaf(ks[e], qv[e], aq);
-      }
-    }
-    ak = rb_sum<8>(ak);
-    aq = rb_sum<8>(aq);
-    if (tid % 8 == 0) {
-      const float r = Gt / Gc[s];
-      sm.cfk[s] = r * ak;
-      sm.cfq[s] = r * aq;
-    }
+    for (int ii = 0; ii < DK / 32; ii++)
+      ks[it][ii] = on ? *(const f32x4*)(Kc + (size_t)s * DK + 4 * (tid % 8) + 32 * ii) : f32x4{0.f, 0.f, 0.f, 0.f};
+    gsv[it] = on ? Gc[s] : 1.f;
   }
   __syncthreads();
-  unpack<N>(raw, P);
   // ---- readout and written vector from the frozen base and the cache ----
   float kqs = 0.f;
 #pragma unroll
   for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
   f32x4 D[G::NCC];
-  matvec<DK, DV>(sm, P, D);
-  const float bb = A.b[x];
+  matvec_raw<DK, DV, N>(sm, raw, D);
+#pragma unroll
+  for (int it = 0; it < DP; it++) {
+    const int s = tid / 8 + it * (G::NT / 8);
+    if (it * (G::NT / 8) >= t) break;
+    float ak = 0.f, aq = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < DK / 32; ii++) {
+      const int i = 4 * (tid % 8) + 32 * ii;
+      const f32x4 kv = *(const f32x4*)&sm.kt[i];
+      const f32x4 qv = *(const f32x4*)&sm.qt[i];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        ak = __builtin_fmaf(ks[it][ii][e], kv[e], ak);
+        aq = __builtin_fmaf(ks[it][ii][e], qv[e], aq);
+      }
+    }
+    ak = rb_sum<8>(ak);
+    aq = rb_sum<8>(aq);
+    if (tid % 8 == 0 && s < t) {
+      const float r = Gt / gsv[it];
+      sm.cfk[s] = r * ak;
+      sm.cfq[s] = r * aq;
+    }
+  }
+  __syncthreads();
   // cache terms: quad G sums its tokens s = 4i + G, then the four quads add up
   float pk[G::NCC], pq[G::NCC];
 #pragma unroll
@@ -680,7 +726,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) {
     const int j = w * G::CPW + 16 * c + n16;
-    const float rr = A.v[x * DV + j] - Gt * (cc[c] * ((D[c][0] + D[c][1]) * inv)) - g4_sum(pk[c]);
+    const float rr = vv[c] - Gt * (cc[c] * ((D[c][0] + D[c][1]) * inv)) - g4_sum(pk[c]);
     const float oo = Gt * (cc[c] * ((D[c][2] + D[c][3]) * inv)) + g4_sum(pq[c]);
     const float u2 = bb * rr;
     if (Gq == 0) {

@@ -254,6 +254,54 @@ __device__ __forceinline__ void unpack_x16(const uint32_t* raw, f16x2* P) {
   }
 }
 
+// unpack<N> of part `part` of PARTS: the pairs P[32/PARTS * part ...], which
+// come from their own stream dwords
+template <int N, int PARTS>
+__device__ __forceinline__ void unpack_part(const uint32_t* raw, f16x2* P, int part) {
+  constexpr int PP = 32 / PARTS;         // pairs per part
+  if constexpr (N == 8) {
+    const f16x2 off = {(f16)-1152.0f, (f16)-1152.0f};
+#pragma unroll
+    for (int r = part * PP / 2; r < (part + 1) * PP / 2; r++) {
+      P[2 * r] = as_h2(__builtin_amdgcn_perm(0x64646464u, raw[r], 0x04010400u)) + off;
+      P[2 * r + 1] = as_h2(__builtin_amdgcn_perm(0x64646464u, raw[r], 0x04030402u)) + off;
+    }
+  } else if constexpr (N == 4) {
+    const f16x2 off = {(f16)-1032.0f, (f16)-1032.0f};
+    const uint32_t k64 = vconst(0x64006400u);
+#pragma unroll
+    for (int m = part * PP / 4; m < (part + 1) * PP / 4; m++) {
+      const uint32_t d = raw[m];
+#pragma unroll
+      for (int c = 0; c < 4; c++) P[4 * m + c] = as_h2(((d >> (4 * c)) & 0x000F000Fu) | k64) + off;
+    }
+  } else if constexpr (N == 6) {
+    const f16x2 off = {(f16)-1056.0f, (f16)-1056.0f};
+    const uint32_t k64 = vconst(0x64006400u);
+#pragma unroll
+    for (int u = part * PP / 8; u < (part + 1) * PP / 8; u++) {
+      uint32_t d0 = raw[3 * u], d1 = raw[3 * u + 1], d2 = raw[3 * u + 2];
+      uint32_t x[4];
+      x[0] = __builtin_amdgcn_perm(d0, d0, 0x02010100u);
+      x[1] = __builtin_amdgcn_perm(d1, d0, 0x05040403u);
+      x[2] = __builtin_amdgcn_perm(d2, d1, 0x04030302u);
+      x[3] = __builtin_amdgcn_perm(d2, d2, 0x03020201u);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        u16x2 xv = __builtin_bit_cast(u16x2, x[q]);
+        u16x2 lo = xv >> (u16x2){0, 4};
+        u16x2 hi = xv >> (u16x2){6, 10};
+        int r = 4 * u + q;
+        P[2 * r] = as_h2((__builtin_bit_cast(uint32_t, lo) & 0x003F003Fu) | k64) + off;
+        P[2 * r + 1] = as_h2((__builtin_bit_cast(uint32_t, hi) & 0x003F003Fu) | k64) + off;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = part * PP; k < (part + 1) * PP; k++) P[k] = as_h2(raw[k]);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ float code_at(const f16x2* P, int r, int c) {
   return (float)P[preg<N>(r, c)][phalf<N>(r, c)];
