@@ -25,6 +25,9 @@ namespace {
 
 enum { MODE_STEP = 0, MODE_STORE = 1 };
 
+typedef __attribute__((address_space(1))) const void* gptr_t;   // global source of a direct-to-LDS load
+typedef __attribute__((address_space(3))) void* lptr_t;         // its LDS destination
+
 struct KArgs {
   uint8_t* pool;
   const int32_t* slots;      // nullptr: slot = request index
@@ -593,8 +596,8 @@ struct WRead {
 // then the token's (G_t, k_t, u_t) appended.  A window that this token fills
 // (t + 1 = W) is left full for the fold kernel that runs next.
 template <int DK, int DV, int N>
-__device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, uint8_t* tile, uint8_t* cache,
-                                            size_t x) {
+__device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, float* cst, uint8_t* tile,
+                                            uint8_t* cache, size_t x) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
   constexpr bool PIV = (N == 16);
@@ -654,27 +657,31 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   }
   kq = wave_sum(kq);
   if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
-  // the lane quad's cached u entries (s = 4i + Gq): issued with the other reads
-  // that wait for t
-  float uq[UQ][G::NCC];
-#pragma unroll
-  for (int i = 0; i < UQ; i++)
-#pragma unroll
-    for (int c = 0; c < G::NCC; c++)
-      uq[i][c] = 4 * i + Gq < t ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
-  // cached keys k_s (s < t) for (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t, 8
-  // consecutive lanes per token: read now, used after the base matvec
+  // The open window's cached k_s and u_s (s < t) go straight from memory to
+  // LDS (cst: W d_k floats, then W d_v), so that nothing waits for them
+  // before the base matvec and no registers hold them meanwhile
+  {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int nk = t * DK * 4, nu = t * DV * 4;          // bytes
+    for (int c = wu; c < (nk + 1023) / 1024; c += G::NW) {
+      const int off = c * 1024 + 16 * l;
+      if (off < nk)
+        __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Kc + off), (lptr_t)((uint8_t*)cst + c * 1024), 16, 0, 0);
+    }
+    for (int c = wu; c < (nu + 1023) / 1024; c += G::NW) {
+      const int off = c * 1024 + 16 * l;
+      if (off < nu)
+        __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + off),
+                                         (lptr_t)((uint8_t*)cst + W * DK * 4 + c * 1024), 16, 0, 0);
+    }
+  }
+  // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t, 8 consecutive lanes per token
   constexpr int DP = (WMAX + G::NT / 8 - 1) / (G::NT / 8);    // passes
-  f32x4 ks[DP][DK / 32];
   float gsv[DP];
 #pragma unroll
   for (int it = 0; it < DP; it++) {
     const int s = tid / 8 + it * (G::NT / 8);
-    const bool on = s < t;
-#pragma unroll
-    for (int ii = 0; ii < DK / 32; ii++)
-      ks[it][ii] = on ? *(const f32x4*)(Kc + (size_t)s * DK + 4 * (tid % 8) + 32 * ii) : f32x4{0.f, 0.f, 0.f, 0.f};
-    gsv[it] = on ? Gc[s] : 1.f;
+    gsv[it] = s < t ? Gc[s] : 1.f;
   }
   __syncthreads();
   // ---- readout and written vector from the frozen base and the cache ----
@@ -683,6 +690,8 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
   for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
   f32x4 D[G::NCC];
   matvec_raw<DK, DV, N>(sm, raw, D);
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this wave's staging loads have landed
+  __syncthreads();                             // and every other wave's
 #pragma unroll
   for (int it = 0; it < DP; it++) {
     const int s = tid / 8 + it * (G::NT / 8);
@@ -693,10 +702,11 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
       const int i = 4 * (tid % 8) + 32 * ii;
       const f32x4 kv = *(const f32x4*)&sm.kt[i];
       const f32x4 qv = *(const f32x4*)&sm.qt[i];
+      const f32x4 ks = *(const f32x4*)&cst[(s < t ? s : 0) * DK + i];   // rows >= t are not staged
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        ak = __builtin_fmaf(ks[it][ii][e], kv[e], ak);
-        aq = __builtin_fmaf(ks[it][ii][e], qv[e], aq);
+        ak = __builtin_fmaf(ks[e], kv[e], ak);
+        aq = __builtin_fmaf(ks[e], qv[e], aq);
       }
     }
     ak = rb_sum<8>(ak);
@@ -719,8 +729,9 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, u
     const float fk = s < t ? sm.cfk[s] : 0.f, fq = s < t ? sm.cfq[s] : 0.f;
 #pragma unroll
     for (int c = 0; c < G::NCC; c++) {
-      pk[c] = __builtin_fmaf(fk, uq[i][c], pk[c]);
-      pq[c] = __builtin_fmaf(fq, uq[i][c], pq[c]);
+      const float u = s < t ? cst[W * DK + (s < t ? s : 0) * DV + w * G::CPW + 16 * c + n16] : 0.f;
+      pk[c] = __builtin_fmaf(fk, u, pk[c]);
+      pq[c] = __builtin_fmaf(fq, u, pq[c]);
     }
   }
 #pragma unroll
@@ -846,6 +857,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
 template <int DK, int DV>
 __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(5))) void k_window_read(KArgs A) {
   __shared__ WRead<DK, DV> sm;
+  extern __shared__ float cst_[];               // W (d_k + d_v) floats: the staged window cache
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
@@ -856,10 +868,10 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
   const size_t x = (size_t)ci * A.H + h;
   switch (A.head_bits[h]) {
-    case 4: window_read<DK, DV, 4>(A, sm, tile, cache, x); break;
-    case 6: window_read<DK, DV, 6>(A, sm, tile, cache, x); break;
-    case 8: window_read<DK, DV, 8>(A, sm, tile, cache, x); break;
-    default: window_read<DK, DV, 16>(A, sm, tile, cache, x); break;
+    case 4: window_read<DK, DV, 4>(A, sm, cst_, tile, cache, x); break;
+    case 6: window_read<DK, DV, 6>(A, sm, cst_, tile, cache, x); break;
+    case 8: window_read<DK, DV, 8>(A, sm, cst_, tile, cache, x); break;
+    default: window_read<DK, DV, 16>(A, sm, cst_, tile, cache, x); break;
   }
 }
 
@@ -2092,7 +2104,8 @@ stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st)
 template <int DK, int DV>
 void launch_window(const KArgs& A, bool step, hipStream_t st) {
   if (step) {
-    hipLaunchKernelGGL((k_window_read<DK, DV>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    hipLaunchKernelGGL((k_window_read<DK, DV>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT),
+                       (size_t)A.W * (DK + DV) * 4, st, A);
     const unsigned T = (unsigned)A.n * (unsigned)A.H;
     hipLaunchKernelGGL((k_window_fold<DK, DV, true>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
   } else {
