@@ -855,7 +855,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
 
 // readout and append of every tile of the call
 template <int DK, int DV>
-__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(5))) void k_window_read(KArgs A) {
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(7))) void k_window_read(KArgs A) {
   __shared__ WRead<DK, DV> sm;
   extern __shared__ float cst_[];               // W (d_k + d_v) floats: the staged window cache
   const int T = A.n * A.H;
