@@ -1712,28 +1712,66 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
     int k4 = c4, k6 = c6, k8 = c8;
     asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));   // per-phase scalar run bounds
     uint32_t sbase = (uint32_t)(uintptr_t)stage;      // LDS address of the staged codes
+    const uint32_t soff = (uint32_t)(uintptr_t)stage;
+    // the 32 steps; dec(r) returns the lane's two codes of record row ws0 + r
+    auto steps = [&](auto dec, uint32_t& sb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < G::NR; r++) {
-      // the lane's two codes start at bit 2 n l of the record: one 64-bit window, two fields
-      const int p = ws0 + r;
-      const int n = 4 + (p >= k4 ? 2 : 0) + (p >= k6 ? 2 : 0);
-      const int rec = 64 * p + 32 * max(p - k4, 0) + 32 * max(p - k6, 0);
-      const uint32_t bit = (uint32_t)(2 * n) * (uint32_t)l;
-      const uint32_t* sw = (const uint32_t*)(stage + ((sbase + rec + 4 * (bit >> 5)) - (uint32_t)(uintptr_t)stage));
-      const uint32_t g = __builtin_amdgcn_alignbit(sw[1], sw[0], bit);
-      const uint32_t f0 = __builtin_amdgcn_ubfe(g, 0, n), f1 = __builtin_amdgcn_ubfe(g, n, n);
-      const uint32_t kb = (0xE400u + (1u << (n - 1))) * 0x10001u;   // -(1024 + 2^(n-1)), both halves
-      P[r] = as_h2(f0 | (f1 << 16) | 0x64006400u) + as_h2(kb);
-      const f32x2 abr = rs.ab[p];
-      const float q0 = (float)P[r][0], q1 = (float)P[r][1];
-      U0 = __builtin_fmaf(q0, abr[0], U0);
-      U1 = __builtin_fmaf(q1, abr[0], U1);
-      W0 = __builtin_fmaf(q0, abr[1], W0);
-      W1 = __builtin_fmaf(q1, abr[1], W1);
-      // four steps at a time (the next four steps' loads wait for these sums):
-      // enough LDS reads in flight, and the scheduler cannot hoist all 32
-      // steps' loads (which spills)
-      if ((r & 3) == 3) asm volatile("" : "+v"(sbase) : "v"(U0), "v"(U1), "v"(W0), "v"(W1));
+      for (int r = 0; r < G::NR; r++) {
+        P[r] = dec(r, sb);
+        const f32x2 abr = rs.ab[ws0 + r];
+        const float q0 = (float)P[r][0], q1 = (float)P[r][1];
+        U0 = __builtin_fmaf(q0, abr[0], U0);
+        U1 = __builtin_fmaf(q1, abr[0], U1);
+        W0 = __builtin_fmaf(q0, abr[1], W0);
+        W1 = __builtin_fmaf(q1, abr[1], W1);
+        // four steps at a time (the next four steps' loads wait for these sums):
+        // enough LDS reads in flight, and the scheduler cannot hoist all 32
+        // steps' loads (which spills)
+        if ((r & 3) == 3) asm volatile("" : "+v"(sb) : "v"(U0), "v"(U1), "v"(W0), "v"(W1));
+      }
+    };
+    // A wave whose 32 rows share one width (no pivots) decodes with that
+    // width's constant record stride and field layout
+    const int uw = ws0 + G::NR <= k4 ? 4 : (ws0 >= k4 && ws0 + G::NR <= k6 ? 6 : (ws0 >= k6 && ws0 + G::NR <= k8 ? 8 : 0));
+    const uint32_t k64 = vconst(0x64006400u);
+    if (uw == 4) {
+      // 64-byte records, the lane's byte l: fields at bits 0 and 4
+      const uint32_t a0 = 64 * ws0 + l;
+      const f16x2 kb = as_h2(0xE408E408u);            // -(1024 + 8)
+      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
+        const uint32_t b = *(const uint8_t*)(stage + ((sb + a0 + 64 * r) - soff));
+        return as_h2(((b | (b << 12)) & 0x000F000Fu) | k64) + kb;
+      }, sbase);
+    } else if (uw == 6) {
+      // 96-byte records: the lane's 12 bits start at bit 12 l
+      const uint32_t a0 = 64 * k4 + 96 * (ws0 - k4) + 4 * ((12 * l) >> 5), sh = (12 * l) & 31;
+      const f16x2 kb = as_h2(0xE420E420u);            // -(1024 + 32)
+      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
+        const uint32_t* sw = (const uint32_t*)(stage + ((sb + a0 + 96 * r) - soff));
+        const uint32_t g = __builtin_amdgcn_alignbit(sw[1], sw[0], sh);   // bits 12.. are the next lanes'
+        return as_h2(((g << 10) & 0x003F0000u) | ((g & 0x3Fu) | k64)) + kb;
+      }, sbase);
+    } else if (uw == 8) {
+      // 128-byte records, the lane's 16 bits at byte 2 l
+      const uint32_t a0 = 64 * k4 + 96 * (k6 - k4) + 128 * (ws0 - k6) + 2 * l;
+      const f16x2 kb = as_h2(0xE480E480u);            // -(1024 + 128)
+      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
+        const uint32_t hw = *(const uint16_t*)(stage + ((sb + a0 + 128 * r) - soff));
+        return as_h2(__builtin_amdgcn_perm(0x64646464u, hw, 0x04010400u)) + kb;
+      }, sbase);
+    } else {
+      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
+        // the lane's two codes start at bit 2 n l of the record: one 64-bit window, two fields
+        const int p = ws0 + r;
+        const int n = 4 + (p >= k4 ? 2 : 0) + (p >= k6 ? 2 : 0);
+        const int rec = 64 * p + 32 * max(p - k4, 0) + 32 * max(p - k6, 0);
+        const uint32_t bit = (uint32_t)(2 * n) * (uint32_t)l;
+        const uint32_t* sw = (const uint32_t*)(stage + ((sb + rec + 4 * (bit >> 5)) - soff));
+        const uint32_t g = __builtin_amdgcn_alignbit(sw[1], sw[0], bit);
+        const uint32_t f0 = __builtin_amdgcn_ubfe(g, 0, n), f1 = __builtin_amdgcn_ubfe(g, n, n);
+        const uint32_t kb = (0xE400u + (1u << (n - 1))) * 0x10001u;   // -(1024 + 2^(n-1)), both halves
+        return as_h2(f0 | (f1 << 16) | 0x64006400u) + as_h2(kb);
+      }, sbase);
     }
   }
   float Up0 = 0.f, Up1 = 0.f, Wp0 = 0.f, Wp1 = 0.f;
