@@ -88,8 +88,8 @@ struct GeoM {
   static constexpr int NW = DV / CPW;       // waves per tile
   static constexpr int NT = 64 * NW;
   static constexpr int TPR = NT / DK;       // threads per row in the row stage
-  static constexpr int NP = NW * 16;        // partial row maxima per row
-  static constexpr int PSTR = NP + 4;       // LDS row stride of the partials (2-way optimal writes)
+  static constexpr int NP = NW * 8;         // partial row maxima per row (lane pairs n, n ^ 8 merged)
+  static constexpr int PSTR = NP + 4;       // LDS row stride of the partials
   static_assert(DK == 64 || DK == 128, "d_k");
   static_assert(NW >= 1 && DV % CPW == 0, "d_v");
   static_assert(TPR == 1 || TPR == 2, "threads per row");
@@ -276,7 +276,10 @@ __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t
 #pragma unroll
           for (int cc = 0; cc < G::NCC; cc++)
             m = __builtin_fmaxf(m, __builtin_fabsf(Y[8 * (cc * G::NRC + rc) + 4 * hf + i]));
-          sm.part[(erow(rc, 4 * hf, Gq) + i) * G::PSTR + w * 16 + n16] = m;
+          // with lane n ^ 8 (same rows): non-negative, so compare bit patterns
+          const uint32_t mb = __float_as_uint(m);
+          const uint32_t mp = __builtin_elementwise_max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x128, 0xF, 0xF, false));
+          sm.part[(erow(rc, 4 * hf, Gq) + i) * G::PSTR + w * 8 + (n16 & 7)] = __uint_as_float(mp);   // both lanes: same value
         }
       }
     lds_barrier();
@@ -316,26 +319,32 @@ __device__ __forceinline__ void refit_store(SmemM<DK, DV>& sm, float* Y, uint8_t
     const int E = ec ? mean_exp(es, ec) : 0;
     if (w >= W0 && rsub == 0) scl[rho] = (uint16_t)bf16_adj(s, -E);
     // ---- column refit: X = Y h, column absmax over the wave's 4 row quads ----
-    float hr[8 * G::NRC];
+    // one 32-row chunk's factors at a time; each chunk's LDS reads wait for the
+    // previous chunk's maxima, so they are not all hoisted (registers)
+    constexpr float RQ = 1.0f / (float)Fmt<N>::QMAX;
+    float rq[G::NCC], cmx[G::NCC];
 #pragma unroll
-    for (int rc = 0; rc < G::NRC; rc++)
+    for (int cc = 0; cc < G::NCC; cc++) cmx[cc] = 0.f;
+    uint32_t rbase = (uint32_t)(uintptr_t)&sm.rowh[4 * Gq];
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++) {
+      float hr[8];
 #pragma unroll
       for (int hf = 0; hf < 2; hf++)
-        *(f32x4*)&hr[8 * rc + 4 * hf] = *(const f32x4*)&sm.rowh[erow(rc, 4 * hf, Gq)];
-    constexpr float RQ = 1.0f / (float)Fmt<N>::QMAX;
-    float rq[G::NCC];
+        *(f32x4*)&hr[4 * hf] = *(const f32x4*)((const uint8_t*)sm.rowh + (rbase + 4 * (32 * rc + 16 * hf) - (uint32_t)(uintptr_t)sm.rowh));
 #pragma unroll
-    for (int cc = 0; cc < G::NCC; cc++) {
-      float cm = 0.f;
-#pragma unroll
-      for (int rc = 0; rc < G::NRC; rc++)
+      for (int cc = 0; cc < G::NCC; cc++)
 #pragma unroll
         for (int t = 0; t < 8; t++) {
           const int e = 8 * (cc * G::NRC + rc) + t;
-          Y[e] = Y[e] * hr[8 * rc + t];
-          cm = __builtin_fmaxf(cm, __builtin_fabsf(Y[e]));
+          Y[e] = Y[e] * hr[t];
+          cmx[cc] = __builtin_fmaxf(cmx[cc], __builtin_fabsf(Y[e]));
         }
-      const float M = g4_max_pos(cm) * RQ;
+      if (SPLIT) asm volatile("" : "+v"(rbase) : "v"(cmx[0]), "v"(cmx[G::NCC - 1]));
+    }
+#pragma unroll
+    for (int cc = 0; cc < G::NCC; cc++) {
+      const float M = g4_max_pos(cmx[cc]) * RQ;
       uint32_t tt = 0x3F80u;
       if (M > 0.f) {
         tt = bf16_ru_pos(M);
