@@ -178,9 +178,9 @@ class OraclePool:
     """Host image of a whole pool buffer, advanced by the oracle."""
 
     def __init__(self, n_slots, n_heads, d_k, d_v, bits, row_weight, gate_kind=0,
-                 unit_kind=0, window=0, image=None):
+                 unit_kind=0, window=0, image=None, n_comp=0):
         self.n_slots, self.H, self.dk, self.dv = n_slots, n_heads, d_k, d_v
-        self.gate, self.unit, self.W = gate_kind, unit_kind, window
+        self.gate, self.unit, self.W, self.C = gate_kind, unit_kind, window, n_comp
         self.bits = _c(bits, np.int32)
         self.wt = _c(row_weight, np.float32).reshape(n_heads, d_k)
         self.nbytes = lib().orc_pool_bytes(*self._d())
@@ -192,7 +192,8 @@ class OraclePool:
             self.img = _c(image, np.uint8).copy()
 
     def _d(self):
-        return (self.n_slots, self.H, self.dk, self.dv, self.gate, self.unit, self.W,
+        # the window argument carries the compensator count in its high half
+        return (self.n_slots, self.H, self.dk, self.dv, self.gate, self.unit, self.W | (self.C << 16),
                 _p(self.bits))
 
     def store(self, slots, S):
@@ -261,6 +262,23 @@ class OraclePool:
         offs, sb = self.head_offsets()
         base = self.hdr_bytes() + slot * sb + offs[h]
         return img[base: base + self._tile_bytes(h)]
+
+    def cache_stride(self):
+        return 256 + 4 * self.W * (self.dk + self.dv) + 4 * self.C * self.dv if self.W else 0
+
+    def cache_view(self, slot, h, img=None):
+        """(count, G[W], K[W][dk], U[W][dv], comp rows[C], comp values[C][dv]) of a tile's window."""
+        img = self.img if img is None else img
+        _, sb = self.head_offsets()
+        st = self.cache_stride()
+        base = self.hdr_bytes() + self.n_slots * sb + (slot * self.H + h) * st
+        c = img[base: base + st]
+        W, dk, dv = self.W, self.dk, self.dv
+        kend = 256 + 4 * W * dk
+        uend = kend + 4 * W * dv
+        return (int(c[0:4].view(np.int32)[0]), c[4: 4 + 4 * W].view(np.float32),
+                c[256:kend].view(np.float32).reshape(W, dk), c[kend:uend].view(np.float32).reshape(W, dv),
+                c[192: 192 + 4 * self.C].view(np.int32), c[uend:].view(np.float32).reshape(self.C, dv))
 
     def decode_tile(self, slot, h, img=None):
         """(Q, sigma, c, widths) of one tile, rows in original order."""

@@ -27,7 +27,9 @@
  *    16-bit scale per row and per column of a 128x128 state; FP16 pivots.
  *  - LeapQuant post (wink.run), techniques one and three: state frozen inside
  *    a token window, updates cached at high precision, readout from both,
- *    requantize with per-row smoothing at the window end.
+ *    requantize with per-row smoothing at the window end; technique two:
+ *    the largest outliers kept at high precision as rank-one terms that ride
+ *    the window's update path (compensator tokens).
  */
 #include <math.h>
 #include <stdint.h>
@@ -116,6 +118,7 @@ static int qmax_of(int n) { return (1 << (n - 1)) - 1; }
 
 typedef struct {
   int n_slots, H, dk, dv, gate, unit, W;
+  int C;                 /* compensator rows per tile (window mode) */
   const int32_t* bits;   /* [H] (per-head units) or [H*dk] (per-row units) */
   const float* wt;       /* [H*dk] */
 } orc_desc;
@@ -435,14 +438,17 @@ static void row_order(const orc_desc* d, int h, int* perm, int* cnt) {
       if (d->bits[(size_t)h * d->dk + i] == W4[k]) { perm[p++] = i; cnt[k]++; }
   }
 }
+/* window cache of a tile: [0,4) token count, [4, 4+4W) G, [192, 192+4C)
+ * compensator rows (int32, -1 = none), 256: k[W][dk], u[W][dv], then the
+ * compensator values [C][dv], all binary32. */
 static size_t cache_stride(const orc_desc* d) {
-  return d->W ? 256 + 4 * (size_t)d->W * (d->dk + d->dv) : 0;
+  return d->W ? 256 + 4 * (size_t)d->W * (d->dk + d->dv) + 4 * (size_t)d->C * d->dv : 0;
 }
 static size_t cache_off(const orc_desc* d) { return hdr_bytes(d) + (size_t)d->n_slots * slot_bytes(d); }
 
 size_t orc_pool_bytes(int n_slots, int H, int dk, int dv, int gate, int unit, int W,
                       const int32_t* bits) {
-  orc_desc d = {n_slots, H, dk, dv, gate, unit, W, bits, NULL};
+  orc_desc d = {n_slots, H, dk, dv, gate, unit, W & 0xFFFF, W >> 16, bits, NULL};
   return cache_off(&d) + (size_t)n_slots * H * cache_stride(&d);
 }
 
@@ -453,12 +459,12 @@ static void put64(uint8_t* p, uint64_t v) { for (int b = 0; b < 8; b++) p[b] = (
  * scales 1.0) + empty windows. */
 void orc_pool_init(int n_slots, int H, int dk, int dv, int gate, int unit, int W,
                    const int32_t* bits, const float* wt, uint8_t* img) {
-  orc_desc d = {n_slots, H, dk, dv, gate, unit, W, bits, wt};
+  orc_desc d = {n_slots, H, dk, dv, gate, unit, W & 0xFFFF, W >> 16, bits, wt};
   size_t total = orc_pool_bytes(n_slots, H, dk, dv, gate, unit, W, bits);
   memset(img, 0, total);
   put32(img + 0, 0x31515453u);
   put32(img + 4, n_slots); put32(img + 8, H); put32(img + 12, dk); put32(img + 16, dv);
-  put32(img + 20, gate); put32(img + 24, unit); put32(img + 28, W);
+  put32(img + 20, gate); put32(img + 24, unit); put32(img + 28, (uint32_t)W);   /* W | C << 16 */
   put64(img + 32, slot_bytes(&d)); put64(img + 40, hdr_bytes(&d));
   put64(img + 48, cache_off(&d)); put64(img + 56, cache_stride(&d));
   for (int h = 0; h < H; h++) {
@@ -501,6 +507,51 @@ static uint8_t* cache_ptr(const orc_desc* d, uint8_t* img, int slot, int h) {
   return img + cache_off(d) + ((size_t)slot * d->H + h) * cache_stride(d);
 }
 
+/* ---- compensator tokens (LeapQuant post, technique two) ----
+ * READING: the C key rows of largest absolute value (row absmax of the
+ * binary32 state about to be quantized; ties to the lower row) are taken out
+ * and kept exactly in binary32 as rank-one terms e_i u^T, u = that row; the
+ * residual, with those rows zero, is what R quantizes.  A quantized head only
+ * (a binary16 pivot head is stored exactly anyway); rows that are all zero
+ * are never taken (the slot is then marked -1).  Inside a window the
+ * compensators belong to the frozen base: they are gated with it and folded
+ * with it. */
+static int32_t* comp_idx(const orc_desc* d, uint8_t* cache) { (void)d; return (int32_t*)(cache + 192); }
+static float* comp_val(const orc_desc* d, uint8_t* cache) {
+  return (float*)(cache + 256 + 4 * (size_t)d->W * (d->dk + d->dv));
+}
+static int comp_head(const orc_desc* d, int h) { return d->W && d->C && d->unit == 0 && d->bits[h] != 16; }
+static void comp_extract(const orc_desc* d, int h, float* S, uint8_t* cache) {
+  if (!d->W || !d->C) return;
+  int dk = d->dk, dv = d->dv;
+  int32_t* idx = comp_idx(d, cache);
+  float* val = comp_val(d, cache);
+  for (int c = 0; c < d->C; c++) {
+    int best = -1;
+    float bm = 0.0f;
+    if (comp_head(d, h))
+      for (int i = 0; i < dk; i++) {
+        float m = 0.0f;
+        for (int j = 0; j < dv; j++) { float x = fabsf(S[(size_t)i * dv + j]); if (x > m) m = x; }
+        if (m > bm) { bm = m; best = i; }     /* strict: ties keep the lower row */
+      }
+    idx[c] = best;
+    for (int j = 0; j < dv; j++) {
+      val[(size_t)c * dv + j] = best >= 0 ? S[(size_t)best * dv + j] : 0.0f;
+      if (best >= 0) S[(size_t)best * dv + j] = 0.0f;
+    }
+  }
+}
+/* the represented base state: D(tile) plus the compensator rows */
+static void comp_add(const orc_desc* d, uint8_t* cache, float* S) {
+  if (!d->W || !d->C) return;
+  const int32_t* idx = comp_idx(d, cache);
+  const float* val = comp_val(d, cache);
+  for (int c = 0; c < d->C; c++)
+    if (idx[c] >= 0)
+      for (int j = 0; j < d->dv; j++) S[(size_t)idx[c] * d->dv + j] += val[(size_t)c * d->dv + j];
+}
+
 typedef struct {
   int32_t* Q; uint16_t* sg; uint16_t* cs; int32_t* nb; float* S; double* A;
 } scratch_t;
@@ -539,7 +590,7 @@ static const float* row_w(const orc_desc* d, const uint8_t* img, int h) {
   return (const float*)(img + woff_of(d)) + (size_t)h * d->dk;
 }
 #define DESC_ARGS int n_slots, int H, int dk, int dv, int gate, int unit, int W, const int32_t* bits
-#define MKDESC orc_desc d = {n_slots, H, dk, dv, gate, unit, W, bits, NULL}
+#define MKDESC orc_desc d = {n_slots, H, dk, dv, gate, unit, W & 0xFFFF, W >> 16, bits, NULL}
 
 /* stq_pool_store: tile := R(S), windows emptied. */
 void orc_pool_store(DESC_ARGS, uint8_t* img, const int32_t* slots, int n, const float* S) {
@@ -551,8 +602,15 @@ void orc_pool_store(DESC_ARGS, uint8_t* img, const int32_t* slots, int n, const 
     for (long x = 0; x < (long)n * H; x++) {
       int c = (int)(x / H), h = (int)(x % H);
       const float* Sx = S + (size_t)x * dk * dv;
-      tile_encode(&d, h, Sx, row_w(&d, img, h), tile_ptr(&d, img, slots[c], h), &t);
-      if (W) memset(cache_ptr(&d, img, slots[c], h), 0, 4);
+      if (d.W) {
+        uint8_t* cp = cache_ptr(&d, img, slots[c], h);
+        memcpy(t.S, Sx, 4 * (size_t)dk * dv);
+        comp_extract(&d, h, t.S, cp);
+        tile_encode(&d, h, t.S, row_w(&d, img, h), tile_ptr(&d, img, slots[c], h), &t);
+        memset(cp, 0, 4);
+      } else {
+        tile_encode(&d, h, Sx, row_w(&d, img, h), tile_ptr(&d, img, slots[c], h), &t);
+      }
     }
     scratch_free(&t);
   }
@@ -567,6 +625,7 @@ void orc_pool_fetch(DESC_ARGS, uint8_t* img, const int32_t* slots, int n, float*
     for (long x = 0; x < (long)n * H; x++) {
       int c = (int)(x / H), h = (int)(x % H);
       tile_decode(&d, h, tile_ptr(&d, img, slots[c], h), &t);
+      if (d.W) comp_add(&d, cache_ptr(&d, img, slots[c], h), t.S);
       memcpy(S + (size_t)x * dk * dv, t.S, 4 * (size_t)dk * dv);
     }
     scratch_free(&t);
@@ -653,6 +712,7 @@ static void window_fold(const orc_desc* d, int h, uint8_t* tile, uint8_t* cache,
   const float* K = (const float*)(cache + 256);
   const float* U = (const float*)(cache + 256 + 4 * (size_t)W * dk);
   tile_decode(d, h, tile, t);
+  comp_add(d, cache, t->S);
   double Gt = G[cnt - 1];
   for (int i = 0; i < dk; i++)
     for (int j = 0; j < dv; j++) {
@@ -662,6 +722,7 @@ static void window_fold(const orc_desc* d, int h, uint8_t* tile, uint8_t* cache,
       t->A[(size_t)i * dv + j] = s;
     }
   for (size_t x = 0; x < (size_t)dk * dv; x++) t->S[x] = (float)t->A[x];
+  comp_extract(d, h, t->S, cache);
   tile_encode(d, h, t->S, w, tile, t);
   memset(cache, 0, 4);
 }
@@ -677,6 +738,7 @@ static void window_step_tile(const orc_desc* d, int h, uint8_t* tile, uint8_t* c
   float* U = (float*)(cache + 256 + 4 * (size_t)W * dk);
   float Gt = (cnt == 0) ? a : G[cnt - 1] * a;   /* binary32 product, as stored */
   tile_decode(d, h, tile, t);
+  comp_add(d, cache, t->S);
   double* yk = (double*)calloc(dv, 8);
   double* yq = (double*)calloc(dv, 8);
   for (int j = 0; j < dv; j++) {
