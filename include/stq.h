@@ -205,6 +205,8 @@ typedef struct stq_pool_desc {
   int32_t gate_kind;    /* STQ_GATE_HEAD or STQ_GATE_CHANNEL                */
   int32_t unit_kind;    /* STQ_UNIT_HEAD (this build) or STQ_UNIT_ROW       */
   int32_t window;       /* 0 = requantize every token; W in [1,32] = window */
+  int32_t n_comp;       /* window mode: compensator rows per tile, 0..8,     */
+                        /* window + n_comp <= 32; 0 without a window         */
   const int32_t* unit_bits;  /* [H] (HEAD) or [H][d_k] (ROW): 4, 6, 8 or 16   */
   const float* row_weight;   /* [H][d_k] row-impact weights, finite and > 0   */
 } stq_pool_desc;

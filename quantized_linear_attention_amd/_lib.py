@@ -22,7 +22,7 @@ class _Desc(ctypes.Structure):
     _fields_ = [("n_slots", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("gate_kind", ctypes.c_int32), ("unit_kind", ctypes.c_int32),
-                ("window", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("n_comp", ctypes.c_int32),
                 ("unit_bits", ctypes.POINTER(ctypes.c_int32)),
                 ("row_weight", ctypes.POINTER(ctypes.c_float))]
 
@@ -70,12 +70,12 @@ def _check(status, what):
 
 
 def make_desc(n_slots, n_heads, d_k, d_v, unit_bits, row_weight, gate_kind=STQ_GATE_HEAD,
-              unit_kind=STQ_UNIT_HEAD, window=0):
+              unit_kind=STQ_UNIT_HEAD, window=0, n_comp=0):
     """Build a stq_pool_desc; the returned object keeps its host arrays alive."""
     bits = np.ascontiguousarray(unit_bits, dtype=np.int32).reshape(-1)
     wt = np.ascontiguousarray(row_weight, dtype=np.float32).reshape(-1)
     d = _Desc(int(n_slots), int(n_heads), int(d_k), int(d_v), int(gate_kind), int(unit_kind),
-              int(window), bits.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+              int(window), int(n_comp), bits.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
               wt.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
     d._keep = (bits, wt)
     return d

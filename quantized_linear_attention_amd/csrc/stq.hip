@@ -32,6 +32,7 @@ struct KArgs {
   uint8_t* pool;
   const int32_t* slots;      // nullptr: slot = request index
   int n, H, n_slots, gate, W;
+  int C;                     // window mode: compensator rows per tile
   uint64_t slots_off, slot_bytes, cache_off, cache_stride;
   const int32_t* head_bits;  // device: header tables
   const uint32_t* head_off;
@@ -106,6 +107,7 @@ struct SmemM {
   float part[DK * GeoM<DK, DV>::PSTR] __attribute__((aligned(16)));   // [row][partial]
   f32x2 kqn[GeoM<DK, DV>::NW];   // per wave: k.q partial sum, 1 if some gate differs from 1
   int epk[GeoM<DK, DV>::NW];     // per wave: sum of row exponents * 256 + row count
+  int csel[8];                   // window mode: the compensator rows just chosen
 };
 
 // element t (0..7) of the lane's two groups of a chunk -> k index of its
@@ -386,6 +388,96 @@ __device__ __forceinline__ void clear_rows(const SmemM<DK, DV>& sm, f16x2* P) {
     }
 }
 
+// Compensator tokens (window mode).  The C key rows of largest absolute value
+// of the state about to be refitted, g_i max_j |Y_ij| (g = 1 at ingest), ties to
+// the lower row, all-zero rows never, are written exactly to the tile's cache
+// (row index, then the values g_i Y_ij) and zeroed in Y, so that the refit
+// sees the residual.  A binary16 pivot tile takes none: its slots get -1 and
+// zeros.  Uses the partials, rowh and kappa[1] of the LDS (free before the
+// refit's own partials).
+template <int DK, int DV>
+__device__ __forceinline__ void comp_extract(SmemM<DK, DV>& sm, float* Y, bool scaled, uint8_t* cache, int W,
+                                             int C, bool quantized) {
+  using G = GeoM<DK, DV>;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  int32_t* idxg = (int32_t*)(cache + 192);
+  float* valg = (float*)(cache + 256 + 4 * (size_t)W * (DK + DV));
+  int* cslot = (int*)sm.kappa[1];
+  int* sel = sm.csel;
+  if (!quantized) {
+    for (int c = tid; c < C; c += G::NT) idxg[c] = -1;
+    for (int x = tid; x < C * DV; x += G::NT) valg[x] = 0.f;
+    return;
+  }
+  // row maxima of |Y| over the lane's columns, merged with lane n ^ 8, to the partials
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        float m = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < G::NCC; cc++) m = __builtin_fmaxf(m, __builtin_fabsf(Y[8 * (cc * G::NRC + rc) + 4 * hf + i]));
+        const uint32_t mb = __float_as_uint(m);
+        const uint32_t mp = __builtin_elementwise_max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x128, 0xF, 0xF, false));
+        sm.part[(erow(rc, 4 * hf, Gq) + i) * G::PSTR + w * 8 + (n16 & 7)] = __uint_as_float(mp);
+      }
+  lds_barrier();
+  if (tid < DK) {
+    uint32_t mxb = 0u;
+    for (int p = 0; p < G::NP; p++) mxb = __builtin_elementwise_max(mxb, __float_as_uint(sm.part[tid * G::PSTR + p]));
+    sm.rowh[tid] = (scaled ? sm.gg[tid] : 1.f) * __uint_as_float(mxb);
+    cslot[tid] = -1;
+  }
+  lds_barrier();
+  if (w == 0) {                                    // C rounds of a wave-wide arg-max
+    const float m0i = sm.rowh[l], m1i = DK > 64 ? sm.rowh[(64 + l) & (DK - 1)] : 0.f;
+    float m0 = m0i, m1 = m1i;
+    for (int c = 0; c < C; c++) {
+      const float mx = wave_max_pos(__builtin_fmaxf(m0, m1));
+      int row = -1;
+      if (mx > 0.f) {
+        const uint64_t b0 = __ballot(m0 == mx);
+        row = b0 ? (int)__builtin_ctzll(b0) : 64 + (int)__builtin_ctzll(__ballot(m1 == mx));
+        if (l == (row & 63)) {
+          if (row < 64) m0 = 0.f;
+          else m1 = 0.f;
+        }
+      }
+      if (l == 0) { sel[c] = row; idxg[c] = row; }
+      if (row >= 0 && l == (row & 63)) cslot[row] = c;
+    }
+  }
+  lds_barrier();
+  // the lane's elements of those rows: to the cache exactly, then zero
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      const int r0 = erow(rc, 4 * hf, Gq);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int cs = cslot[r0 + i];
+        if (cs >= 0) {
+          const float g = scaled ? sm.gg[r0 + i] : 1.f;
+#pragma unroll
+          for (int cc = 0; cc < G::NCC; cc++) {
+            const int e = 8 * (cc * G::NRC + rc) + 4 * hf + i;
+            valg[cs * DV + w * G::CPW + 16 * cc + n16] = g * Y[e];
+            Y[e] = 0.f;
+          }
+        }
+      }
+    }
+  for (int c = 0; c < C; c++)
+    if (sel[c] < 0)
+      for (int j = tid; j < DV; j += G::NT) valg[c * DV + j] = 0.f;
+  lds_barrier();                                 // the refit reuses rowh and the partials
+}
+
 // ------------------------------------------------------------------------
 // Tile body: MODE_STEP = decode step (unpack, gate, delta update, readout,
 // then refit_store); MODE_STORE = refit_store of a given fp32 tile.
@@ -537,6 +629,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
     if (rsub == 0) sm.gg[rho] = 1.f;
     if (cache) {
       if (A.S_in) {
+        if (A.C > 0) comp_extract<DK, DV>(sm, Y, false, cache, A.W, A.C, !PIV);
         if (tid == 0) *(int32_t*)cache = 0;                 // empty the window
       } else {                                              // pool creation: clear the whole cache
         for (uint64_t off = 16 * (uint64_t)tid; off < A.cache_stride; off += 16 * G::NT)
@@ -638,6 +731,10 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) vv[c] = A.v[x * DV + w * G::CPW + 16 * c + n16];
   const int t = *cntp;                         // tokens already in the window
+  // the base's compensators (a quantized tile): rows, read with the tile
+  const int nc = PIV ? 0 : A.C;
+  int cid = tid < nc ? ((const int32_t*)(cache + 192))[tid] : -1;
+  asm volatile("" : "+v"(cid));
   pin(a); pin(bb);
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) pin(vv[c]);
@@ -683,6 +780,14 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
         __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + off),
                                          (lptr_t)((uint8_t*)cst + W * DK * 4 + c * 1024), 16, 0, 0);
     }
+    // the compensator values [C][d_v] follow the W cached u rows, here and in memory
+    const int ncb = nc * DV * 4;
+    for (int c = wu; c < (ncb + 1023) / 1024; c += G::NW) {
+      const int off = c * 1024 + 16 * l;
+      if (off < ncb)
+        __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + W * DV * 4 + off),
+                                         (lptr_t)((uint8_t*)cst + W * (DK + DV) * 4 + c * 1024), 16, 0, 0);
+    }
   }
   // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t, 8 consecutive lanes per token
   constexpr int DP = (WMAX + G::NT / 8 - 1) / (G::NT / 8);    // passes
@@ -726,6 +831,11 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
       sm.cfq[s] = r * aq;
     }
   }
+  // compensator c is token t + c: G_t k_t[row], G_t q_t[row]
+  if (tid < nc) {
+    sm.cfk[t + tid] = cid >= 0 ? Gt * sm.kt[cid] : 0.f;
+    sm.cfq[t + tid] = cid >= 0 ? Gt * sm.qt[cid] : 0.f;
+  }
   __syncthreads();
   // cache terms: quad G sums its tokens s = 4i + G, then the four quads add up
   float pk[G::NCC], pq[G::NCC];
@@ -733,12 +843,15 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
   for (int c = 0; c < G::NCC; c++) pk[c] = pq[c] = 0.f;
 #pragma unroll
   for (int i = 0; i < UQ; i++) {
-    if (4 * i >= t) break;
+    if (4 * i >= t + nc) break;
     const int s = 4 * i + Gq;
-    const float fk = s < t ? sm.cfk[s] : 0.f, fq = s < t ? sm.cfq[s] : 0.f;
+    const bool on = s < t + nc;
+    const float fk = on ? sm.cfk[s] : 0.f, fq = on ? sm.cfq[s] : 0.f;
+    // staged row of token s: cached u (s < t), else compensator s - t
+    const int ur = !on ? 0 : (s < t ? s : W + s - t);
 #pragma unroll
     for (int c = 0; c < G::NCC; c++) {
-      const float u = s < t ? cst[W * DK + (s < t ? s : 0) * DV + w * G::CPW + 16 * c + n16] : 0.f;
+      const float u = on ? cst[W * DK + ur * DV + w * G::CPW + 16 * c + n16] : 0.f;
       pk[c] = __builtin_fmaf(fk, u, pk[c]);
       pq[c] = __builtin_fmaf(fq, u, pq[c]);
     }
@@ -780,8 +893,13 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   float* Kc = (float*)(cache + 256);
   float* Uc = Kc + (size_t)W * DK;
   float* kap = WSmem<DK, DV>::IN_PART ? sm.part : ws.kap;
-  // ns: tokens in the window (read by the caller), 1 <= ns <= W
+  // ns: tokens in the window (read by the caller), 1 <= ns <= W.  The base's
+  // compensators ride along as nc more tokens s = ns + c: k = e_row, G = 1
+  // relative to the window's start, u = the kept row (W + C <= 32)
   const float Gt = Gc[ns - 1];
+  const int nc = PIV ? 0 : A.C;
+  const int32_t* cidx = (const int32_t*)(cache + 192);
+  const float* cval = (const float*)(cache + 256 + 4 * (size_t)W * (DK + DV));
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
@@ -794,7 +912,8 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   for (int i = 0; i < UQ; i++)
 #pragma unroll
     for (int c = 0; c < G::NCC; c++)
-      uq[i][c] = 4 * i + Gq < ns ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16] : 0.f;
+      uq[i][c] = 4 * i + Gq < ns ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16]
+               : (4 * i + Gq < ns + nc ? cval[(size_t)(4 * i + Gq - ns) * DV + w * G::CPW + 16 * c + n16] : 0.f);
   const uint32_t sgr = PIV ? 0x3F80u : scl[rho];
   const float wgt = A.weights[(size_t)h * DK + rho];
   // kappa_s,i = k_s,i / (G_s sigma_i) for every token of the window, 4 rows per
@@ -825,6 +944,12 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
       *(f32x4*)&kap[s * DK + r0] = o4;
     }
   }
+  // compensator tokens: kappa_{ns+c, i} = [i = row_c] / sigma_i
+  for (int j = tid; j < nc * DK; j += G::NT) {
+    const int c = j / DK, i = j - c * DK;
+    const int rc = cidx[c];
+    kap[(ns + c) * DK + i] = i == rc ? 1.f / bf16f(scl[i]) : 0.f;
+  }
   __syncthreads();
   unpack<N>(raw, P);
   opaque(P);
@@ -844,9 +969,9 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
       // four rank-one terms per MFMA: lane quad G carries token 4i + G
 #pragma unroll
       for (int i = 0; i < UQ; i++) {
-        if (4 * i >= ns) break;
+        if (4 * i >= ns + nc) break;
         const int s = 4 * i + Gq;
-        const float kv = s < ns ? kap[s * DK + r0 + n16] : 0.f;
+        const float kv = s < ns + nc ? kap[s * DK + r0 + n16] : 0.f;
 #pragma unroll
         for (int c = 0; c < G::NCC; c++) C[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, uq[i][c], C[c], 0, 0, 0);
       }
@@ -859,6 +984,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
     }
   if (tid == 0) *cntp = 0;
   if constexpr (WSmem<DK, DV>::IN_PART) lds_barrier();     // kappa reads done before the partials
+  if (A.C > 0) comp_extract<DK, DV>(sm, Y, true, cache, W, A.C, !PIV);
   refit_store<DK, DV, N, false, true>(sm, Y, tile, wgt);
 }
 
@@ -2001,6 +2127,27 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) void k_fetch(KArgs A) {
   }
 }
 
+// Fetch in window mode: add each tile's compensator rows to D(base); thread j
+// owns column j of every compensator in turn (the zero state holds row 0 with
+// zero values in every slot).
+__global__ __launch_bounds__(128) void k_comp_add(KArgs A, int DK, int DV) {
+  const int T = A.n * A.H;
+  const int tau = (int)blockIdx.x;
+  if (tau >= T) return;
+  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int slot = A.slots[ci];
+  if ((unsigned)slot >= (unsigned)A.n_slots || A.head_bits[h] == 16) return;
+  const uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
+  const int32_t* idx = (const int32_t*)(cache + 192);
+  const float* val = (const float*)(cache + 256 + 4 * (size_t)A.W * (DK + DV));
+  float* S = A.S_out + (size_t)tau * DK * DV;
+  for (int j = threadIdx.x; j < DV; j += blockDim.x)
+    for (int c = 0; c < A.C; c++) {
+      const int r = idx[c];
+      if (r >= 0 && r < DK) S[(size_t)r * DV + j] += val[(size_t)c * DV + j];
+    }
+}
+
 __global__ void k_debug_rcp(float* out) {
   const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < 65536u) out[b] = rcp_bf16(bf16f(b));
@@ -2012,7 +2159,7 @@ __global__ void k_debug_rcp(float* out) {
 // Host side
 // ==========================================================================
 struct stq_pool {
-  int32_t n_slots, H, dk, dv, gate, unit, W;
+  int32_t n_slots, H, dk, dv, gate, unit, W, C;
   std::vector<int32_t> bits;            // [H] or [H][d_k]
   std::vector<uint32_t> head_off;
   uint64_t hdr, woff, roff, slot_bytes, slots_off, cache_off, cache_stride, total;
@@ -2035,6 +2182,7 @@ bool desc_ok(const stq_pool_desc* d) {
   if (d->gate_kind != STQ_GATE_HEAD && d->gate_kind != STQ_GATE_CHANNEL) return false;
   if (d->unit_kind != STQ_UNIT_HEAD && d->unit_kind != STQ_UNIT_ROW) return false;
   if (d->window < 0 || d->window > 32) return false;
+  if (d->n_comp < 0 || d->n_comp > 8 || (d->n_comp > 0 && (d->window == 0 || d->window + d->n_comp > 32))) return false;
   if (!d->unit_bits || !d->row_weight) return false;
   const int nb = d->unit_kind == STQ_UNIT_ROW ? d->n_heads * d->d_k : d->n_heads;
   for (int i = 0; i < nb; i++) {
@@ -2050,7 +2198,7 @@ bool desc_ok(const stq_pool_desc* d) {
 
 void layout(const stq_pool_desc* d, stq_pool* p) {
   p->n_slots = d->n_slots; p->H = d->n_heads; p->dk = d->d_k; p->dv = d->d_v;
-  p->gate = d->gate_kind; p->unit = d->unit_kind; p->W = d->window;
+  p->gate = d->gate_kind; p->unit = d->unit_kind; p->W = d->window; p->C = d->n_comp;
   const bool rows = p->unit == STQ_UNIT_ROW;
   p->bits.assign(d->unit_bits, d->unit_bits + (rows ? d->n_heads * d->d_k : d->n_heads));
   p->head_off.resize(d->n_heads);
@@ -2077,7 +2225,7 @@ void layout(const stq_pool_desc* d, stq_pool* p) {
   p->hdr = rows ? ru256(p->roff + 2ull * p->H * p->dk + 16ull * p->H) : p->roff;
   p->slots_off = p->hdr;
   p->cache_off = p->slots_off + (uint64_t)p->n_slots * p->slot_bytes;
-  p->cache_stride = p->W ? 256 + 4ull * p->W * (p->dk + p->dv) : 0;
+  p->cache_stride = p->W ? 256 + 4ull * p->W * (p->dk + p->dv) + 4ull * p->C * p->dv : 0;
   p->total = p->cache_off + (uint64_t)p->n_slots * p->H * p->cache_stride;
 }
 
@@ -2089,7 +2237,7 @@ KArgs base_args(const stq_pool* p, const int32_t* slots, int n) {
   memset(&A, 0, sizeof(A));
   A.pool = p->dev;
   A.slots = slots;
-  A.n = n; A.H = p->H; A.n_slots = p->n_slots; A.gate = p->gate; A.W = p->W;
+  A.n = n; A.H = p->H; A.n_slots = p->n_slots; A.gate = p->gate; A.W = p->W; A.C = p->C;
   A.slots_off = p->slots_off; A.slot_bytes = p->slot_bytes;
   A.cache_off = p->cache_off; A.cache_stride = p->cache_stride;
   A.head_bits = (const int32_t*)(p->dev + 64);
@@ -2152,7 +2300,7 @@ template <int DK, int DV>
 void launch_window(const KArgs& A, bool step, hipStream_t st) {
   if (step) {
     hipLaunchKernelGGL((k_window_read<DK, DV>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT),
-                       (size_t)A.W * (DK + DV) * 4, st, A);
+                       ((size_t)A.W * (DK + DV) + (size_t)A.C * DV) * 4, st, A);
     const unsigned T = (unsigned)A.n * (unsigned)A.H;
     hipLaunchKernelGGL((k_window_fold<DK, DV, true>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
   } else {
@@ -2223,7 +2371,7 @@ stq_status stq_pool_create(const stq_pool_desc* d, void* dev_buf, size_t bytes, 
   uint8_t* hb = p->header.data();
   put32(hb + 0, 0x31515453u);
   put32(hb + 4, p->n_slots); put32(hb + 8, p->H); put32(hb + 12, p->dk); put32(hb + 16, p->dv);
-  put32(hb + 20, p->gate); put32(hb + 24, p->unit); put32(hb + 28, p->W);
+  put32(hb + 20, p->gate); put32(hb + 24, p->unit); put32(hb + 28, (uint32_t)p->W | ((uint32_t)p->C << 16));
   put64(hb + 32, p->slot_bytes); put64(hb + 40, p->slots_off); put64(hb + 48, p->cache_off);
   put64(hb + 56, p->cache_stride);
   const bool rows = p->unit == STQ_UNIT_ROW;
@@ -2286,7 +2434,10 @@ stq_status stq_pool_fetch(const stq_pool* p, const int32_t* slots, int32_t n, fl
   KArgs A = base_args(p, slots, n);
   A.S_out = S;
   if (p->unit == STQ_UNIT_ROW) return dispatch<LRows<RMODE_FETCH>::T>(p, A, st);
-  return dispatch<LFetch<false>::T>(p, A, st);
+  s = dispatch<LFetch<false>::T>(p, A, st);
+  if (s != STQ_OK || p->W == 0 || p->C == 0) return s;
+  hipLaunchKernelGGL(k_comp_add, dim3((unsigned)n * p->H), dim3(128), 0, st, A, p->dk, p->dv);
+  return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
 }
 
 stq_status stq_requant_fixed_scales(stq_pool* p, const int32_t* slots, int32_t n, hipStream_t st) {

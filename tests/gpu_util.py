@@ -14,19 +14,19 @@ def say(*a):
 class Pair:
     """A GPU pool (through the C ABI) and the oracle's pool, same description."""
 
-    def __init__(self, orc, wl, n_slots=None, window=None):
+    def __init__(self, orc, wl, n_slots=None, window=None, n_comp=0):
         import torch
         import quantized_linear_attention_amd as stq
         self.stq, self.orc, self.wl = stq, orc, wl
         self.n_slots = wl.B if n_slots is None else n_slots
         W = wl.cfg.window if window is None else window
         self.desc = stq.make_desc(self.n_slots, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1),
-                                  wl.row_weight, wl.cfg.gate, wl.cfg.unit, W)
+                                  wl.row_weight, wl.cfg.gate, wl.cfg.unit, W, n_comp)
         nbytes = stq.stq_pool_bytes(self.desc)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.pool = stq.stq_pool_create(self.desc, self.buf)
         self.ref = orc.OraclePool(self.n_slots, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1),
-                                  wl.row_weight, wl.cfg.gate, wl.cfg.unit, W)
+                                  wl.row_weight, wl.cfg.gate, wl.cfg.unit, W, n_comp=n_comp)
         assert self.ref.nbytes == nbytes
 
     def image(self):

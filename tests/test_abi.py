@@ -57,9 +57,23 @@ def test_invalid_descriptors(stq):
     assert stq.stq_pool_bytes(stq.make_desc(**ok)) > 0
     bad = [dict(ok, n_slots=0), dict(ok, d_k=96), dict(ok, d_v=32), dict(ok, unit_bits=[6, 5]),
            dict(ok, row_weight=np.r_[np.ones(255), 0.0]), dict(ok, row_weight=np.r_[np.ones(255), np.nan]),
-           dict(ok, window=64), dict(ok, gate_kind=3)]
+           dict(ok, window=64), dict(ok, gate_kind=3),
+           dict(ok, n_comp=2), dict(ok, window=8, n_comp=9), dict(ok, window=30, n_comp=3),
+           dict(ok, window=8, n_comp=-1)]
     for b in bad:
         assert stq.stq_pool_bytes(stq.make_desc(**b)) == 0
+
+
+def test_compensator_cache_layout(stq, orc):
+    """Window caches grow by n_comp binary32 rows of d_v; the header keeps
+    W | n_comp << 16; sizes agree with the oracle's layout."""
+    base = dict(n_slots=3, n_heads=2, d_k=128, d_v=64, unit_bits=[6, 16], row_weight=np.ones(256), window=8)
+    n0 = stq.stq_pool_bytes(stq.make_desc(**base))
+    n4 = stq.stq_pool_bytes(stq.make_desc(**dict(base, n_comp=4)))
+    assert n4 - n0 == 3 * 2 * 4 * 4 * 64
+    ref = orc.OraclePool(3, 2, 128, 64, np.array([6, 16]), np.ones((2, 128)), window=8, n_comp=4)
+    assert ref.nbytes == n4
+    assert int(ref.img[28:32].view(np.uint32)[0]) == 8 | (4 << 16)
 
 
 def test_create_rejects_on_host(stq):

@@ -477,3 +477,108 @@ def test_window_flush(torch_cuda, orc):
     for s in (0, 2, 3, 5, 7):                                   # untouched slots keep their window
         assert _cache_view(ref, post, int(s), 0)[0] == 5
         np.testing.assert_array_equal(ref.tile_view(int(s), 0, post), ref.tile_view(int(s), 0, img))
+
+
+# ---- compensator tokens (window mode) ----
+
+def _planted_state(wl, slots, seed):
+    """Pool states with three outlier key rows per tile (x60, x40, x25)."""
+    rng = np.random.default_rng(seed)
+    S = wl.state(slots).copy()
+    for c in range(S.shape[0]):
+        for h in range(S.shape[1]):
+            for r, f in zip(rng.choice(wl.dk, 3, replace=False), (60.0, 40.0, 25.0)):
+                S[c, h, r] *= f
+    return S
+
+
+def _comp_pool(orc, W, C, B=12, n_slots=14):
+    wl = Workload("C5", B=B)
+    wl.bits = Workload("C2", H=wl.H).bits        # 4/6/8-bit heads and a binary16 pivot head
+    return wl, Pair(orc, wl, n_slots=n_slots, window=W, n_comp=C)
+
+
+def test_comp_store_fetch_bit_exact(torch_cuda, orc):
+    """Ingest with compensators: the C largest rows kept exactly, R of the
+    residual; pool image (tiles, scales, caches with the compensator rows and
+    values) bit-exact with the oracle's, and fetch adds the rows back."""
+    say("case compensators store/fetch")
+    import torch
+    wl, P = _comp_pool(orc, 8, 4)
+    slots = np.random.default_rng(11).permutation(P.n_slots)[:wl.B]
+    S = _planted_state(wl, slots, 5)
+    P.store(slots, S)
+    np.testing.assert_array_equal(P.image(), P.ref.img)
+    F = torch.empty((len(slots), wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    P.stq.stq_pool_fetch(P.pool, P.slots_t(slots), F)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(F.cpu().numpy(), P.ref.fetch(slots))
+
+
+@pytest.mark.parametrize("W,C,T", [(8, 3, 17), (4, 8, 9), (16, 4, 17)])
+def test_comp_window_teacher_forced(torch_cuda, orc, W, C, T):
+    """Window steps with compensator tokens riding the cache path: readout and
+    cached u every token, and at each fold the new compensator rows (same
+    rows; values to binary32 rounding) and the new base's codes to the bar."""
+    say("case compensators window", W, C, T)
+    wl, P = _comp_pool(orc, W, C)
+    slots = np.random.default_rng(12).permutation(P.n_slots)[:wl.B]
+    P.store(slots, _planted_state(wl, slots, 6))
+    agg = dict(mism=0, codes=0, maxd=0, scale_mism=0, scales=0, piv_bad=0, piv=0, piv_mism=0)
+    worst_o = worst_u = worst_c = 0.0
+    for t in range(T):
+        img = P.image()
+        ref = orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, window=W, image=img,
+                             n_comp=C)
+        q, k, v, a, b = wl.token(t, len(slots))
+        o = P.gpu_step(slots, q, k, v, a, b)
+        o_ref = ref.step(slots, q, k, v, a, b)
+        post = P.image()
+        worst_o = max(worst_o, readout_ok(o, o_ref))
+        for s in slots[:5]:
+            for h in range(wl.H):
+                cg, Gg, Kg, Ug, ig, vg = ref.cache_view(int(s), h, post)
+                cr, Gr, Kr, Ur, ir, vr = ref.cache_view(int(s), h)
+                assert cg == cr == (t + 1) % W
+                np.testing.assert_array_equal(Gg[:cg], Gr[:cr])
+                np.testing.assert_array_equal(Kg[:cg], Kr[:cr])
+                if cg:
+                    worst_u = max(worst_u, float(np.abs(Ug[:cg] - Ur[:cr]).max() / np.abs(Ur[:cr]).max()))
+                np.testing.assert_array_equal(ig, ir)
+                if (ir >= 0).any():
+                    worst_c = max(worst_c, float(np.abs(vg - vr).max() / np.abs(vr).max()))
+        if (t + 1) % W == 0:
+            r = compare_codes(orc, ref, post, ref.img, slots)
+            for key in agg:
+                agg[key] = max(agg[key], r[key]) if key == "maxd" else agg[key] + r[key]
+    say("  W=%d C=%d: readout %.3f, cache u %.2e, compensators %.2e, fold code mismatch %d of %d (max |dQ| %d)"
+        % (W, C, worst_o, worst_u, worst_c, agg["mism"], agg["codes"], agg["maxd"]))
+    assert worst_o <= 1.0
+    assert worst_u <= 1e-4
+    assert worst_c <= 1e-5
+    _assert_codes(agg)
+
+
+def test_comp_flush(torch_cuda, orc):
+    say("case compensators flush")
+    W, C = 16, 2
+    wl, P = _comp_pool(orc, W, C, B=8, n_slots=8)
+    slots = np.arange(8)
+    P.store(slots, _planted_state(wl, slots, 7))
+    for t in range(5):
+        P.gpu_step(slots, *wl.token(t, 8))
+    img = P.image()
+    ref = orc.OraclePool(8, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, window=W, image=img, n_comp=C)
+    part = np.array([0, 3, 5])
+    P.stq.stq_window_flush(P.pool, P.slots_t(part))
+    ref.window_flush(part)
+    post = P.image()
+    _assert_codes(compare_codes(orc, ref, post, ref.img, part))
+    for s in part:
+        for h in range(wl.H):
+            cg, _, _, _, ig, vg = ref.cache_view(int(s), h, post)
+            cr, _, _, _, ir, vr = ref.cache_view(int(s), h)
+            assert cg == cr == 0
+            np.testing.assert_array_equal(ig, ir)
+            if (ir >= 0).any():
+                assert np.abs(vg - vr).max() <= 1e-5 * np.abs(vr).max()
