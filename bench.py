@@ -45,7 +45,7 @@ def io_bytes(dk, dv, gate_per_row):
     return 4 * (2 * dk + dv) + 4 * (dk if gate_per_row else 1) + 4 + 4 * dv
 
 
-def algorithmic_bytes(wl, pos=0):
+def algorithmic_bytes(wl, pos=0, n_comp=0):
     """Bytes the method must move in one launch over all B x H tiles.
 
     Per-head and per-key-row modes: the packed state read and written once,
@@ -53,7 +53,10 @@ def algorithmic_bytes(wl, pos=0):
     `pos` (tokens already cached): the frozen base read, the pos cached
     (Gamma, k, u) entries read, the new entry and the count written, the
     inputs and readout, and at the window's last token the base written by
-    the fold.  Per-head metadata is excluded."""
+    the fold.  With n_comp compensator rows per tile a quantized tile's
+    readout also reads them (values and row indices), and the fold reads
+    and rewrites them (a binary16 pivot tile only has its empty slots
+    rewritten).  Per-head metadata is excluded."""
     c, H, dk, dv = wl.cfg, wl.H, wl.dk, wl.dv
     per_row = wl.bits.ndim == 2
     tiles = [tile_bytes(wl.bits[h], dk, dv) for h in range(H)]
@@ -62,7 +65,10 @@ def algorithmic_bytes(wl, pos=0):
         return wl.B * sum(2 * t + io for t in tiles)
     ent = 4 * (dk + dv + 1)
     fold = pos + 1 == c.window
-    per = [t + 8 + pos * ent + ent + io + (t if fold else 0) for t in tiles]
+    comp = n_comp * (4 * dv + 4)
+    quant = [np.atleast_1d(wl.bits[h])[0] != 16 for h in range(H)]
+    per = [t + 8 + pos * ent + ent + io + (t if fold else 0)
+           + (comp if q else 0) + ((2 * comp if q else comp) if fold else 0) for t, q in zip(tiles, quant)]
     assert not per_row
     return wl.B * sum(per)
 
@@ -128,6 +134,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--n-comp", type=int, default=0,
+                    help="window workloads: compensator rows per tile (0 = the workload as specified)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -165,7 +173,11 @@ def main():
         span = L * c.window
         K = max(span, -(-K // span) * span)
         Wu = -(-Wu // span) * span
-    desc = stq.make_desc(B, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window)
+    C = args.n_comp
+    if C and not c.window:
+        print("--n-comp needs a window workload", file=sys.stderr)
+        sys.exit(2)
+    desc = stq.make_desc(B, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window, C)
     nbytes = stq.stq_pool_bytes(desc)
     slots = torch.arange(B, dtype=torch.int32, device=dev)
     gen = torch.Generator(device=dev)
@@ -215,7 +227,7 @@ def main():
     if c.window:
         # launch s is token (Wu + s) // L of its pool: window position that mod W
         pos = [((Wu + s) // L) % c.window for s in range(K)]
-        bytes_step = float(np.mean([algorithmic_bytes(wl, p) for p in pos]))
+        bytes_step = float(np.mean([algorithmic_bytes(wl, p, C) for p in pos]))
     else:
         bytes_step = float(algorithmic_bytes(wl))
     achieved = bytes_step / (avg_ms * 1e-3) / 1e9
@@ -225,7 +237,7 @@ def main():
         import oracle
         oracle.build()
         ns = 32 if key != "C4" else 16             # slots per oracle call
-        P = oracle.OraclePool(ns, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window)
+        P = oracle.OraclePool(ns, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window, n_comp=C)
         sl = np.arange(ns)
         P.store(sl, wl.state(sl))
         tk = [wl.token(t, ns) for t in range(NTOK)]
@@ -240,7 +252,7 @@ def main():
                "sample": "%d calls x %d tiles of the same workload (B=%d slots, all %d heads%s), %.1f s"
                          % (calls, ns * H, ns, H, ", whole windows" if c.window else "", el)}
 
-    traffic = measured_traffic(key)
+    traffic = measured_traffic(key) if C == 0 else None
     line = {
         "metric": spec["metric"],
         "value": T * K / (total_ms * 1e-3),
@@ -250,7 +262,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": spec["dtype"],
         "data": "synthetic (seeded; pool states drawn on the GPU with the workload recipe)",
-        "config": {"workload": spec["workload"] + ", %d layer pools round-robin" % L,
+        "config": {"workload": spec["workload"] + (", %d compensator rows per tile" % C if C else "")
+                   + ", %d layer pools round-robin" % L,
                    "global_batch": B, "heads": H, "d_k": dk, "d_v": dv, "layers": L},
         "hbm_gbs": achieved, "hbm_frac": achieved / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -697,7 +697,7 @@ struct WRead {
 // One token of an open window: readout from the frozen base and the cache,
 // then the token's (G_t, k_t, u_t) appended.  A window that this token fills
 // (t + 1 = W) is left full for the fold kernel that runs next.
-template <int DK, int DV, int N>
+template <int DK, int DV, int N, bool COMP>
 __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, float* cst, uint8_t* tile,
                                             uint8_t* cache, size_t x) {
   using G = GeoM<DK, DV>;
@@ -732,9 +732,12 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
   for (int c = 0; c < G::NCC; c++) vv[c] = A.v[x * DV + w * G::CPW + 16 * c + n16];
   const int t = *cntp;                         // tokens already in the window
   // the base's compensators (a quantized tile): rows, read with the tile
-  const int nc = PIV ? 0 : A.C;
-  int cid = tid < nc ? ((const int32_t*)(cache + 192))[tid] : -1;
-  asm volatile("" : "+v"(cid));
+  const int nc = PIV || !COMP ? 0 : A.C;
+  int cid = -1;
+  if (COMP) {
+    cid = tid < nc ? ((const int32_t*)(cache + 192))[tid] : -1;
+    asm volatile("" : "+v"(cid));
+  }
   pin(a); pin(bb);
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) pin(vv[c]);
@@ -782,7 +785,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
     }
     // the compensator values [C][d_v] follow the W cached u rows, here and in memory
     const int ncb = nc * DV * 4;
-    for (int c = wu; c < (ncb + 1023) / 1024; c += G::NW) {
+    for (int c = wu; COMP && c < (ncb + 1023) / 1024; c += G::NW) {
       const int off = c * 1024 + 16 * l;
       if (off < ncb)
         __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + W * DV * 4 + off),
@@ -832,7 +835,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
     }
   }
   // compensator c is token t + c: G_t k_t[row], G_t q_t[row]
-  if (tid < nc) {
+  if (COMP && tid < nc) {
     sm.cfk[t + tid] = cid >= 0 ? Gt * sm.kt[cid] : 0.f;
     sm.cfq[t + tid] = cid >= 0 ? Gt * sm.qt[cid] : 0.f;
   }
@@ -875,7 +878,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
 
 // Fold of a tile's open window: S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T, refit,
 // window emptied.  Folds windows holding at least `need` tokens.
-template <int DK, int DV, int N>
+template <int DK, int DV, int N, bool COMP>
 __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK, DV>& ws, uint8_t* tile,
                                             uint8_t* cache, int h, int ns) {
   using G = GeoM<DK, DV>;
@@ -897,7 +900,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   // compensators ride along as nc more tokens s = ns + c: k = e_row, G = 1
   // relative to the window's start, u = the kept row (W + C <= 32)
   const float Gt = Gc[ns - 1];
-  const int nc = PIV ? 0 : A.C;
+  const int nc = PIV || !COMP ? 0 : A.C;
   const int32_t* cidx = (const int32_t*)(cache + 192);
   const float* cval = (const float*)(cache + 256 + 4 * (size_t)W * (DK + DV));
   uint32_t raw[2 * N];
@@ -945,7 +948,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
     }
   }
   // compensator tokens: kappa_{ns+c, i} = [i = row_c] / sigma_i
-  for (int j = tid; j < nc * DK; j += G::NT) {
+  for (int j = tid; COMP && j < nc * DK; j += G::NT) {
     const int c = j / DK, i = j - c * DK;
     const int rc = cidx[c];
     kap[(ns + c) * DK + i] = i == rc ? 1.f / bf16f(scl[i]) : 0.f;
@@ -984,12 +987,12 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
     }
   if (tid == 0) *cntp = 0;
   if constexpr (WSmem<DK, DV>::IN_PART) lds_barrier();     // kappa reads done before the partials
-  if (A.C > 0) comp_extract<DK, DV>(sm, Y, true, cache, W, A.C, !PIV);
+  if (COMP) comp_extract<DK, DV>(sm, Y, true, cache, W, A.C, !PIV);
   refit_store<DK, DV, N, false, true>(sm, Y, tile, wgt);
 }
 
 // readout and append of every tile of the call
-template <int DK, int DV>
+template <int DK, int DV, bool COMP>
 __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(7))) void k_window_read(KArgs A) {
   __shared__ WRead<DK, DV> sm;
   extern __shared__ float cst_[];               // W (d_k + d_v) floats: the staged window cache
@@ -1003,10 +1006,10 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
   const size_t x = (size_t)ci * A.H + h;
   switch (A.head_bits[h]) {
-    case 4: window_read<DK, DV, 4>(A, sm, cst_, tile, cache, x); break;
-    case 6: window_read<DK, DV, 6>(A, sm, cst_, tile, cache, x); break;
-    case 8: window_read<DK, DV, 8>(A, sm, cst_, tile, cache, x); break;
-    default: window_read<DK, DV, 16>(A, sm, cst_, tile, cache, x); break;
+    case 4: window_read<DK, DV, 4, COMP>(A, sm, cst_, tile, cache, x); break;
+    case 6: window_read<DK, DV, 6, COMP>(A, sm, cst_, tile, cache, x); break;
+    case 8: window_read<DK, DV, 8, COMP>(A, sm, cst_, tile, cache, x); break;
+    default: window_read<DK, DV, 16, COMP>(A, sm, cst_, tile, cache, x); break;
   }
 }
 
@@ -1015,7 +1018,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
 // empty launch costs one wave of small workgroups.  Flush: one tile per
 // workgroup, any non-empty window.
 constexpr int FPW = 16;
-template <int DK, int DV, bool STEP>
+template <int DK, int DV, bool STEP, bool COMP>
 __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_window_fold(KArgs A) {
   __shared__ SmemM<DK, DV> sm;
   __shared__ WSmem<DK, DV> ws;
@@ -1047,10 +1050,10 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     if (!first) __syncthreads();               // the previous fold's LDS reads are done
     first = false;
     switch (A.head_bits[h]) {
-      case 4: window_fold<DK, DV, 4>(A, sm, ws, tile, cache, h, ns); break;
-      case 6: window_fold<DK, DV, 6>(A, sm, ws, tile, cache, h, ns); break;
-      case 8: window_fold<DK, DV, 8>(A, sm, ws, tile, cache, h, ns); break;
-      default: window_fold<DK, DV, 16>(A, sm, ws, tile, cache, h, ns); break;
+      case 4: window_fold<DK, DV, 4, COMP>(A, sm, ws, tile, cache, h, ns); break;
+      case 6: window_fold<DK, DV, 6, COMP>(A, sm, ws, tile, cache, h, ns); break;
+      case 8: window_fold<DK, DV, 8, COMP>(A, sm, ws, tile, cache, h, ns); break;
+      default: window_fold<DK, DV, 16, COMP>(A, sm, ws, tile, cache, h, ns); break;
     }
   }
 }
@@ -2299,12 +2302,20 @@ stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st)
 template <int DK, int DV>
 void launch_window(const KArgs& A, bool step, hipStream_t st) {
   if (step) {
-    hipLaunchKernelGGL((k_window_read<DK, DV>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT),
-                       ((size_t)A.W * (DK + DV) + (size_t)A.C * DV) * 4, st, A);
+    const size_t lds = ((size_t)A.W * (DK + DV) + (size_t)A.C * DV) * 4;
+    if (A.C > 0)
+      hipLaunchKernelGGL((k_window_read<DK, DV, true>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), lds, st, A);
+    else
+      hipLaunchKernelGGL((k_window_read<DK, DV, false>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), lds, st, A);
     const unsigned T = (unsigned)A.n * (unsigned)A.H;
-    hipLaunchKernelGGL((k_window_fold<DK, DV, true>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    if (A.C > 0)
+      hipLaunchKernelGGL((k_window_fold<DK, DV, true, true>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    else
+      hipLaunchKernelGGL((k_window_fold<DK, DV, true, false>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
+  } else if (A.C > 0) {
+    hipLaunchKernelGGL((k_window_fold<DK, DV, false, true>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
   } else {
-    hipLaunchKernelGGL((k_window_fold<DK, DV, false>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    hipLaunchKernelGGL((k_window_fold<DK, DV, false, false>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
   }
 }
 stq_status dispatch_window(const stq_pool* p, const KArgs& A, bool step, hipStream_t st) {
