@@ -16,7 +16,8 @@
  *       approximate state), "STEPQuant 核心设计…" (dual-axis key-row fitting,
  *       lifetime-aware bits), "从状态压缩到高效服务…" (packed-state kernels).
  *  [P3] "线性注意力每生成一个token都要搬状态,LeapQuant…" (wink.run), techniques
- *       one and three: per-window quantization, residual row smoothing.
+ *       one, two and three: per-window quantization, compensator tokens
+ *       (outliers kept at high precision), residual row smoothing.
  *  [P4] "STEPQuant: estados recurrentes a «6 bit»…" (gpt-diffusion.com),
  *       "Las dos ideas" (bit units: head for GDN, key row for KDA; FP16
  *       pivots) and "Qué dice realmente el «6-bit»" (6 + 16/128 + 16/128 bits
@@ -143,12 +144,26 @@
  * (0, 1] whose product over W tokens stays >= 2^-126.  Smaller products are
  * outside the contract of window mode (the per-token mode accepts any gate).
  *
+ * COMPENSATOR TOKENS (n_comp = C > 0, window mode; [P3] technique two, the
+ * largest outliers kept at high precision as rank-one terms on the window's
+ * update path).  READING: whenever a quantized tile's base is written (ingest,
+ * fold, flush), the C key rows of largest absolute value of the binary32
+ * state being written (row absmax; ties to the lower row; all-zero rows never)
+ * are kept exactly, in binary32, as rank-one terms e_i u^T (u = that row), and
+ * R quantizes the residual, those rows set to zero.  The represented base is
+ * then S0 = D(tile) + sum_c e_{i_c} u_c^T; inside a window the compensators are
+ * gated with it and read out as cached tokens with k = e_{i_c} and G = 1:
+ *   u_t, o_t as above with S0 including them; the fold materialises S_W from
+ *   that S0 and takes its compensators anew.  A binary16 pivot head takes
+ *   none (its slots hold row -1 and zeros).  A fresh pool holds row 0 with
+ *   zero values in every slot, which adds nothing.
+ *
  * ------------------------------------------------------------------------
  * POOL BUFFER (one caller-owned device buffer of stq_pool_bytes() bytes):
  *  header (HDR bytes):
  *    [0,4) magic 0x31515453 ('STQ1')  [4,8) n_slots  [8,12) n_heads
  *    [12,16) d_k  [16,20) d_v  [20,24) gate_kind  [24,28) unit_kind
- *    [28,32) window  [32,40) slot_bytes  [40,48) slots_off  [48,56) cache_off
+ *    [28,32) window | n_comp << 16  [32,40) slot_bytes  [40,48) slots_off  [48,56) cache_off
  *    [56,64) cache_stride   (integers little-endian, u64 for the last four)
  *    [64, 64+4H)    int32 width of head h (0 for per-row units)
  *    [64+4H, 64+8H) uint32 byte offset of head h's tile inside a slot
@@ -162,9 +177,11 @@
  *    at + head_off[h]; head_off = running sum of tile strides.
  *  window caches (window > 0): cache_off = slots_off + n_slots*slot_bytes,
  *    tile (s,h) at cache_off + (s*H + h)*cache_stride, cache_stride =
- *    256 + 4*W*(d_k + d_v):  [0,4) int32 t = tokens in the open window,
- *    [4+4m) fp32 G of token m+1 (m < W), [256 + 4*d_k*m) fp32 k of token
- *    m+1, [256 + 4*W*d_k + 4*d_v*m) fp32 u of token m+1.
+ *    256 + 4*W*(d_k + d_v) + 4*C*d_v:  [0,4) int32 t = tokens in the open
+ *    window, [4+4m) fp32 G of token m+1 (m < W), [192 + 4c) int32 row of
+ *    compensator c, [256 + 4*d_k*m) fp32 k of token m+1,
+ *    [256 + 4*W*d_k + 4*d_v*m) fp32 u of token m+1,
+ *    [256 + 4*W*(d_k + d_v) + 4*d_v*c) fp32 values of compensator c.
  * Inputs of a call with n requests: q, k, v fp32 [n][H][d] (d = d_k for q, k,
  * d_v for v), a fp32 [n][H] (GDN) or [n][H][d_k] (KDA), b fp32 [n][H],
  * o fp32 [n][H][d_v]; request c of the call uses slot slots_dev[c].
@@ -238,7 +255,8 @@ stq_status stq_pool_store(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                           const float* S_dev, hipStream_t stream);
 
 /* Inspect: S_dev[c][h] := D(tile (slots_dev[c], h)) (in window mode the
- * frozen base only, without the open window's updates). */
+ * frozen base only, without the open window's updates; with compensator
+ * tokens the base includes them: D(tile) + sum_c e_{i_c} u_c^T). */
 stq_status stq_pool_fetch(const stq_pool* pool, const int32_t* slots_dev, int32_t n,
                           float* S_dev, hipStream_t stream);
 
