@@ -116,8 +116,10 @@ BENCH = {
            "workload": "KDA pool B=256 H=32 d_k=d_v=128, per-channel gate, key rows "
                        "{4b:30%, 6b:50%, 8b:19%, fp16:1%}",
            "dtype": "f32 update, per-key-row 4/6/8-bit + f16 state"},
-    "C5": {"layers": 2, "kernel": "k_window_read<128, 128> + k_window_fold<128, 128, true>",
-           "regex": "k_window_(read<128, 128>|fold<128, 128, true>)", "prof": "k_window_step",
+    "C5": {"layers": 2,
+           "kernel": "k_window_read<128, 128, false> + k_window_fold<128, 128, true, false>",
+           "regex": "k_window_(read<128, 128, false>|fold<128, 128, true, false>)",
+           "prof": "k_window_step",
            "metric": "request-head decode steps/s (B=512, H=32, d=128, 4-bit GDN, window W=16)",
            "workload": "windowed GDN pool B=512 H=32 d_k=d_v=128, all heads 4-bit, W=16 "
                        "(binary32 window caches, one fold per 16 tokens)",
@@ -270,7 +272,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "traffic_gbs": None if traffic is None else traffic / (avg_ms * 1e-3) / 1e9,
-                     "kernel": spec["kernel"], "bytes_per_launch": bytes_step,
+                     "kernel": spec["kernel"].replace("false>", "true>") if C else spec["kernel"],
+                     "bytes_per_launch": bytes_step,
                      "avg_launch_ms": avg_ms, "p10_ms": float(np.percentile(per, 10)),
                      "p90_ms": float(np.percentile(per, 90))},
         "cpu_baseline": cpu,
