@@ -54,6 +54,7 @@ def lib():
         L.orc_pool_requant_fixed.argtypes = D + [P, P, I]
         L.orc_decode_step.argtypes = D + [P, P, I, P, P, P, P, P, P]
         L.orc_window_flush.argtypes = D + [P, P, I]
+        L.orc_prefill.argtypes = D + [P, P, I, P, P, P, P, P, P, P, P]
         L.orc_update_f64.argtypes = [I, I, P, P, P, P, P, I, ctypes.c_double, P, P]
         L.orc_num_threads.restype = I
         L.orc_clip_events.restype = ctypes.c_long
@@ -226,6 +227,28 @@ class OraclePool:
         lib().orc_decode_step(*self._d(), _p(self.img), _p(slots), n, _p(q), _p(k), _p(v),
                               _p(a), _p(b), _p(o))
         return o
+
+    def prefill(self, slots, seq_start, q, k, v, a, b, final_state=False):
+        """Prefill ingest of token-major sequences (request c owns tokens
+        seq_start[c] .. seq_start[c+1]-1); returns the binary64 readouts
+        o [tok][H][d_v] and, if asked, the binary64 final states [n][H][d_k][d_v]."""
+        slots = _c(slots, np.int32)
+        n = slots.size
+        ss = _c(seq_start, np.int32)
+        assert ss.size == n + 1 and np.all(np.diff(ss) >= 0) and ss[0] >= 0
+        T = int(ss[-1])
+        q = _c(q, np.float32).reshape(T, self.H, self.dk)
+        k = _c(k, np.float32).reshape(T, self.H, self.dk)
+        v = _c(v, np.float32).reshape(T, self.H, self.dv)
+        a = _c(a, np.float32)
+        assert a.size == (T * self.H * self.dk if self.gate else T * self.H)
+        b = _c(b, np.float32).reshape(T, self.H)
+        o = np.zeros((T, self.H, self.dv), np.float64)
+        Sf = np.zeros((n, self.H, self.dk, self.dv), np.float64) if final_state else None
+        assert self.W == 0, "prefill: pools without a window"
+        lib().orc_prefill(*self._d(), _p(self.img), _p(slots), n, _p(ss), _p(q), _p(k), _p(v),
+                          _p(a), _p(b), _p(o), _p(Sf) if final_state else None)
+        return (o, Sf) if final_state else o
 
     def window_flush(self, slots):
         slots = _c(slots, np.int32)

@@ -29,7 +29,9 @@
  *    a token window, updates cached at high precision, readout from both,
  *    requantize with per-row smoothing at the window end; technique two:
  *    the largest outliers kept at high precision as rank-one terms that ride
- *    the window's update path (compensator tokens).
+ *    the window's update path (compensator tokens); section on decode cost
+ *    and state memory under prefix caching: a request's state is produced
+ *    from its prompt (prefill) and then held in the pool.
  */
 #include <math.h>
 #include <stdint.h>
@@ -798,6 +800,58 @@ void orc_decode_step(DESC_ARGS, uint8_t* img, const int32_t* slots, int n,
                   v + (size_t)x * dv, ax, b[x], o + (size_t)x * dv, &t);
       }
     }
+    scratch_free(&t);
+  }
+}
+
+/* Prefill ingest (LeapQuant post, section on decode cost and state memory
+ * under prefix caching: a request's state is produced once from its prompt
+ * and then lives in the pool).  For request c and head h, the per-token
+ * recurrence of orc_update_f64 runs in binary64 over the request's tokens
+ * ss[c] .. ss[c+1]-1 from D(tile), writing every token's readout; then
+ * tile := R(fl32(S_T)) once.  No tokens, or only identity tokens (every gate
+ * 1 and b = 0): the tile is left as it is.  Pools without a window only.
+ * Token-major inputs: q, k [tok][H][dk], v [tok][H][dv], a [tok][H] (KDA:
+ * [tok][H][dk]), b [tok][H]; o [tok][H][dv] in binary64.  S_fin (optional,
+ * NULL to skip): [n][H][dk][dv] binary64 final state before R. */
+void orc_prefill(DESC_ARGS, uint8_t* img, const int32_t* slots, int n, const int32_t* ss,
+                 const float* q, const float* k, const float* v, const float* a, const float* b,
+                 double* o, double* S_fin) {
+  MKDESC;
+  if (d.W) return;
+  #pragma omp parallel
+  {
+    scratch_t t = scratch_new(dk, dv);
+    double* S0 = (double*)malloc(8 * (size_t)dk * dv);
+    double* vec = (double*)malloc(8 * (size_t)(4 * dk + dv));
+    double *qd = vec, *kd = vec + dk, *vd = vec + 2 * dk, *ad = vec + 2 * dk + dv;
+    #pragma omp for schedule(dynamic, 1)
+    for (long x = 0; x < (long)n * H; x++) {
+      int c = (int)(x / H), h = (int)(x % H);
+      uint8_t* tp = tile_ptr(&d, img, slots[c], h);
+      int ng = gate ? dk : 1;
+      tile_decode(&d, h, tp, &t);
+      for (size_t e = 0; e < (size_t)dk * dv; e++) S0[e] = t.S[e];
+      int identity = 1;
+      for (int tok = ss[c]; tok < ss[c + 1]; tok++) {
+        size_t r = (size_t)tok * H + h;
+        for (int i = 0; i < dk; i++) { qd[i] = q[r * dk + i]; kd[i] = k[r * dk + i]; }
+        for (int j = 0; j < dv; j++) vd[j] = v[r * dv + j];
+        for (int i = 0; i < ng; i++) {
+          ad[i] = a[r * ng + i];
+          identity = identity && (a[r * ng + i] == 1.0f);
+        }
+        identity = identity && (b[r] == 0.0f);
+        orc_update_f64(dk, dv, S0, qd, kd, vd, ad, gate, (double)b[r], t.A, o + r * dv);
+        memcpy(S0, t.A, 8 * (size_t)dk * dv);
+      }
+      if (S_fin) memcpy(S_fin + (size_t)x * dk * dv, S0, 8 * (size_t)dk * dv);
+      if (identity) continue;   /* also covers a request with no tokens */
+      for (size_t e = 0; e < (size_t)dk * dv; e++) t.S[e] = (float)S0[e];
+      tile_encode(&d, h, t.S, row_w(&d, img, h), tp, &t);
+    }
+    free(S0);
+    free(vec);
     scratch_free(&t);
   }
 }

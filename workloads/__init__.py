@@ -155,8 +155,11 @@ class Workload:
     def token(self, t, n=None):
         """(q, k, v, a, b) for token t and the first n requests (default B)."""
         n = self.B if n is None else n
+        return self._io(self._rng(5, int(t)), n)
+
+    def _io(self, g, n):
+        """One draw of (q, k, v, a, b) with leading axis n, in a fixed order."""
         H, dk, dv = self.H, self.dk, self.dv
-        g = self._rng(5, int(t))
         q = g.standard_normal((n, H, dk))
         k = g.standard_normal((n, H, dk))
         v = g.standard_normal((n, H, dv))
@@ -180,3 +183,15 @@ class Workload:
             a = 2.0 ** (-1.0 / hp)
         f = np.float32
         return q.astype(f), k.astype(f), v.astype(f), a.astype(f), b.astype(f)
+
+    def prompts(self, lens):
+        """Token-major prompt inputs for requests of the given lengths:
+        (seq_start [n+1] int32, q, k, v [tok][H][d], a, b [tok][H] (per-channel
+        gate: a [tok][H][dk])); request c's tokens are drawn with the per-token
+        law from a stream that depends only on (seed, c)."""
+        lens = [int(x) for x in lens]
+        ss = np.zeros(len(lens) + 1, np.int32)
+        ss[1:] = np.cumsum(lens)
+        parts = [self._io(self._rng(6, c), L) for c, L in enumerate(lens)]
+        cat = [np.concatenate([p[i] for p in parts], axis=0) for i in range(5)]
+        return (ss,) + tuple(cat)
