@@ -273,6 +273,32 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                            const float* a_dev, const float* b_dev, float* o_dev,
                            hipStream_t stream);
 
+/* Prefill ingest ([P3] section on decode cost and state memory under prefix
+ * caching: a request's state is produced once from its prompt and then held
+ * in the pool).  For request c < n and every head h, runs the gated delta
+ * rule over the request's tokens seq_start_dev[c] .. seq_start_dev[c+1]-1,
+ * starting from D(tile (slots_dev[c], h)) (the all-zero state of a fresh
+ * slot), and
+ *   - writes the readout o_t = S_t^T q_t of every token, S_t the binary32
+ *     state after token t (no requantization between tokens), and
+ *   - writes the final state into the tile through R once.
+ * A request with no tokens, or whose tokens are all the identity (a = 1 and
+ * b = 0), leaves its tiles as they are (the decode step's identity rule).
+ * Layouts, token-major as a packed batch of prompts: q_dev, k_dev fp32
+ * [tok][H][d_k]; v_dev [tok][H][d_v]; a_dev, b_dev [tok][H]; o_dev
+ * [tok][H][d_v]; seq_start_dev int32 [n+1], non-decreasing (a decreasing
+ * pair is an empty request).  All device pointers, owned by the caller.
+ * The state runs in binary32 (products on the matrix cores in binary32):
+ * S_T and o differ from the exact recurrence by binary32 rounding only, so
+ * a final code can differ from R of the exact state where that state sits
+ * within rounding of a code boundary.  Requests must name distinct slots.
+ * Supported: per-head units, GDN gate, no window; otherwise
+ * STQ_ERR_UNSUPPORTED. */
+stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
+                       const int32_t* seq_start_dev, const float* q_dev, const float* k_dev,
+                       const float* v_dev, const float* a_dev, const float* b_dev, float* o_dev,
+                       hipStream_t stream);
+
 /* Window mode only: fold the open window of each listed slot into its base
  * now (S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T -> R), e.g. when a request ends
  * or before a snapshot.  A slot with an empty window is left unchanged.

@@ -51,6 +51,8 @@ def _load():
         getattr(L, name).argtypes = [P, P, I, P, St]
     L.stq_decode_step.restype = I
     L.stq_decode_step.argtypes = [P, P, I, P, P, P, P, P, P, St]
+    L.stq_prefill.restype = I
+    L.stq_prefill.argtypes = [P, P, I, P, P, P, P, P, P, P, St]
     for name in ("stq_window_flush", "stq_requant_fixed_scales"):
         getattr(L, name).restype = I
         getattr(L, name).argtypes = [P, P, I, St]
@@ -153,6 +155,16 @@ def stq_decode_step(pool, slots, q, k, v, a, b, o, stream=None):
     _check(_L.stq_decode_step(pool.handle, sp, n, _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"),
                               _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"), _stream(stream)),
            "stq_decode_step")
+
+
+def stq_prefill(pool, slots, seq_start, q, k, v, a, b, o, stream=None):
+    import torch
+    f = torch.float32
+    sp, n = _slots(slots)
+    _check(_L.stq_prefill(pool.handle, sp, n, _dev(seq_start, torch.int32, "seq_start"), _dev(q, f, "q"),
+                          _dev(k, f, "k"), _dev(v, f, "v"), _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"),
+                          _stream(stream)),
+           "stq_prefill")
 
 
 def stq_window_flush(pool, slots, stream=None):

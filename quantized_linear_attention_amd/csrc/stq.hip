@@ -44,6 +44,7 @@ struct KArgs {
   const float* S_in;         // store: [n][H][d_k][d_v] (nullptr: zeros)
   float* S_out;              // fetch
   uint32_t stage_bytes;      // per-key-row step: LDS bytes of the staged codes / row partials
+  const int32_t* seq_start;  // prefill: request c owns tokens seq_start[c] .. seq_start[c+1]-1
 };
 
 // LDS of the per-key-row ingest / decode / fixed-scale kernel
@@ -2151,6 +2152,308 @@ __global__ __launch_bounds__(128) void k_comp_add(KArgs A, int DK, int DV) {
     }
 }
 
+// ------------------------------------------------------------------------
+// Prefill ingest.  One workgroup per (request, head) runs the request's
+// prompt through the gated delta rule in chunks of PL tokens.  The state
+// stays in binary32 registers in the step kernel's lane layout (Y = S,
+// g = 1) and is written through refit_store once, after the last chunk.
+// Per chunk, with gamma_t = prod_{r<=t} a_r and rho[t][s] = prod_{s<r<=t} a_r
+// (products, never quotients, so zero gates stay exact):
+//   A[t][s] = b_t rho[t][s] k_t.k_s (s < t),   T = (I + A)^-1,
+//   Delta   = T diag(b) (V - diag(gamma) K S),
+//   O       = diag(gamma) Q S + tril(rho . Q K^T) Delta,
+//   S      <- gamma_{L-1} S + K^T diag(rho[L-1][:]) Delta,
+// the per-token recurrence regrouped by chunk (each token's correction is
+// solved from the ones before it through T).  Every product is a
+// v_mfma_f32_16x16x4_f32 (16 x 16 output blocks, 4 terms each); T comes
+// from forward substitution on one wave.  The state products take the
+// state straight from registers: the MFMA A operand of lane (G, n) for the
+// four rows 4G + i of a 16-row block is exactly the lane's Y element i.
+// ------------------------------------------------------------------------
+constexpr int PL = 32;           // tokens per chunk
+constexpr int PLP = PL + 4;      // LDS row stride of token-indexed rows
+
+template <int DK, int DV>
+struct PSmem {
+  float kc[PL][DK + 4];          // K, token-major
+  float qc[PL][DK + 4];
+  float vc[PL][DV + 4];
+  float kt[DK][PLP];             // K^T
+  float rhs[DV][PLP];            // diag(b) (V - diag(gamma) K S), transposed
+  float del[DV][PLP];            // Delta, transposed
+  float rt[PL][PLP];             // rho[t][s], 0 for s > t
+  float am[PL][PLP];             // A
+  float pm[PL][PLP];             // tril(rho . Q K^T)
+  float ti[PL][PLP];             // T
+  float ga[PL], gb[PL], gam[PL];
+};
+
+template <int DK, int DV>
+union PrefillSmem {
+  PSmem<DK, DV> p;
+  SmemM<DK, DV> m;
+};
+
+// Y := D(tile) in the lane layout (exact: sigma c Q has at most 24 bits)
+template <int DK, int DV, int N>
+__device__ __forceinline__ void decode_state(const uint8_t* tile, float* Y) {
+  using G = GeoM<DK, DV>;
+  constexpr int K = N / 2;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  const uint16_t* scl = (const uint16_t*)(tile + DK * DV * N / 8);
+  uint32_t raw[2 * N];
+  f16x2 P[32];
+#pragma unroll
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(tile + 16 * ((w * K + k) * 64 + l));
+  unpack<N>(raw, P);
+  float cc[G::NCC];
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) cc[c] = N == 16 ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
+#pragma unroll
+  for (int e = 0; e < 64; e++) {
+    const int b = e >> 3, t = e & 7, c = b / G::NRC;
+    const float qv = code_e<N>(P, e);
+    Y[e] = N == 16 ? qv : (bf16f(scl[erow(b % G::NRC, t, Gq)]) * cc[c]) * qv;
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int DK, int DV, int N>
+__device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>& sh, uint8_t* tile, int ci,
+                                             int h) {
+  using G = GeoM<DK, DV>;
+  PSmem<DK, DV>& ps = sh.p;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  const int tb0 = A.seq_start[ci], tb1 = A.seq_start[ci + 1];
+  if (tb1 <= tb0) return;                            // no tokens: the tile is left as it is
+  float Y[64];
+  decode_state<DK, DV, N>(tile, Y);
+  int moved = 0;                                     // some token is not the identity
+  const int col0 = w * G::CPW;
+  for (int t0 = tb0; t0 < tb1; t0 += PL) {
+    const int Lc = min(PL, tb1 - t0);
+    // ---- the chunk's inputs -> LDS (tokens past the end: k = q = v = 0, a = 1, b = 0)
+    for (int f = tid; f < PL * DK / 4; f += G::NT) {
+      const int t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = {0.f, 0.f, 0.f, 0.f};
+      if (t < Lc) {
+        const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
+        kk = *(const f32x4*)(A.k + r);
+        qq = *(const f32x4*)(A.q + r);
+      }
+      *(f32x4*)&ps.kc[t][d4] = kk;
+      *(f32x4*)&ps.qc[t][d4] = qq;
+#pragma unroll
+      for (int j = 0; j < 4; j++) ps.kt[d4 + j][t] = kk[j];
+    }
+    for (int f = tid; f < PL * DV / 4; f += G::NT) {
+      const int t = f / (DV / 4), d4 = 4 * (f % (DV / 4));
+      f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+      if (t < Lc) vv = *(const f32x4*)(A.v + ((size_t)(t0 + t) * A.H + h) * DV + d4);
+      *(f32x4*)&ps.vc[t][d4] = vv;
+    }
+    if (tid < PL) {
+      float av = 1.f, bv = 0.f;
+      if (tid < Lc) {
+        const size_t r = (size_t)(t0 + tid) * A.H + h;
+        av = A.a[r];
+        bv = A.b[r];
+      }
+      ps.ga[tid] = av;
+      ps.gb[tid] = bv;
+      moved |= (av != 1.f) | (bv != 0.f);
+    }
+    lds_barrier();
+    // ---- gate products
+    for (int p = tid; p < PL * PL; p += G::NT) {
+      const int t = p / PL, s = p % PL;
+      float r = 0.f;
+      if (s <= t) {
+        r = 1.f;
+        for (int u = s + 1; u <= t; u++) r *= ps.ga[u];
+      }
+      ps.rt[t][s] = r;
+    }
+    if (tid < PL) {
+      float g = 1.f;
+      for (int u = 0; u <= tid; u++) g *= ps.ga[u];
+      ps.gam[tid] = g;
+    }
+    // ---- S^T K^T and S^T Q^T: this wave's columns x the chunk's tokens
+    f32x4 ck[G::NCC][2], cq[G::NCC][2];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) ck[c][tb] = cq[c][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+        for (int tb = 0; tb < 2; tb++) {
+          const f32x4 kb = *(const f32x4*)&ps.kc[16 * tb + n16][32 * rc + 16 * hf + 4 * Gq];
+          const f32x4 qb = *(const f32x4*)&ps.qc[16 * tb + n16][32 * rc + 16 * hf + 4 * Gq];
+#pragma unroll
+          for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const float y = Y[8 * (c * G::NRC + rc) + 4 * hf + i];
+              ck[c][tb] = mfma4(y, kb[i], ck[c][tb]);
+              cq[c][tb] = mfma4(y, qb[i], cq[c][tb]);
+            }
+        }
+    // ---- K K^T and Q K^T on and below the diagonal: 6 blocks dealt to the waves
+    constexpr int NB = (6 + G::NW - 1) / G::NW;
+    f32x4 kq[NB];
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      const int bi = w + j * G::NW;
+      kq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (bi < 6) {
+        const int isq = bi >= 3, bb = bi % 3, tb = bb ? 1 : 0, sb = bb == 2 ? 1 : 0;
+        const float* xr = isq ? &ps.qc[16 * tb + n16][4 * Gq] : &ps.kc[16 * tb + n16][4 * Gq];
+        const float* kr = &ps.kc[16 * sb + n16][4 * Gq];
+#pragma unroll
+        for (int d0 = 0; d0 < DK; d0 += 16) {
+          const f32x4 xa = *(const f32x4*)(xr + d0), kb = *(const f32x4*)(kr + d0);
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) kq[j] = mfma4(xa[jj], kb[jj], kq[j]);
+        }
+      }
+    }
+    lds_barrier();
+    // ---- A and the readout mask (rows t = 16 tb + 4G + i, column s = 16 sb + n)
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      const int bi = w + j * G::NW;
+      if (bi < 6) {
+        const int isq = bi >= 3, bb = bi % 3, tb = bb ? 1 : 0, sb = bb == 2 ? 1 : 0;
+        const int s = 16 * sb + n16;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int t = 16 * tb + 4 * Gq + i;
+          const float r = ps.rt[t][s];
+          if (isq) ps.pm[t][s] = r * kq[j][i];                         // r = 0 above the diagonal
+          else ps.am[t][s] = s < t ? ps.gb[t] * (r * kq[j][i]) : 0.f;
+        }
+      }
+    }
+    // ---- right-hand side (columns j = col0 + 16 c + 4G + i, token t = 16 tb + n)
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) {
+        const int t = 16 * tb + n16, j0 = col0 + 16 * c + 4 * Gq;
+        const f32x4 vv = *(const f32x4*)&ps.vc[t][j0];
+        const float gt = ps.gam[t], bt = ps.gb[t];
+#pragma unroll
+        for (int i = 0; i < 4; i++) ps.rhs[j0 + i][t] = bt * (vv[i] - gt * ck[c][tb][i]);
+      }
+    lds_barrier();
+    // ---- T = (I + A)^-1 by forward substitution; lane s < PL owns column s
+    if (w == 0) {
+      float x[PL];
+#pragma unroll
+      for (int t = 0; t < PL; t++) {
+        float acc = t == l ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 0; r < t; r++) acc = __builtin_fmaf(-ps.am[t][r], x[r], acc);
+        x[t] = acc;
+      }
+      if (l < PL) {
+#pragma unroll
+        for (int t = 0; t < PL; t++) ps.ti[t][l] = x[t];
+      }
+    }
+    lds_barrier();
+    // ---- Delta = T rhs for this wave's columns (T is lower triangular)
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r0 = 0; r0 <= 16 * tb; r0 += 16) {
+          const f32x4 ta = *(const f32x4*)&ps.ti[16 * tb + n16][r0 + 4 * Gq];
+          const f32x4 rb = *(const f32x4*)&ps.rhs[col0 + 16 * c + n16][r0 + 4 * Gq];
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) d = mfma4(ta[jj], rb[jj], d);
+        }
+        *(f32x4*)&ps.del[col0 + 16 * c + n16][16 * tb + 4 * Gq] = d;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back only its own columns
+    // ---- readout O^T = S^T Q^T diag(gamma) + Delta^T tril(...)^T
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) {
+        const int t = 16 * tb + n16;
+        f32x4 o = cq[c][tb] * ps.gam[t];
+#pragma unroll
+        for (int s0 = 0; s0 <= 16 * tb; s0 += 16) {
+          const f32x4 da = *(const f32x4*)&ps.del[col0 + 16 * c + n16][s0 + 4 * Gq];
+          const f32x4 pb = *(const f32x4*)&ps.pm[t][s0 + 4 * Gq];
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) o = mfma4(da[jj], pb[jj], o);
+        }
+        if (t < Lc) *(f32x4*)(A.o + ((size_t)(t0 + t) * A.H + h) * DV + col0 + 16 * c + 4 * Gq) = o;
+      }
+    // ---- state: S <- gamma_{L-1} S + K^T diag(rho[L-1][:]) Delta
+    const float gl = ps.gam[PL - 1];
+    f32x4 wb[G::NCC][2];
+#pragma unroll
+    for (int sg = 0; sg < 2; sg++) {
+      const f32x4 rl = *(const f32x4*)&ps.rt[PL - 1][16 * sg + 4 * Gq];
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) wb[c][sg] = *(const f32x4*)&ps.del[col0 + 16 * c + n16][16 * sg + 4 * Gq] * rl;
+    }
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++) {
+        f32x4 ka[2];
+#pragma unroll
+        for (int sg = 0; sg < 2; sg++) ka[sg] = *(const f32x4*)&ps.kt[32 * rc + 16 * hf + n16][16 * sg + 4 * Gq];
+#pragma unroll
+        for (int c = 0; c < G::NCC; c++) {
+          const int e0 = 8 * (c * G::NRC + rc) + 4 * hf;
+          f32x4 C = {Y[e0] * gl, Y[e0 + 1] * gl, Y[e0 + 2] * gl, Y[e0 + 3] * gl};
+#pragma unroll
+          for (int sg = 0; sg < 2; sg++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) C = mfma4(ka[sg][jj], wb[c][sg][jj], C);
+#pragma unroll
+          for (int i = 0; i < 4; i++) Y[e0 + i] = C[i];
+        }
+      }
+    lds_barrier();
+  }
+  // identity tokens only: the tile is left as it is (the decode step's rule)
+  if (!__syncthreads_or(moved)) return;
+  const int rho = tid / G::TPR;
+  if (tid % G::TPR == 0) sh.m.gg[rho] = 1.f;
+  refit_store<DK, DV, N, true>(sh.m, Y, tile, A.weights[(size_t)h * DK + rho]);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) void k_prefill(KArgs A) {
+  __shared__ PrefillSmem<DK, DV> sh;
+  const int ci = (int)blockIdx.x / A.H, h = (int)blockIdx.x - ci * A.H;
+  if (ci >= A.n) return;
+  const int slot = ld_const(A.slots + ci);
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + ld_const(A.head_off + h);
+  switch (ld_const(A.head_bits + h)) {
+    case 4: prefill_body<DK, DV, 4>(A, sh, tile, ci, h); break;
+    case 6: prefill_body<DK, DV, 6>(A, sh, tile, ci, h); break;
+    case 8: prefill_body<DK, DV, 8>(A, sh, tile, ci, h); break;
+    default: prefill_body<DK, DV, 16>(A, sh, tile, ci, h); break;
+  }
+}
+
 __global__ void k_debug_rcp(float* out) {
   const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < 65536u) out[b] = rcp_bf16(bf16f(b));
@@ -2335,6 +2638,11 @@ struct LFetch {
   };
 };
 
+template <int DK, int DV>
+void launch_prefill(const KArgs& A, hipStream_t st) {
+  hipLaunchKernelGGL((k_prefill<DK, DV>), dim3((unsigned)A.n * (unsigned)A.H), dim3(GeoM<DK, DV>::NT), 0, st, A);
+}
+
 stq_status check_call(const stq_pool* p, const int32_t* slots, int32_t n) {
   if (!p) return STQ_ERR_ARG;
   if (n < 0 || n > p->n_slots) return STQ_ERR_ARG;
@@ -2473,6 +2781,23 @@ stq_status stq_decode_step(stq_pool* p, const int32_t* slots, int32_t n, const f
   return dispatch<LTile<MODE_STEP>::T>(p, A, st);
 }
 
+stq_status stq_prefill(stq_pool* p, const int32_t* slots, int32_t n, const int32_t* seq_start,
+                       const float* q, const float* k, const float* v, const float* a, const float* b,
+                       float* o, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (p->unit != STQ_UNIT_HEAD || p->gate != STQ_GATE_HEAD || p->W != 0) return STQ_ERR_UNSUPPORTED;
+  if (n == 0) return STQ_OK;
+  if (!seq_start || !q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
+  KArgs A = base_args(p, slots, n);
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  A.seq_start = seq_start;
+  if (p->dk == 128 && p->dv == 128) launch_prefill<128, 128>(A, st);
+  else if (p->dk == 64 && p->dv == 64) launch_prefill<64, 64>(A, st);
+  else if (p->dk == 64 && p->dv == 128) launch_prefill<64, 128>(A, st);
+  else launch_prefill<128, 64>(A, st);
+  return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
+}
 stq_status stq_window_flush(stq_pool* p, const int32_t* slots, int32_t n, hipStream_t st) {
   stq_status s = check_call(p, slots, n);
   if (s != STQ_OK) return s;

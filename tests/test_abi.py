@@ -91,3 +91,14 @@ def test_create_rejects_on_host(stq):
     r = lib.stq_pool_create(ctypes.byref(bad), ctypes.c_void_p(0x10000), ctypes.c_size_t(need), None, ctypes.byref(out))
     assert r == -1
     assert "LAYOUT" in stq.stq_status_str(-2)
+
+
+def test_prefill_rejects_on_host(stq):
+    """A null pool handle is refused before anything is enqueued."""
+    lib = ctypes.CDLL(stq.library_path())
+    lib.stq_prefill.restype = ctypes.c_int32
+    P = ctypes.c_void_p
+    lib.stq_prefill.argtypes = [P, P, ctypes.c_int32] + [P] * 7 + [P]
+    r = lib.stq_prefill(None, P(0x10000), 1, P(0x10000), P(0x10000), P(0x10000), P(0x10000),
+                        P(0x10000), P(0x10000), P(0x10000), None)
+    assert r == -1

@@ -1,0 +1,177 @@
+"""GPU parity of the prefill ingest (stq_prefill) against the oracle, through the C ABI.
+
+The oracle runs the per-token recurrence in binary64 and writes R(fl32(S_T));
+the kernel runs the chunkwise form in binary32 and writes R of its own binary32
+S_T.  Bar (written here):
+  - readout: |o - o_ref| <= 1e-3 (|o_ref| + 0.01 max|o_ref|) per (token, head);
+  - final state, every element: |D(tile) - S_T| <= half the tile's own code step
+    sigma_i c_j (binary16 pivots: half an ulp) + 1e-4 max|S_T| of the tile, i.e.
+    each code is the nearest one to the exact state up to the binary32 error of
+    the evaluation;
+  - codes against the oracle's R(fl32(S_T)): every difference <= 1 step and at
+    most 2% of the codes differ (only codes whose exact value lies within that
+    binary32 error of a rounding boundary, or rows whose bf16 scale does, can);
+  - empty requests and requests of identity tokens leave their tiles' bytes.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import Pair, compare_codes, readout_ok, say
+from workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+def _run(P, wl, slots, lens, edit=None):
+    import torch
+    dev = lambda x: torch.as_tensor(x, device="cuda")
+    ss, q, k, v, a, b = wl.prompts(lens)
+    if edit:
+        edit(ss, q, k, v, a, b)
+    pre = P.image()
+    ref = P.orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, image=pre)
+    T = int(ss[-1])
+    o = torch.full((T, wl.H, wl.dv), float("nan"), dtype=torch.float32, device="cuda")
+    P.stq.stq_prefill(P.pool, P.slots_t(slots), dev(ss), dev(q), dev(k), dev(v), dev(a), dev(b), o)
+    torch.cuda.synchronize()
+    o_ref, S_fin = ref.prefill(slots, ss, q, k, v, a, b, final_state=True)
+    return pre, P.image(), ref, o.cpu().numpy(), o_ref, S_fin, ss
+
+
+def _state_ok(orc, ref, img, slots, S_fin, moved):
+    """Worst ratio of |D(tile) - S_T| to its bound over the tiles that moved."""
+    D = orc.OraclePool(ref.n_slots, ref.H, ref.dk, ref.dv, ref.bits, ref.wt, image=img).fetch(slots)
+    worst = 0.0
+    for c, s in enumerate(slots):
+        if not moved[c]:
+            continue
+        for h in range(ref.H):
+            S = S_fin[c, h]
+            Q, sg, cs, nb = ref.decode_tile(int(s), h, img)
+            eps = 1e-4 * np.abs(S).max()
+            if int(ref.bits[h]) == 16:
+                half = np.abs(S) * 2.0 ** -11 + 2.0 ** -25
+            else:
+                sig = (sg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                col = (cs.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                half = 0.5 * sig[:, None] * col[None, :] * (1 + 1e-6)
+            err = np.abs(D[c, h].astype(np.float64) - S)
+            worst = max(worst, float((err / (half + eps)).max()))
+    return worst
+
+
+def _check(P, wl, slots, lens, pre, img, ref, o, o_ref, S_fin, ss, moved):
+    T = int(ss[-1])
+    if T:
+        r = readout_ok(o.reshape(T, 1, wl.H, wl.dv), o_ref.reshape(T, 1, wl.H, wl.dv))
+        say("  readout worst ratio %.3g" % r)
+        assert r <= 1.0
+    w = _state_ok(P.orc, ref, img, slots, S_fin, moved)
+    say("  state worst ratio %.3g" % w)
+    assert w <= 1.0
+    mv = [s for c, s in enumerate(slots) if moved[c]]
+    if mv:
+        res = compare_codes(P.orc, ref, img, ref.img, mv)
+        say("  codes", res)
+        assert res["maxd"] <= 1 and res["mism"] <= 0.02 * res["codes"]
+        assert res["piv_bad"] == 0
+    H = wl.H
+    for c, s in enumerate(slots):
+        if not moved[c]:
+            for h in range(H):
+                assert np.array_equal(ref.tile_view(int(s), h, img), ref.tile_view(int(s), h, pre)), (c, h)
+
+
+@pytest.mark.parametrize("key,H,lens", [
+    ("C2", 32, [33, 0, 1, 100, 32, 7]),          # GDN head mix with a binary16 head, ragged tails
+    ("C1", 2, [70, 3, 0, 64, 31]),               # 64 x 64 tiles, 8-bit
+    ("C3", 8, [257, 5]),                         # persistent outlier rows and columns, long prompt
+])
+def test_prefill_parity(torch_cuda, orc, key, H, lens):
+    say("case prefill", key, H, lens)
+    B = len(lens)
+    wl = Workload(key, B=B, H=H)
+    P = Pair(orc, wl, n_slots=B + 3)
+    slots = np.random.default_rng(B).permutation(B + 3)[:B].astype(np.int32)   # distinct slots
+    P.store(slots, wl.state(slots))
+    out = _run(P, wl, slots, lens)
+    _check(P, wl, slots, lens, *out, moved=[L > 0 for L in lens])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_prefill_other_shapes(torch_cuda, orc, dk, dv):
+    say("case prefill shape", dk, dv)
+    wl = Workload("C2", B=3, H=8)
+    wl.dk, wl.dv = dk, dv
+    wl.row_weight = wl.row_weight[:, :dk].copy()
+    wl.bits = np.array([4, 6, 8, 16, 6, 4, 8, 6], np.int32)
+    P = Pair(orc, wl)
+    slots = np.arange(3, dtype=np.int32)
+    rng = np.random.default_rng(dk * 3 + dv)
+    S = (rng.standard_normal((3, 8, dk, dv)) * np.exp(rng.normal(0, 1.5, (1, 8, dk, 1)))).astype(np.float32)
+    P.store(slots, S)
+    lens = [45, 16, 1]
+    out = _run(P, wl, slots, lens)
+    _check(P, wl, slots, lens, *out, moved=[True] * 3)
+
+
+def test_prefill_fresh_pool_and_identity(torch_cuda, orc):
+    """From the all-zero state of a fresh pool; one request of identity tokens only."""
+    say("case prefill fresh + identity")
+    wl = Workload("C2", B=3, H=32)
+    P = Pair(orc, wl)
+    slots = np.array([2, 0, 1], np.int32)
+    lens = [40, 12, 9]
+
+    def edit(ss, q, k, v, a, b):
+        a[ss[1]:ss[2]] = 1.0
+        b[ss[1]:ss[2]] = 0.0
+
+    out = _run(P, wl, slots, lens, edit)
+    _check(P, wl, slots, lens, *out, moved=[True, False, True])
+
+
+def test_prefill_zero_gates(torch_cuda, orc):
+    """Zero gates inside a chunk forget everything before them (no division by
+    a gate product anywhere); b = 0 tokens in between."""
+    say("case prefill zero gates")
+    wl = Workload("C2", B=2, H=8)
+    P = Pair(orc, wl)
+    slots = np.array([0, 1], np.int32)
+    P.store(slots, wl.state(slots))
+    lens = [50, 20]
+
+    def edit(ss, q, k, v, a, b):
+        a[3, :] = 0.0
+        a[40, :4] = 0.0
+        b[41:45, :] = 0.0
+        a[ss[1] + 19, :] = 0.0        # the last token of a request
+
+    out = _run(P, wl, slots, lens, edit)
+    _check(P, wl, slots, lens, *out, moved=[True, True])
+
+
+def test_prefill_unsupported_and_empty(torch_cuda, orc):
+    import torch
+    import quantized_linear_attention_amd as stq
+    say("case prefill unsupported pools, n = 0")
+    f = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda")
+    ss = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for key in ("C4", "C5"):                       # per-key-row units; window mode
+        wl = Workload(key, B=1, H=2)
+        P = Pair(orc, wl, n_slots=1)
+        with pytest.raises(stq.StqError) as e:
+            stq.stq_prefill(P.pool, P.slots_t([0]), ss, f(1), f(1), f(1), f(1), f(1), f(1))
+        assert e.value.status == -5
+    wl = Workload("C2", B=1, H=2)
+    P = Pair(orc, wl, n_slots=1)
+    pre = P.image()
+    stq.stq_prefill(P.pool, P.slots_t(np.zeros(0, np.int32)), ss, f(1), f(1), f(1), f(1), f(1), f(1))
+    assert np.array_equal(P.image(), pre)
