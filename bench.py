@@ -7,7 +7,9 @@ of one layer (stq_decode_step over all 16,384 (request, head) tiles).  L
 independent layer pools are stepped round-robin, as a model does, so the
 working set exceeds the 256 MB Infinity Cache and the timing is HBM-bound.
 `--workload C4` times the per-channel-gate, per-key-row-width pool (B=256)
-and `--workload C5` the windowed 4-bit pool (W=16, whole windows timed).
+and `--workload C5` the windowed 4-bit pool (W=16, whole windows timed);
+`--workload P3` times the prefill ingest of a batch of prompts into the C3
+pool (stq_prefill; one step = one call over all prompts).
 
 Prints one JSON line with throughput, the dominant kernel's roofline figure
 (algorithmic bytes / average kernel duration, from HIP events on the launch
@@ -130,9 +132,11 @@ BENCH = {
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", choices=sorted(BENCH), default="C3")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 512; P3: 8)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 32; P3: 2)")
+    ap.add_argument("--workload", choices=sorted(BENCH) + ["P3"], default="C3")
+    ap.add_argument("--prompt-len", type=int, default=1024, help="P3: tokens per prompt")
+    ap.add_argument("--prompts", type=int, default=64, help="P3: prompts per prefill call")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,6 +165,8 @@ def main():
     from workloads import Workload
 
     key = args.workload
+    if key == "P3":
+        return prefill_bench(args)
     spec = BENCH[key]
     dev = torch.device("cuda:0")
     wl = Workload(key)
@@ -168,7 +174,8 @@ def main():
     B, H, dk, dv = wl.B, wl.H, wl.dk, wl.dv
     T = B * H
     L = spec["layers"] if args.layers is None else args.layers
-    K, Wu = args.steps, args.warmup
+    K = 512 if args.steps is None else args.steps
+    Wu = 32 if args.warmup is None else args.warmup
     if c.window:
         # whole windows in the warm-up and in the timed region, so every pool
         # enters the timed region with an empty window
@@ -276,6 +283,113 @@ def main():
                      "bytes_per_launch": bytes_step,
                      "avg_launch_ms": avg_ms, "p10_ms": float(np.percentile(per, 10)),
                      "p90_ms": float(np.percentile(per, 90))},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+PL = 32                     # tokens per chunk of the prefill kernel
+MFMA_F32_PEAK = 157.3       # TFLOP/s, dense binary32 matrix cores
+
+
+def prefill_flops(n_tok, H, dk, dv):
+    """Matrix-core flops of the chunkwise prefill per token and head, counting
+    each product at the extent the chunk form needs: the three state products
+    (S^T K^T, S^T Q^T, K^T Delta) 6 dk dv, the strictly lower K K^T and the
+    lower Q K^T dk L, the two lower-triangular products with Delta 2 dv (L + 1)."""
+    return n_tok * H * (6 * dk * dv + dk * PL + 2 * dv * (PL + 1))
+
+
+def prefill_bench(args):
+    """P3: prefill ingest of a batch of prompts into the C3 pool (GDN head mix,
+    H = 32, d = 128): one step = one stq_prefill call over all prompts."""
+    import torch
+
+    import quantized_linear_attention_amd as stq
+    from workloads import Workload
+    dev = torch.device("cuda:0")
+    B, Lp = args.prompts, args.prompt_len
+    wl = Workload("C3", B=B)
+    c, H, dk, dv = wl.cfg, wl.H, wl.dk, wl.dv
+    T = B * Lp
+    desc = stq.make_desc(B, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, 0, 0)
+    buf = torch.empty(stq.stq_pool_bytes(desc), dtype=torch.uint8, device=dev)
+    pool = stq.stq_pool_create(desc, buf)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed * 100 + 77)
+    r_prof = torch.as_tensor(wl.r_prof, dtype=torch.float32, device=dev)
+    c_prof = torch.as_tensor(wl.c_prof, dtype=torch.float32, device=dev)
+    z = torch.randn((B, H, dk, dv), generator=gen, device=dev)
+    stq.stq_pool_store(pool, slots, (0.1 * z * r_prof[None, :, :, None] * c_prof[None, :, None, :]).contiguous())
+    del z
+    # prompts: the per-token law of workloads.Workload (normalised q, k with the
+    # persistent row profile, v with the column profile, GDN half-life gates), drawn on the GPU
+    rbar = r_prof / torch.exp(torch.log(r_prof).mean(dim=1, keepdim=True))
+    cbar = c_prof / torch.exp(torch.log(c_prof).mean(dim=1, keepdim=True))
+    q = torch.randn((T, H, dk), generator=gen, device=dev)
+    k = torch.randn((T, H, dk), generator=gen, device=dev) * torch.sqrt(rbar)[None]
+    v = torch.randn((T, H, dv), generator=gen, device=dev) * cbar[None]
+    q = (q / q.norm(dim=-1, keepdim=True)).contiguous()
+    k = (k / k.norm(dim=-1, keepdim=True)).contiguous()
+    b = (0.05 + 0.9 * torch.rand((T, H), generator=gen, device=dev)).contiguous()
+    hl = torch.as_tensor(wl.half_life, dtype=torch.float32, device=dev)
+    hp = hl[None, :] * torch.exp(0.1 * torch.randn((T, H), generator=gen, device=dev))
+    a = torch.clamp(2.0 ** (-1.0 / hp), 0.9, 0.9999).contiguous()
+    ss = torch.arange(0, T + 1, Lp, dtype=torch.int32, device=dev)
+    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    K = 8 if args.steps is None else args.steps
+    Wu = 2 if args.warmup is None else args.warmup
+    torch.cuda.synchronize()
+    for _ in range(Wu):
+        stq.stq_prefill(pool, slots, ss, q, k, v, a, b, o)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        ev[s].record()
+        stq.stq_prefill(pool, slots, ss, q, k, v, a, b, o)
+    ev[K].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(K)])
+    total_ms = float(ev[0].elapsed_time(ev[K]))
+    avg_ms = float(per.mean())
+    flops = prefill_flops(T, H, dk, dv)
+    tflops = flops / (avg_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build()
+        ns, Ls = 2, 64
+        P = oracle.OraclePool(ns, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, 0)
+        P.store(np.arange(ns), wl.state(np.arange(ns)))
+        pr = wl.prompts([Ls] * ns)
+        calls = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            P.prefill(np.arange(ns), *pr)
+            calls += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": calls * ns * Ls * H / el, "unit": "request-head prompt tokens/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "%d calls x %d prompts of %d tokens, all %d heads, %.1f s" % (calls, ns, Ls, H, el)}
+    line = {
+        "metric": "request-head prompt tokens/s (prefill ingest, B=%d prompts x %d tokens, H=32, d=128, "
+                  "6-bit nominal GDN pool)" % (B, Lp),
+        "value": T * H * K / (total_ms * 1e-3),
+        "unit": "request-head prompt tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wu, "ms_per_step": total_ms / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 state and products, 4/6/8-bit + f16 final state",
+        "data": "synthetic (seeded; states and prompts drawn on the GPU with the workload recipe)",
+        "config": {"workload": "prefill of %d prompts x %d tokens into the GDN pool H=32 d_k=d_v=128, heads "
+                               "{4b:9, 6b:16, 8b:6, fp16:1}" % (B, Lp),
+                   "global_batch": B, "prompt_len": Lp, "heads": H, "d_k": dk, "d_v": dv},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_F32_PEAK, "traffic": None, "kernel": "k_prefill<128, 128>",
+                     "flops_per_launch": flops, "avg_launch_ms": avg_ms,
+                     "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
+                     "hbm_gbs": (T * H * (4 * (2 * dk + 2 * dv) + 8)) / (avg_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
