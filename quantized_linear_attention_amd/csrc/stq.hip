@@ -2173,14 +2173,12 @@ __global__ __launch_bounds__(128) void k_comp_add(KArgs A, int DK, int DV) {
 constexpr int PL = 32;           // tokens per chunk
 constexpr int PLP = PL + 4;      // LDS row stride of token-indexed rows
 
+// 71 KB at d_k = d_v = 128: two workgroups per CU
 template <int DK, int DV>
 struct PSmem {
   float kc[PL][DK + 4];          // K, token-major
   float qc[PL][DK + 4];
-  float vc[PL][DV + 4];
-  float kt[DK][PLP];             // K^T
-  float rhs[DV][PLP];            // diag(b) (V - diag(gamma) K S), transposed
-  float del[DV][PLP];            // Delta, transposed
+  float rd[DV][PLP];             // diag(b) (V - diag(gamma) K S), transposed; then Delta in its place
   float rt[PL][PLP];             // rho[t][s], 0 for s > t
   float am[PL][PLP];             // A
   float pm[PL][PLP];             // tril(rho . Q K^T)
@@ -2221,21 +2219,28 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int DK, int DV, int N>
-__device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>& sh, uint8_t* tile, int ci,
-                                             int h) {
+// The chunks of one request, tokens tb0 .. tb1-1 (tb0 < tb1), on Y; returns
+// nonzero in some thread if some token is not the identity.
+template <int DK, int DV>
+__device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps, float* Y, int tb0, int tb1,
+                                              int h) {
   using G = GeoM<DK, DV>;
-  PSmem<DK, DV>& ps = sh.p;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
-  const int tb0 = A.seq_start[ci], tb1 = A.seq_start[ci + 1];
-  if (tb1 <= tb0) return;                            // no tokens: the tile is left as it is
-  float Y[64];
-  decode_state<DK, DV, N>(tile, Y);
-  int moved = 0;                                     // some token is not the identity
+  int moved = 0;
   const int col0 = w * G::CPW;
   for (int t0 = tb0; t0 < tb1; t0 += PL) {
     const int Lc = min(PL, tb1 - t0);
-    // ---- the chunk's inputs -> LDS (tokens past the end: k = q = v = 0, a = 1, b = 0)
+    // ---- this lane's V entries of the right-hand side (token 16 tb + n, columns col0 + 16 c + 4G ..)
+    f32x4 vr[G::NCC][2];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) {
+        const int t = 16 * tb + n16;
+        vr[c][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < Lc) vr[c][tb] = *(const f32x4*)(A.v + ((size_t)(t0 + t) * A.H + h) * DV + col0 + 16 * c + 4 * Gq);
+      }
+    // ---- K, Q of the chunk -> LDS (tokens past the end: k = q = 0, a = 1, b = 0)
     for (int f = tid; f < PL * DK / 4; f += G::NT) {
       const int t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = {0.f, 0.f, 0.f, 0.f};
@@ -2246,14 +2251,6 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
       }
       *(f32x4*)&ps.kc[t][d4] = kk;
       *(f32x4*)&ps.qc[t][d4] = qq;
-#pragma unroll
-      for (int j = 0; j < 4; j++) ps.kt[d4 + j][t] = kk[j];
-    }
-    for (int f = tid; f < PL * DV / 4; f += G::NT) {
-      const int t = f / (DV / 4), d4 = 4 * (f % (DV / 4));
-      f32x4 vv = {0.f, 0.f, 0.f, 0.f};
-      if (t < Lc) vv = *(const f32x4*)(A.v + ((size_t)(t0 + t) * A.H + h) * DV + d4);
-      *(f32x4*)&ps.vc[t][d4] = vv;
     }
     if (tid < PL) {
       float av = 1.f, bv = 0.f;
@@ -2267,20 +2264,21 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
       moved |= (av != 1.f) | (bv != 0.f);
     }
     lds_barrier();
-    // ---- gate products
-    for (int p = tid; p < PL * PL; p += G::NT) {
-      const int t = p / PL, s = p % PL;
-      float r = 0.f;
-      if (s <= t) {
-        r = 1.f;
-        for (int u = s + 1; u <= t; u++) r *= ps.ga[u];
-      }
-      ps.rt[t][s] = r;
-    }
+    // ---- gate products: thread s < PL runs down column s of rho, thread PL down gamma
     if (tid < PL) {
+      float r = 1.f;
+#pragma unroll
+      for (int t = 0; t < PL; t++) {
+        if (t > tid) r *= ps.ga[t];
+        ps.rt[t][tid] = t >= tid ? r : 0.f;
+      }
+    } else if (tid == PL) {
       float g = 1.f;
-      for (int u = 0; u <= tid; u++) g *= ps.ga[u];
-      ps.gam[tid] = g;
+#pragma unroll
+      for (int t = 0; t < PL; t++) {
+        g *= ps.ga[t];
+        ps.gam[t] = g;
+      }
     }
     // ---- S^T K^T and S^T Q^T: this wave's columns x the chunk's tokens
     f32x4 ck[G::NCC][2], cq[G::NCC][2];
@@ -2289,11 +2287,11 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
 #pragma unroll
       for (int tb = 0; tb < 2; tb++) ck[c][tb] = cq[c][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rc = 0; rc < G::NRC; rc++)
+    for (int tb = 0; tb < 2; tb++)
 #pragma unroll
-      for (int hf = 0; hf < 2; hf++)
+      for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
-        for (int tb = 0; tb < 2; tb++) {
+        for (int hf = 0; hf < 2; hf++) {
           const f32x4 kb = *(const f32x4*)&ps.kc[16 * tb + n16][32 * rc + 16 * hf + 4 * Gq];
           const f32x4 qb = *(const f32x4*)&ps.qc[16 * tb + n16][32 * rc + 16 * hf + 4 * Gq];
 #pragma unroll
@@ -2347,10 +2345,9 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
 #pragma unroll
       for (int tb = 0; tb < 2; tb++) {
         const int t = 16 * tb + n16, j0 = col0 + 16 * c + 4 * Gq;
-        const f32x4 vv = *(const f32x4*)&ps.vc[t][j0];
         const float gt = ps.gam[t], bt = ps.gb[t];
 #pragma unroll
-        for (int i = 0; i < 4; i++) ps.rhs[j0 + i][t] = bt * (vv[i] - gt * ck[c][tb][i]);
+        for (int i = 0; i < 4; i++) ps.rd[j0 + i][t] = bt * (vr[c][tb][i] - gt * ck[c][tb][i]);
       }
     lds_barrier();
     // ---- T = (I + A)^-1 by forward substitution; lane s < PL owns column s
@@ -2369,7 +2366,8 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
       }
     }
     lds_barrier();
-    // ---- Delta = T rhs for this wave's columns (T is lower triangular)
+    // ---- Delta = T rhs for this wave's columns (T is lower triangular), written over rhs
+    f32x4 dl[2][G::NCC];
 #pragma unroll
     for (int tb = 0; tb < 2; tb++)
 #pragma unroll
@@ -2378,13 +2376,19 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
 #pragma unroll
         for (int r0 = 0; r0 <= 16 * tb; r0 += 16) {
           const f32x4 ta = *(const f32x4*)&ps.ti[16 * tb + n16][r0 + 4 * Gq];
-          const f32x4 rb = *(const f32x4*)&ps.rhs[col0 + 16 * c + n16][r0 + 4 * Gq];
+          const f32x4 rb = *(const f32x4*)&ps.rd[col0 + 16 * c + n16][r0 + 4 * Gq];
 #pragma unroll
           for (int jj = 0; jj < 4; jj++) d = mfma4(ta[jj], rb[jj], d);
         }
-        *(f32x4*)&ps.del[col0 + 16 * c + n16][16 * tb + 4 * Gq] = d;
+        dl[tb][c] = d;
       }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back only its own columns
+    // the wave's own columns only: order its reads of rhs before its writes of Delta
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) *(f32x4*)&ps.rd[col0 + 16 * c + n16][16 * tb + 4 * Gq] = dl[tb][c];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // ---- readout O^T = S^T Q^T diag(gamma) + Delta^T tril(...)^T
 #pragma unroll
     for (int c = 0; c < G::NCC; c++)
@@ -2394,7 +2398,7 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
         f32x4 o = cq[c][tb] * ps.gam[t];
 #pragma unroll
         for (int s0 = 0; s0 <= 16 * tb; s0 += 16) {
-          const f32x4 da = *(const f32x4*)&ps.del[col0 + 16 * c + n16][s0 + 4 * Gq];
+          const f32x4 da = *(const f32x4*)&ps.rd[col0 + 16 * c + n16][s0 + 4 * Gq];
           const f32x4 pb = *(const f32x4*)&ps.pm[t][s0 + 4 * Gq];
 #pragma unroll
           for (int jj = 0; jj < 4; jj++) o = mfma4(da[jj], pb[jj], o);
@@ -2408,15 +2412,17 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
     for (int sg = 0; sg < 2; sg++) {
       const f32x4 rl = *(const f32x4*)&ps.rt[PL - 1][16 * sg + 4 * Gq];
 #pragma unroll
-      for (int c = 0; c < G::NCC; c++) wb[c][sg] = *(const f32x4*)&ps.del[col0 + 16 * c + n16][16 * sg + 4 * Gq] * rl;
+      for (int c = 0; c < G::NCC; c++) wb[c][sg] = *(const f32x4*)&ps.rd[col0 + 16 * c + n16][16 * sg + 4 * Gq] * rl;
     }
 #pragma unroll
     for (int rc = 0; rc < G::NRC; rc++)
 #pragma unroll
       for (int hf = 0; hf < 2; hf++) {
-        f32x4 ka[2];
+        float ka[2][4];                                 // K^T entries: row 32 rc + 16 hf + n, token 16 sg + 4G + jj
 #pragma unroll
-        for (int sg = 0; sg < 2; sg++) ka[sg] = *(const f32x4*)&ps.kt[32 * rc + 16 * hf + n16][16 * sg + 4 * Gq];
+        for (int sg = 0; sg < 2; sg++)
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) ka[sg][jj] = ps.kc[16 * sg + 4 * Gq + jj][32 * rc + 16 * hf + n16];
 #pragma unroll
         for (int c = 0; c < G::NCC; c++) {
           const int e0 = 8 * (c * G::NRC + rc) + 4 * hf;
@@ -2431,26 +2437,39 @@ __device__ __forceinline__ void prefill_body(const KArgs& A, PrefillSmem<DK, DV>
       }
     lds_barrier();
   }
-  // identity tokens only: the tile is left as it is (the decode step's rule)
-  if (!__syncthreads_or(moved)) return;
-  const int rho = tid / G::TPR;
-  if (tid % G::TPR == 0) sh.m.gg[rho] = 1.f;
-  refit_store<DK, DV, N, true>(sh.m, Y, tile, A.weights[(size_t)h * DK + rho]);
+  return moved;
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__((GeoM<DK, DV>::NT)) void k_prefill(KArgs A) {
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(KArgs A) {
   __shared__ PrefillSmem<DK, DV> sh;
   const int ci = (int)blockIdx.x / A.H, h = (int)blockIdx.x - ci * A.H;
   if (ci >= A.n) return;
   const int slot = ld_const(A.slots + ci);
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + ld_const(A.head_off + h);
-  switch (ld_const(A.head_bits + h)) {
-    case 4: prefill_body<DK, DV, 4>(A, sh, tile, ci, h); break;
-    case 6: prefill_body<DK, DV, 6>(A, sh, tile, ci, h); break;
-    case 8: prefill_body<DK, DV, 8>(A, sh, tile, ci, h); break;
-    default: prefill_body<DK, DV, 16>(A, sh, tile, ci, h); break;
+  const int tb0 = A.seq_start[ci], tb1 = A.seq_start[ci + 1];
+  if (tb1 <= tb0) return;                            // no tokens: the tile is left as it is
+  const int nb = ld_const(A.head_bits + h);
+  float Y[64];
+  switch (nb) {
+    case 4: decode_state<DK, DV, 4>(tile, Y); break;
+    case 6: decode_state<DK, DV, 6>(tile, Y); break;
+    case 8: decode_state<DK, DV, 8>(tile, Y); break;
+    default: decode_state<DK, DV, 16>(tile, Y); break;
+  }
+  const int moved = prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
+  // identity tokens only: the tile is left as it is (the decode step's rule)
+  if (!__syncthreads_or(moved)) return;
+  using G = GeoM<DK, DV>;
+  const int rho = (int)threadIdx.x / G::TPR;
+  if (threadIdx.x % G::TPR == 0) sh.m.gg[rho] = 1.f;
+  const float wgt = A.weights[(size_t)h * DK + rho];
+  switch (nb) {
+    case 4: refit_store<DK, DV, 4, true>(sh.m, Y, tile, wgt); break;
+    case 6: refit_store<DK, DV, 6, true>(sh.m, Y, tile, wgt); break;
+    case 8: refit_store<DK, DV, 8, true>(sh.m, Y, tile, wgt); break;
+    default: refit_store<DK, DV, 16, true>(sh.m, Y, tile, wgt); break;
   }
 }
 
