@@ -2350,20 +2350,36 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
         for (int i = 0; i < 4; i++) ps.rd[j0 + i][t] = bt * (vr[c][tb][i] - gt * ck[c][tb][i]);
       }
     lds_barrier();
-    // ---- T = (I + A)^-1 by forward substitution; lane s < PL owns column s
+    // ---- T = (I + A)^-1 in 16 x 16 blocks on wave 0: both diagonal blocks by
+    // forward substitution at once (lane l < 16 solves column l of the first,
+    // lane 16 + l column l of the second; lanes 32.. repeat them), then
+    // T21 = -T22 (A21 T11) on the matrix cores
     if (w == 0) {
-      float x[PL];
+      const int bo = l & 16, cl = l & 15;
+      float x[16];
 #pragma unroll
-      for (int t = 0; t < PL; t++) {
-        float acc = t == l ? 1.f : 0.f;
+      for (int t = 0; t < 16; t++) {
+        float acc = t == cl ? 1.f : 0.f;
 #pragma unroll
-        for (int r = 0; r < t; r++) acc = __builtin_fmaf(-ps.am[t][r], x[r], acc);
+        for (int r = 0; r < t; r++) acc = __builtin_fmaf(-ps.am[bo + t][bo + r], x[r], acc);
         x[t] = acc;
       }
       if (l < PL) {
 #pragma unroll
-        for (int t = 0; t < PL; t++) ps.ti[t][l] = x[t];
+        for (int t = 0; t < 16; t++) ps.ti[bo + t][bo + cl] = x[t];
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      f32x4 m = {0.f, 0.f, 0.f, 0.f};              // A21 T11: row 4G + i, column n
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 4) m = mfma4(ps.am[16 + n16][r0 + Gq], ps.ti[r0 + Gq][n16], m);
+#pragma unroll
+      for (int i = 0; i < 4; i++) ps.am[16 + 4 * Gq + i][n16] = m[i];   // over A21, read by this wave only
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      f32x4 tt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 4) tt = mfma4(ps.ti[16 + n16][16 + r0 + Gq], ps.am[16 + r0 + Gq][n16], tt);
+#pragma unroll
+      for (int i = 0; i < 4; i++) ps.ti[16 + 4 * Gq + i][n16] = -tt[i];
     }
     lds_barrier();
     // ---- Delta = T rhs for this wave's columns (T is lower triangular), written over rhs
