@@ -2228,40 +2228,55 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
   int moved = 0;
   const int col0 = w * G::CPW;
-  for (int t0 = tb0; t0 < tb1; t0 += PL) {
-    const int Lc = min(PL, tb1 - t0);
-    // ---- this lane's V entries of the right-hand side (token 16 tb + n, columns col0 + 16 c + 4G ..)
-    f32x4 vr[G::NCC][2];
+  // a chunk's inputs in registers: K, Q (KV float4 per thread), gates (threads < PL) and
+  // this lane's V entries of the right-hand side (token 16 tb + n, columns col0 + 16 c + 4G ..);
+  // tokens past the end: k = q = v = 0, a = 1, b = 0.  Read for the next chunk while
+  // this one's last products run.
+  constexpr int KV = PL * DK / 4 / G::NT;
+  static_assert(KV * 4 * G::NT == PL * DK, "chunk rows");
+  f32x4 kn[KV], qn[KV], vr[G::NCC][2];
+  float an, bn;
+  auto fetch = [&](int t0, int n) {
+#pragma unroll
+    for (int u = 0; u < KV; u++) {
+      const int f = tid + u * G::NT, t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
+      kn[u] = qn[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < n) {
+        const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
+        kn[u] = *(const f32x4*)(A.k + r);
+        qn[u] = *(const f32x4*)(A.q + r);
+      }
+    }
+    an = 1.f;
+    bn = 0.f;
+    if (tid < n) {
+      const size_t r = (size_t)(t0 + tid) * A.H + h;
+      an = A.a[r];
+      bn = A.b[r];
+    }
 #pragma unroll
     for (int c = 0; c < G::NCC; c++)
 #pragma unroll
       for (int tb = 0; tb < 2; tb++) {
         const int t = 16 * tb + n16;
         vr[c][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (t < Lc) vr[c][tb] = *(const f32x4*)(A.v + ((size_t)(t0 + t) * A.H + h) * DV + col0 + 16 * c + 4 * Gq);
+        if (t < n) vr[c][tb] = *(const f32x4*)(A.v + ((size_t)(t0 + t) * A.H + h) * DV + col0 + 16 * c + 4 * Gq);
       }
-    // ---- K, Q of the chunk -> LDS (tokens past the end: k = q = 0, a = 1, b = 0)
-    for (int f = tid; f < PL * DK / 4; f += G::NT) {
-      const int t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
-      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = {0.f, 0.f, 0.f, 0.f};
-      if (t < Lc) {
-        const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
-        kk = *(const f32x4*)(A.k + r);
-        qq = *(const f32x4*)(A.q + r);
-      }
-      *(f32x4*)&ps.kc[t][d4] = kk;
-      *(f32x4*)&ps.qc[t][d4] = qq;
+  };
+  fetch(tb0, min(PL, tb1 - tb0));
+  for (int t0 = tb0; t0 < tb1; t0 += PL) {
+    const int Lc = min(PL, tb1 - t0);
+    // ---- the chunk's K, Q and gates from registers to LDS
+#pragma unroll
+    for (int u = 0; u < KV; u++) {
+      const int f = tid + u * G::NT, t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
+      *(f32x4*)&ps.kc[t][d4] = kn[u];
+      *(f32x4*)&ps.qc[t][d4] = qn[u];
     }
     if (tid < PL) {
-      float av = 1.f, bv = 0.f;
-      if (tid < Lc) {
-        const size_t r = (size_t)(t0 + tid) * A.H + h;
-        av = A.a[r];
-        bv = A.b[r];
-      }
-      ps.ga[tid] = av;
-      ps.gb[tid] = bv;
-      moved |= (av != 1.f) | (bv != 0.f);
+      ps.ga[tid] = an;
+      ps.gb[tid] = bn;
+      moved |= (an != 1.f) | (bn != 0.f);
     }
     lds_barrier();
     // ---- gate products: thread s < PL runs down column s of rho, thread PL down gamma
@@ -2451,6 +2466,7 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
           for (int i = 0; i < 4; i++) Y[e0 + i] = C[i];
         }
       }
+    if (t0 + PL < tb1) fetch(t0 + PL, min(PL, tb1 - t0 - PL));
     lds_barrier();
   }
   return moved;
