@@ -306,6 +306,28 @@ stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
 stq_status stq_window_flush(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                             hipStream_t stream);
 
+/* Lifetime-aware bit allocation (host only; the offline step that produces a
+ * pool's unit_bits).  [P1] "STEPQuant 核心设计…" (time axis: widths from each
+ * unit's error per width and its lifetime, under a fixed budget); [P5] "O que
+ * os autores propõem" (lifetime-weighted distortion minimised under a fixed
+ * bit budget, riskiest units kept in binary16 as pivots) and "Como funciona"
+ * (the lifetime weight decays about exponentially); [P4] "Qué dice realmente
+ * el «6-bit»" (pivots counted apart from the nominal budget).  READING:
+ *   w_u = sum_{t>=0} 2^(-t/h_u) = 1/(1 - 2^(-1/h_u)), h_u = half_life[u] > 0;
+ *   the n_pivots units of largest w_u err[u][2] (ties to the lower index)
+ *   become binary16 pivots (bits 16, no distortion);
+ *   the other m units take b_u in {4, 6, 8} minimising
+ *   sum_u w_u err[u][(b_u - 4)/2] subject to sum_u (b_u - 4)/2 <=
+ *   floor((budget_bits - 4) m / 2) (binary64), i.e. mean width <= budget_bits.
+ * err: host [n][3] distortion per step at 4, 6, 8 bits (finite, >= 0);
+ * bits_out: host [n]; objective_out (may be NULL): the minimised sum.  Exact
+ * (dynamic programming) while m * (budget steps + 1) <= 2^26; larger inputs
+ * take greedy upgrades along each unit's lower convex hull (within one
+ * unit's gain of the optimum).  STQ_ERR_ARG on n < 1, n_pivots outside
+ * [0, n], budget_bits < 4, a non-positive half-life or a negative error. */
+stq_status stq_allocate_bits(int32_t n, const double* err, const double* half_life, int32_t n_pivots,
+                             double budget_bits, int32_t* bits_out, double* objective_out);
+
 /* Test export (exact invariant "fixed-scale round trip"): requantize each
  * listed tile's own decoded state against its STORED scales,
  *   Q'_ij = round-half-even(fl(S^_ij * fl(1/sigma_i)) * fl(1/c_j)),

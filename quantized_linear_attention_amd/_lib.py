@@ -52,6 +52,8 @@ def _load():
     L.stq_decode_step.restype = I
     L.stq_decode_step.argtypes = [P, P, I, P, P, P, P, P, P, St]
     L.stq_prefill.restype = I
+    L.stq_allocate_bits.restype = I
+    L.stq_allocate_bits.argtypes = [I, P, P, I, ctypes.c_double, P, P]
     L.stq_prefill.argtypes = [P, P, I, P, P, P, P, P, P, P, St]
     for name in ("stq_window_flush", "stq_requant_fixed_scales"):
         getattr(L, name).restype = I
@@ -165,6 +167,22 @@ def stq_prefill(pool, slots, seq_start, q, k, v, a, b, o, stream=None):
                           _dev(k, f, "k"), _dev(v, f, "v"), _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"),
                           _stream(stream)),
            "stq_prefill")
+
+
+def stq_allocate_bits(err, half_life, n_pivots, budget_bits):
+    """Host numpy arrays: err [n][3] (4, 6, 8 bits), half_life [n]; returns (bits [n] int32, objective)."""
+    import numpy as np
+    e = np.ascontiguousarray(err, np.float64)
+    hl = np.ascontiguousarray(half_life, np.float64)
+    n = hl.size
+    if e.shape != (n, 3):
+        raise StqError(-1, "err must be [n][3]")
+    bits = np.zeros(n, np.int32)
+    obj = ctypes.c_double(0.0)
+    _check(_L.stq_allocate_bits(n, e.ctypes.data_as(ctypes.c_void_p), hl.ctypes.data_as(ctypes.c_void_p),
+                                int(n_pivots), float(budget_bits), bits.ctypes.data_as(ctypes.c_void_p),
+                                ctypes.byref(obj)), "stq_allocate_bits")
+    return bits, obj.value
 
 
 def stq_window_flush(pool, slots, stream=None):

@@ -5,7 +5,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = [os.path.join(PKG, "csrc", "stq.hip")]
+SRC = [os.path.join(PKG, "csrc", "stq.hip"), os.path.join(PKG, "csrc", "alloc.cpp")]
 DEPS = SRC + [os.path.join(PKG, "csrc", "stq_device.h"), os.path.join(ROOT, "include", "stq.h")]
 LIB = os.path.join(PKG, "libstq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
