@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n-comp", type=int, default=0,
                     help="window workloads: compensator rows per tile (0 = the workload as specified)")
+    ap.add_argument("--split", action="store_true",
+                    help="C3: time the step split into readout and commit, the commit on a second stream")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -211,6 +213,11 @@ def main():
         toks.append([torch.as_tensor(x, device=dev) for x in (q, k, v, a, b)])
     o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    if args.split:
+        if c.window or c.unit:
+            print("--split: per-head pools without a window (C1-C3)", file=sys.stderr)
+            sys.exit(2)
+        return split_timing(stq, torch, pools, slots, toks, o, L, K, Wu, wl, spec)
 
     def step(s):
         q, k, v, a, b = toks[(s // L) % NTOK]
@@ -284,6 +291,74 @@ def main():
                      "avg_launch_ms": avg_ms, "p10_ms": float(np.percentile(per, 10)),
                      "p90_ms": float(np.percentile(per, 90))},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def split_timing(stq, torch, pools, slots, toks, o, L, K, Wu, wl, spec):
+    """The decode step as readout (stream 1) + commit (stream 2, after the
+    readout of the same layer; the next readout of a layer waits for its
+    commit), layers round-robin as in the fused timing."""
+    B, H, dk, dv = wl.B, wl.H, wl.dk, wl.dv
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    done = [None] * L
+    rt, ct = [], []
+
+    def step(s, timed):
+        lay = s % L
+        q, k, v, a, b = toks[(s // L) % len(toks)]
+        if done[lay] is not None:
+            sa.wait_event(done[lay])
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(sa)
+        stq.stq_decode_readout(pools[lay], slots, q, k, v, a, b, o, stream=sa)
+        e[1].record(sa)
+        sb.wait_event(e[1])
+        e[2].record(sb)
+        stq.stq_decode_commit(pools[lay], slots, q, k, v, a, b, stream=sb)
+        e[3].record(sb)
+        done[lay] = e[3]
+        if timed:
+            rt.append((e[0], e[1]))
+            ct.append((e[2], e[3]))
+
+    for s in range(Wu):
+        step(s, False)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(sa)
+    sb.wait_event(start)
+    for s in range(K):
+        step(Wu + s, True)
+    for d in done:
+        sa.wait_event(d)
+    stop.record(sa)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    r_ms = float(np.mean([x.elapsed_time(y) for x, y in rt]))
+    c_ms = float(np.mean([x.elapsed_time(y) for x, y in ct]))
+    T = B * H
+    state = B * sum(tile_bytes(wl.bits[h], dk, dv) for h in range(H))
+    inputs = T * 4 * (2 * dk + dv + 2)
+    r_bytes, c_bytes = state + inputs + T * 4 * dv, 2 * state + inputs
+    achieved = c_bytes / (c_ms * 1e-3) / 1e9
+    line = {
+        "metric": spec["metric"],
+        "value": T * K / (total_ms * 1e-3),
+        "unit": "request-head steps/s",
+        "n_gpus": 1, "steps": K, "warmup": Wu, "ms_per_step": total_ms / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec["dtype"],
+        "data": "synthetic (seeded; pool states drawn on the GPU with the workload recipe)",
+        "config": {"workload": spec["workload"] + ", %d layer pools round-robin; step split into readout "
+                   "(stream 1) and commit (stream 2)" % L,
+                   "global_batch": B, "heads": H, "d_k": dk, "d_v": dv, "layers": L},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_tile<128, 128, 3> (commit)",
+                     "bytes_per_launch": c_bytes, "avg_launch_ms": c_ms},
+        "split": {"readout_ms": r_ms, "readout_bytes": r_bytes,
+                  "readout_gbs": r_bytes / (r_ms * 1e-3) / 1e9, "commit_ms": c_ms, "commit_bytes": c_bytes},
+        "cpu_baseline": None,
     }
     print(json.dumps(line))
 

@@ -299,6 +299,26 @@ stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                        const float* v_dev, const float* a_dev, const float* b_dev, float* o_dev,
                        hipStream_t stream);
 
+/* The decode step split in two, for overlapped writeback ([P4] "Las dos
+ * ideas": the pages' serving system writes back on a separate stream so that
+ * the state updates overlap the model's other work).  stq_decode_readout
+ * writes o exactly as stq_decode_step would and leaves the pool untouched;
+ * stq_decode_commit then advances the states exactly as stq_decode_step
+ * would (same bytes), writing no o.  Same inputs, same layouts and range
+ * contract as stq_decode_step.  The commit rewrites the tiles the readout
+ * reads: it must be ordered after the readout of the same slots (same
+ * stream, or an event), and the next readout of those slots after the
+ * commit.  The pair reads each tile twice (one read more than the fused
+ * step): it shortens the time until o is available, not the bytes moved.
+ * Per-head units without a window only; otherwise STQ_ERR_UNSUPPORTED. */
+stq_status stq_decode_readout(stq_pool* pool, const int32_t* slots_dev, int32_t n,
+                              const float* q_dev, const float* k_dev, const float* v_dev,
+                              const float* a_dev, const float* b_dev, float* o_dev,
+                              hipStream_t stream);
+stq_status stq_decode_commit(stq_pool* pool, const int32_t* slots_dev, int32_t n,
+                             const float* q_dev, const float* k_dev, const float* v_dev,
+                             const float* a_dev, const float* b_dev, hipStream_t stream);
+
 /* Window mode only: fold the open window of each listed slot into its base
  * now (S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T -> R), e.g. when a request ends
  * or before a snapshot.  A slot with an empty window is left unchanged.

@@ -52,6 +52,10 @@ def _load():
     L.stq_decode_step.restype = I
     L.stq_decode_step.argtypes = [P, P, I, P, P, P, P, P, P, St]
     L.stq_prefill.restype = I
+    L.stq_decode_readout.restype = I
+    L.stq_decode_readout.argtypes = [P, P, I, P, P, P, P, P, P, St]
+    L.stq_decode_commit.restype = I
+    L.stq_decode_commit.argtypes = [P, P, I, P, P, P, P, P, St]
     L.stq_allocate_bits.restype = I
     L.stq_allocate_bits.argtypes = [I, P, P, I, ctypes.c_double, P, P]
     L.stq_prefill.argtypes = [P, P, I, P, P, P, P, P, P, P, St]
@@ -183,6 +187,24 @@ def stq_allocate_bits(err, half_life, n_pivots, budget_bits):
                                 int(n_pivots), float(budget_bits), bits.ctypes.data_as(ctypes.c_void_p),
                                 ctypes.byref(obj)), "stq_allocate_bits")
     return bits, obj.value
+
+
+def stq_decode_readout(pool, slots, q, k, v, a, b, o, stream=None):
+    import torch
+    f = torch.float32
+    sp, n = _slots(slots)
+    _check(_L.stq_decode_readout(pool.handle, sp, n, _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"),
+                                 _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"), _stream(stream)),
+           "stq_decode_readout")
+
+
+def stq_decode_commit(pool, slots, q, k, v, a, b, stream=None):
+    import torch
+    f = torch.float32
+    sp, n = _slots(slots)
+    _check(_L.stq_decode_commit(pool.handle, sp, n, _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"),
+                                _dev(a, f, "a"), _dev(b, f, "b"), _stream(stream)),
+           "stq_decode_commit")
 
 
 def stq_window_flush(pool, slots, stream=None):

@@ -23,7 +23,9 @@ using namespace stq;
 
 namespace {
 
-enum { MODE_STEP = 0, MODE_STORE = 1 };
+// MODE_READ / MODE_COMMIT: the step split in two (readout without touching the
+// tile; the update, refit and store without the readout)
+enum { MODE_STEP = 0, MODE_STORE = 1, MODE_READ = 2, MODE_COMMIT = 3 };
 
 typedef __attribute__((address_space(1))) const void* gptr_t;   // global source of a direct-to-LDS load
 typedef __attribute__((address_space(3))) void* lptr_t;         // its LDS destination
@@ -481,7 +483,8 @@ __device__ __forceinline__ void comp_extract(SmemM<DK, DV>& sm, float* Y, bool s
 
 // ------------------------------------------------------------------------
 // Tile body: MODE_STEP = decode step (unpack, gate, delta update, readout,
-// then refit_store); MODE_STORE = refit_store of a given fp32 tile.
+// then refit_store); MODE_READ = its readout only; MODE_COMMIT = all of it but
+// the readout; MODE_STORE = refit_store of a given fp32 tile.
 // ------------------------------------------------------------------------
 template <int DK, int DV, int MODE, int N>
 __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uint8_t* tile, size_t x, int h,
@@ -495,7 +498,7 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
   const int rho = tid / G::TPR, rsub = tid % G::TPR;
   float Y[64];
 
-  if constexpr (MODE == MODE_STEP) {
+  if constexpr (MODE != MODE_STORE) {
     // ---- every global load of the tile first: one memory latency per tile ----
     uint32_t raw[2 * N];
     f16x2 P[32];
@@ -584,8 +587,9 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
       const float u = cc[c] * ((D[c][0] + D[c][1]) * inv);
       const float wq = cc[c] * ((D[c][2] + D[c][3]) * inv);
       delta[c] = bb * (vv[c] - u);
-      if (Gq == 0) A.o[x * DV + j] = __builtin_fmaf(delta[c], kqs, wq);
+      if (MODE != MODE_COMMIT && Gq == 0) A.o[x * DV + j] = __builtin_fmaf(delta[c], kqs, wq);
     }
+    if (MODE == MODE_READ) return;
     if (bb == 0.f && allone) return;      // identity update: keep the encoding
     if (nes >= 256.f) clear_rows<DK, DV, N>(sm, P);   // some gate is zero (rare)
     opaque(P);
@@ -2848,6 +2852,28 @@ stq_status stq_prefill(stq_pool* p, const int32_t* slots, int32_t n, const int32
   else if (p->dk == 64 && p->dv == 128) launch_prefill<64, 128>(A, st);
   else launch_prefill<128, 64>(A, st);
   return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
+}
+stq_status stq_decode_readout(stq_pool* p, const int32_t* slots, int32_t n, const float* q, const float* k,
+                              const float* v, const float* a, const float* b, float* o, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (p->W > 0 || p->unit == STQ_UNIT_ROW) return STQ_ERR_UNSUPPORTED;
+  if (n == 0) return STQ_OK;
+  if (!q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
+  KArgs A = base_args(p, slots, n);
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  return dispatch<LTile<MODE_READ>::T>(p, A, st);
+}
+stq_status stq_decode_commit(stq_pool* p, const int32_t* slots, int32_t n, const float* q, const float* k,
+                             const float* v, const float* a, const float* b, hipStream_t st) {
+  stq_status s = check_call(p, slots, n);
+  if (s != STQ_OK) return s;
+  if (p->W > 0 || p->unit == STQ_UNIT_ROW) return STQ_ERR_UNSUPPORTED;
+  if (n == 0) return STQ_OK;
+  if (!q || !k || !v || !a || !b) return STQ_ERR_ARG;
+  KArgs A = base_args(p, slots, n);
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b;
+  return dispatch<LTile<MODE_COMMIT>::T>(p, A, st);
 }
 stq_status stq_window_flush(stq_pool* p, const int32_t* slots, int32_t n, hipStream_t st) {
   stq_status s = check_call(p, slots, n);
