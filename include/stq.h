@@ -203,7 +203,7 @@ typedef int32_t stq_status;
 #define STQ_ERR_LAYOUT      -2  /* buffer too small / misaligned, header mismatch */
 #define STQ_ERR_HIP         -3  /* a HIP runtime call or launch failed */
 #define STQ_ERR_STATE       -4  /* call not valid for this pool (e.g. flush without window) */
-#define STQ_ERR_UNSUPPORTED -5  /* valid request outside what this build implements */
+#define STQ_ERR_UNSUPPORTED -5  /* valid request outside what the library implements */
 
 #define STQ_GATE_HEAD     0  /* GDN: scalar gate per (request, head) */
 #define STQ_GATE_CHANNEL  1  /* KDA: gate per (request, head, key channel) */
@@ -220,7 +220,7 @@ typedef struct stq_pool_desc {
   int32_t n_heads;      /* H >= 1                                           */
   int32_t d_k, d_v;     /* each 64 or 128                                   */
   int32_t gate_kind;    /* STQ_GATE_HEAD or STQ_GATE_CHANNEL                */
-  int32_t unit_kind;    /* STQ_UNIT_HEAD (this build) or STQ_UNIT_ROW       */
+  int32_t unit_kind;    /* STQ_UNIT_HEAD or STQ_UNIT_ROW                    */
   int32_t window;       /* 0 = requantize every token; W in [1,32] = window */
   int32_t n_comp;       /* window mode: compensator rows per tile, 0..8,     */
                         /* window + n_comp <= 32; 0 without a window         */

@@ -2716,7 +2716,7 @@ const char* stq_status_str(stq_status s) {
     case STQ_ERR_LAYOUT: return "STQ_ERR_LAYOUT: buffer too small or misaligned";
     case STQ_ERR_HIP: return "STQ_ERR_HIP: HIP runtime or launch failure";
     case STQ_ERR_STATE: return "STQ_ERR_STATE: call not valid for this pool";
-    case STQ_ERR_UNSUPPORTED: return "STQ_ERR_UNSUPPORTED: not implemented in this build";
+    case STQ_ERR_UNSUPPORTED: return "STQ_ERR_UNSUPPORTED: not implemented by the library";
     default: return "unknown stq_status";
   }
 }
