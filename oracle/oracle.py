@@ -245,7 +245,6 @@ class OraclePool:
         b = _c(b, np.float32).reshape(T, self.H)
         o = np.zeros((T, self.H, self.dv), np.float64)
         Sf = np.zeros((n, self.H, self.dk, self.dv), np.float64) if final_state else None
-        assert self.W == 0, "prefill: pools without a window"
         lib().orc_prefill(*self._d(), _p(self.img), _p(slots), n, _p(ss), _p(q), _p(k), _p(v),
                           _p(a), _p(b), _p(o), _p(Sf) if final_state else None)
         return (o, Sf) if final_state else o

@@ -810,7 +810,10 @@ void orc_decode_step(DESC_ARGS, uint8_t* img, const int32_t* slots, int n,
  * recurrence of orc_update_f64 runs in binary64 over the request's tokens
  * ss[c] .. ss[c+1]-1 from D(tile), writing every token's readout; then
  * tile := R(fl32(S_T)) once.  No tokens, or only identity tokens (every gate
- * 1 and b = 0): the tile is left as it is.  Pools without a window only.
+ * 1 and b = 0): the tile is left as it is.  A window pool first folds every
+ * listed slot's open window (as the flush does); the prompt then runs from
+ * D(base) plus the compensator rows, and the final state is stored as the
+ * ingest stores it (compensators taken again, window empty).
  * Token-major inputs: q, k [tok][H][dk], v [tok][H][dv], a [tok][H] (KDA:
  * [tok][H][dk]), b [tok][H]; o [tok][H][dv] in binary64.  S_fin (optional,
  * NULL to skip): [n][H][dk][dv] binary64 final state before R. */
@@ -818,7 +821,6 @@ void orc_prefill(DESC_ARGS, uint8_t* img, const int32_t* slots, int n, const int
                  const float* q, const float* k, const float* v, const float* a, const float* b,
                  double* o, double* S_fin) {
   MKDESC;
-  if (d.W) return;
   #pragma omp parallel
   {
     scratch_t t = scratch_new(dk, dv);
@@ -829,8 +831,11 @@ void orc_prefill(DESC_ARGS, uint8_t* img, const int32_t* slots, int n, const int
     for (long x = 0; x < (long)n * H; x++) {
       int c = (int)(x / H), h = (int)(x % H);
       uint8_t* tp = tile_ptr(&d, img, slots[c], h);
+      uint8_t* cp = d.W ? cache_ptr(&d, img, slots[c], h) : NULL;
       int ng = gate ? dk : 1;
+      if (cp) window_fold(&d, h, tp, cp, row_w(&d, img, h), &t);
       tile_decode(&d, h, tp, &t);
+      if (cp) comp_add(&d, cp, t.S);
       for (size_t e = 0; e < (size_t)dk * dv; e++) S0[e] = t.S[e];
       int identity = 1;
       for (int tok = ss[c]; tok < ss[c + 1]; tok++) {
@@ -848,6 +853,7 @@ void orc_prefill(DESC_ARGS, uint8_t* img, const int32_t* slots, int n, const int
       if (S_fin) memcpy(S_fin + (size_t)x * dk * dv, S0, 8 * (size_t)dk * dv);
       if (identity) continue;   /* also covers a request with no tokens */
       for (size_t e = 0; e < (size_t)dk * dv; e++) t.S[e] = (float)S0[e];
+      if (cp) comp_extract(&d, h, t.S, cp);
       tile_encode(&d, h, t.S, row_w(&d, img, h), tp, &t);
     }
     free(S0);

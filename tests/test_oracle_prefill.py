@@ -9,7 +9,10 @@ memory under prefix caching).  Pins:
   - delta-rule retrieval: a = 1, b = 1, orthonormal keys: S_T^T k_s = v_s;
   - one token = the oracle's decode step (bytes and readout), GDN and KDA;
   - no tokens / identity tokens leave the tile; the written tile is the
-    oracle's own store of fl32(S_T); requests are independent of each other.
+    oracle's own store of fl32(S_T); requests are independent of each other;
+  - window pools: with an empty window and no compensators, exactly the plain
+    pool's prefill; otherwise the prompt starts from the folded state with its
+    compensators (checked by pure decay) and ends as the ingest's store.
 """
 import numpy as np
 import pytest
@@ -161,3 +164,45 @@ def test_requests_are_independent():
         oc = Q.prefill([c], np.array([0, t1 - t0], np.int32), q[t0:t1], k[t0:t1], v[t0:t1], a[t0:t1], b[t0:t1])
         assert np.array_equal(oc, o[t0:t1])
     assert np.array_equal(P.img, Q.img)
+
+
+def _window_pool(wl, n_slots, W, C):
+    P = oracle.OraclePool(n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, 0, 0, W, n_comp=C)
+    P.store(np.arange(n_slots), wl.state(np.arange(n_slots)))
+    return P
+
+
+def test_window_pool_empty_window_is_plain_prefill():
+    """No compensators and an empty window: the same tiles and readouts as a pool without a window."""
+    wl = Workload("C5", B=2, H=4)
+    Pw = _window_pool(wl, 2, 16, 0)
+    Pp = oracle.OraclePool(2, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, 0, 0, 0)
+    Pp.store(np.arange(2), wl.state(np.arange(2)))
+    ss, q, k, v, a, b = wl.prompts([21, 40])
+    ow = Pw.prefill([0, 1], ss, q, k, v, a, b)
+    op = Pp.prefill([0, 1], ss, q, k, v, a, b)
+    assert np.array_equal(ow, op)
+    for s in range(2):
+        for h in range(wl.H):
+            assert np.array_equal(Pw.tile_view(s, h), Pp.tile_view(s, h))
+
+
+def test_window_pool_starts_from_folded_state_with_compensators():
+    """Pure decay (b = 0, a = 1/2): the final state is 2^-T times the state the
+    pool holds after its open window is folded, compensators included; the
+    written base and compensators are the store of that final state."""
+    wl = Workload("C5", B=2, H=4)
+    P = _window_pool(wl, 2, 8, 3)
+    q0, k0, v0, a0, b0 = wl.token(0, n=2)
+    P.step([0, 1], q0, k0, v0, a0, b0)                     # open a window of one token
+    F = oracle.OraclePool(2, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, 0, 0, 8, image=P.img, n_comp=3)
+    F.window_flush([0, 1])
+    S_folded = F.fetch([0, 1]).astype(np.float64)
+    ss, q, k, v, a, b = wl.prompts([5, 9])
+    a[:] = 0.5
+    b[:] = 0.0
+    o, Sf = P.prefill([0, 1], ss, q, k, v, a, b, final_state=True)
+    for c, T in enumerate([5, 9]):
+        assert np.array_equal(Sf[c], S_folded[c] * 0.5 ** T)
+    F.store([0, 1], Sf.astype(np.float32))
+    assert np.array_equal(P.img, F.img)
