@@ -292,8 +292,11 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  * S_T and o differ from the exact recurrence by binary32 rounding only, so
  * a final code can differ from R of the exact state where that state sits
  * within rounding of a code boundary.  Requests must name distinct slots.
- * Supported: per-head units, GDN gate, no window; otherwise
- * STQ_ERR_UNSUPPORTED. */
+ * Window pools: every listed slot's open window is folded first (as
+ * stq_window_flush does); the prompt then runs from the base plus its
+ * compensator rows, and the final state is written as stq_pool_store writes
+ * one (compensator rows taken again, window empty).
+ * Supported: per-head units, GDN gate; otherwise STQ_ERR_UNSUPPORTED. */
 stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                        const int32_t* seq_start_dev, const float* q_dev, const float* k_dev,
                        const float* v_dev, const float* a_dev, const float* b_dev, float* o_dev,

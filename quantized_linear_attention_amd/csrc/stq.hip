@@ -2484,6 +2484,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   const int slot = ld_const(A.slots + ci);
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + ld_const(A.head_off + h);
+  uint8_t* cache = A.W ? A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride : nullptr;
   const int tb0 = A.seq_start[ci], tb1 = A.seq_start[ci + 1];
   if (tb1 <= tb0) return;                            // no tokens: the tile is left as it is
   const int nb = ld_const(A.head_bits + h);
@@ -2494,12 +2495,28 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     case 8: decode_state<DK, DV, 8>(tile, Y); break;
     default: decode_state<DK, DV, 16>(tile, Y); break;
   }
+  using G = GeoM<DK, DV>;
+  if (cache && A.C > 0 && nb != 16) {
+    // window pool (its open window already folded): the state is the base plus
+    // the compensator rows
+    const int32_t* idx = (const int32_t*)(cache + 192);
+    const float* val = (const float*)(cache + 256 + 4 * (size_t)A.W * (DK + DV));
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+    for (int c = 0; c < A.C; c++) {
+      const int r = idx[c];
+#pragma unroll
+      for (int e = 0; e < 64; e++) {
+        const int b = e >> 3, t = e & 7;
+        if (erow(b % G::NRC, t, Gq) == r) Y[e] += val[(size_t)c * DV + w * G::CPW + 16 * (b / G::NRC) + n16];
+      }
+    }
+  }
   const int moved = prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
   // identity tokens only: the tile is left as it is (the decode step's rule)
   if (!__syncthreads_or(moved)) return;
-  using G = GeoM<DK, DV>;
   const int rho = (int)threadIdx.x / G::TPR;
   if (threadIdx.x % G::TPR == 0) sh.m.gg[rho] = 1.f;
+  if (cache && A.C > 0) comp_extract<DK, DV>(sh.m, Y, false, cache, A.W, A.C, nb != 16);
   const float wgt = A.weights[(size_t)h * DK + rho];
   switch (nb) {
     case 4: refit_store<DK, DV, 4, true>(sh.m, Y, tile, wgt); break;
@@ -2841,10 +2858,14 @@ stq_status stq_prefill(stq_pool* p, const int32_t* slots, int32_t n, const int32
                        float* o, hipStream_t st) {
   stq_status s = check_call(p, slots, n);
   if (s != STQ_OK) return s;
-  if (p->unit != STQ_UNIT_HEAD || p->gate != STQ_GATE_HEAD || p->W != 0) return STQ_ERR_UNSUPPORTED;
+  if (p->unit != STQ_UNIT_HEAD || p->gate != STQ_GATE_HEAD) return STQ_ERR_UNSUPPORTED;
   if (n == 0) return STQ_OK;
   if (!seq_start || !q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
   KArgs A = base_args(p, slots, n);
+  if (p->W > 0) {                                     // window pools: end the open windows first
+    const stq_status f = dispatch_window(p, A, false, st);
+    if (f != STQ_OK) return f;
+  }
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
   A.seq_start = seq_start;
   if (p->dk == 128 && p->dv == 128) launch_prefill<128, 128>(A, st);

@@ -11,7 +11,8 @@ S_T.  Bar (written here):
   - codes against the oracle's R(fl32(S_T)): every difference <= 1 step and at
     most 2% of the codes differ (only codes whose exact value lies within that
     binary32 error of a rounding boundary, or rows whose bf16 scale does, can);
-  - empty requests and requests of identity tokens leave their tiles' bytes.
+  - empty requests and requests of identity tokens leave their tiles' bytes
+    (window pools: their folded windows are compared like the rest).
 """
 import numpy as np
 import pytest
@@ -36,7 +37,8 @@ def _run(P, wl, slots, lens, edit=None):
     if edit:
         edit(ss, q, k, v, a, b)
     pre = P.image()
-    ref = P.orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, image=pre)
+    ref = P.orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, 0, 0, P.ref.W, image=pre,
+                           n_comp=P.ref.C)
     T = int(ss[-1])
     o = torch.full((T, wl.H, wl.dv), float("nan"), dtype=torch.float32, device="cuda")
     P.stq.stq_prefill(P.pool, P.slots_t(slots), dev(ss), dev(q), dev(k), dev(v), dev(a), dev(b), o)
@@ -47,7 +49,8 @@ def _run(P, wl, slots, lens, edit=None):
 
 def _state_ok(orc, ref, img, slots, S_fin, moved):
     """Worst ratio of |D(tile) - S_T| to its bound over the tiles that moved."""
-    D = orc.OraclePool(ref.n_slots, ref.H, ref.dk, ref.dv, ref.bits, ref.wt, image=img).fetch(slots)
+    D = orc.OraclePool(ref.n_slots, ref.H, ref.dk, ref.dv, ref.bits, ref.wt, 0, 0, ref.W, image=img,
+                       n_comp=ref.C).fetch(slots)
     worst = 0.0
     for c, s in enumerate(slots):
         if not moved[c]:
@@ -76,7 +79,8 @@ def _check(P, wl, slots, lens, pre, img, ref, o, o_ref, S_fin, ss, moved):
     w = _state_ok(P.orc, ref, img, slots, S_fin, moved)
     say("  state worst ratio %.3g" % w)
     assert w <= 1.0
-    mv = [s for c, s in enumerate(slots) if moved[c]]
+    # a window pool folds every listed slot's open window first: those tiles all change
+    mv = [s for c, s in enumerate(slots) if moved[c] or ref.W]
     if mv:
         res = compare_codes(P.orc, ref, img, ref.img, mv)
         say("  codes", res)
@@ -84,7 +88,7 @@ def _check(P, wl, slots, lens, pre, img, ref, o, o_ref, S_fin, ss, moved):
         assert res["piv_bad"] == 0
     H = wl.H
     for c, s in enumerate(slots):
-        if not moved[c]:
+        if not moved[c] and not ref.W:
             for h in range(H):
                 assert np.array_equal(ref.tile_view(int(s), h, img), ref.tile_view(int(s), h, pre)), (c, h)
 
@@ -158,13 +162,39 @@ def test_prefill_zero_gates(torch_cuda, orc):
     _check(P, wl, slots, lens, *out, moved=[True, True])
 
 
+@pytest.mark.parametrize("W,C", [(16, 0), (8, 4)])
+def test_prefill_window_pool(torch_cuda, orc, W, C):
+    """Window pools: slots with open windows (folded first) and compensator rows
+    (part of the start state, taken again from the final state)."""
+    say("case prefill window pool", W, C)
+    wl = Workload("C5", B=4, H=8)
+    P = Pair(orc, wl, n_slots=5, window=W, n_comp=C)
+    slots = np.array([3, 0, 4, 1], np.int32)
+    P.store(slots, wl.state(slots))
+    for t in range(3):                                  # leave a window open in every slot
+        q, k, v, a, b = wl.token(t, n=4)
+        P.gpu_step(slots, q, k, v, a, b)
+    lens = [37, 0, 5, 64]
+    out = _run(P, wl, slots, lens)
+    pre, img, ref = out[0], out[1], out[2]
+    _check(P, wl, slots, lens, *out, moved=[L > 0 for L in lens])
+    # compensator rows: the same rows, values within the evaluation error; windows empty
+    for c, s in enumerate(slots):
+        for h in range(wl.H):
+            g, r = ref.cache_view(int(s), h, img), ref.cache_view(int(s), h, ref.img)
+            assert g[0] == 0 and r[0] == 0
+            if C:
+                assert np.array_equal(g[4], r[4]), (c, h)
+                assert np.abs(g[5] - r[5]).max() <= 1e-4 * np.abs(r[5]).max(), (c, h)
+
+
 def test_prefill_unsupported_and_empty(torch_cuda, orc):
     import torch
     import quantized_linear_attention_amd as stq
     say("case prefill unsupported pools, n = 0")
     f = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda")
     ss = torch.zeros(2, dtype=torch.int32, device="cuda")
-    for key in ("C4", "C5"):                       # per-key-row units; window mode
+    for key in ("C4",):                            # per-key-row units
         wl = Workload(key, B=1, H=2)
         P = Pair(orc, wl, n_slots=1)
         with pytest.raises(stq.StqError) as e:
