@@ -500,10 +500,11 @@ __device__ __forceinline__ void tile_body(const KArgs& A, SmemM<DK, DV>& sm, uin
 
   if constexpr (MODE != MODE_STORE) {
     // ---- every global load of the tile first: one memory latency per tile ----
+    // (the codes are read once per step and streamed: non-temporal loads)
     uint32_t raw[2 * N];
     f16x2 P[32];
 #pragma unroll
-    for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+    for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = __builtin_nontemporal_load((const u32x4*)(codes + 16 * ((w * K + k) * 64 + l)));
     constexpr int NS = DK / 64;
     float sa[NS], ss[NS];                  // gate and row scale of rows l + 64 s
 #pragma unroll
@@ -721,7 +722,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
   // one round trip; then the reads that do
   uint32_t raw[2 * N];
 #pragma unroll
-  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = __builtin_nontemporal_load((const u32x4*)(codes + 16 * ((w * K + k) * 64 + l)));
   float cc[G::NCC];
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) cc[c] = PIV ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
@@ -911,7 +912,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
-  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = __builtin_nontemporal_load((const u32x4*)(codes + 16 * ((w * K + k) * 64 + l)));
   float cc[G::NCC];
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) cc[c] = PIV ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
@@ -2089,7 +2090,7 @@ __device__ __forceinline__ void fetch_body(const KArgs& A, uint8_t* tile, size_t
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
-  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(codes + 16 * ((w * K + k) * 64 + l));
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = __builtin_nontemporal_load((const u32x4*)(codes + 16 * ((w * K + k) * 64 + l)));
   unpack<N>(raw, P);
   float cc[G::NCC];
 #pragma unroll
@@ -2206,7 +2207,7 @@ __device__ __forceinline__ void decode_state(const uint8_t* tile, float* Y) {
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
-  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = *(const u32x4*)(tile + 16 * ((w * K + k) * 64 + l));
+  for (int k = 0; k < K; k++) *(u32x4*)&raw[4 * k] = __builtin_nontemporal_load((const u32x4*)(tile + 16 * ((w * K + k) * 64 + l)));
   unpack<N>(raw, P);
   float cc[G::NCC];
 #pragma unroll
