@@ -775,19 +775,20 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
   // The open window's cached k_s and u_s (s < t) go straight from memory to
   // LDS (cst: W d_k floats, then W d_v), so that nothing waits for them
   // before the base matvec and no registers hold them meanwhile
+  // (cache policy 2: non-temporal, the cached entries are streamed)
   {
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const int nk = t * DK * 4, nu = t * DV * 4;          // bytes
     for (int c = wu; c < (nk + 1023) / 1024; c += G::NW) {
       const int off = c * 1024 + 16 * l;
       if (off < nk)
-        __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Kc + off), (lptr_t)((uint8_t*)cst + c * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Kc + off), (lptr_t)((uint8_t*)cst + c * 1024), 16, 0, 2);
     }
     for (int c = wu; c < (nu + 1023) / 1024; c += G::NW) {
       const int off = c * 1024 + 16 * l;
       if (off < nu)
         __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + off),
-                                         (lptr_t)((uint8_t*)cst + W * DK * 4 + c * 1024), 16, 0, 0);
+                                         (lptr_t)((uint8_t*)cst + W * DK * 4 + c * 1024), 16, 0, 2);
     }
     // the compensator values [C][d_v] follow the W cached u rows, here and in memory
     const int ncb = nc * DV * 4;
@@ -795,7 +796,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
       const int off = c * 1024 + 16 * l;
       if (off < ncb)
         __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + W * DV * 4 + off),
-                                         (lptr_t)((uint8_t*)cst + W * (DK + DV) * 4 + c * 1024), 16, 0, 0);
+                                         (lptr_t)((uint8_t*)cst + W * (DK + DV) * 4 + c * 1024), 16, 0, 2);
     }
   }
   // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t, 8 consecutive lanes per token
