@@ -285,8 +285,8 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  * A request with no tokens, or whose tokens are all the identity (a = 1 and
  * b = 0), leaves its tiles as they are (the decode step's identity rule).
  * Layouts, token-major as a packed batch of prompts: q_dev, k_dev fp32
- * [tok][H][d_k]; v_dev [tok][H][d_v]; a_dev, b_dev [tok][H]; o_dev
- * [tok][H][d_v]; seq_start_dev int32 [n+1], non-decreasing (a decreasing
+ * [tok][H][d_k]; v_dev [tok][H][d_v]; a_dev [tok][H] (per-channel gate:
+ * [tok][H][d_k]); b_dev [tok][H]; o_dev [tok][H][d_v]; seq_start_dev int32 [n+1], non-decreasing (a decreasing
  * pair is an empty request).  All device pointers, owned by the caller.
  * The state runs in binary32 (products on the matrix cores in binary32):
  * S_T and o differ from the exact recurrence by binary32 rounding only, so
@@ -296,7 +296,9 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  * stq_window_flush does); the prompt then runs from the base plus its
  * compensator rows, and the final state is written as stq_pool_store writes
  * one (compensator rows taken again, window empty).
- * Supported: per-head units, GDN gate; otherwise STQ_ERR_UNSUPPORTED. */
+ * Supported: per-head units (GDN gate: the chunkwise form on the matrix
+ * cores; per-channel gate: the recurrence token by token); per-key-row units
+ * return STQ_ERR_UNSUPPORTED. */
 stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                        const int32_t* seq_start_dev, const float* q_dev, const float* k_dev,
                        const float* v_dev, const float* a_dev, const float* b_dev, float* o_dev,

@@ -2192,9 +2192,19 @@ struct PSmem {
   float ga[PL], gb[PL], gam[PL];
 };
 
+// per-channel gates: a chunk's K, Q, gates and V, token-major (the token loop
+// reads a row quad per lane, the same address across a lane group: no padding)
+template <int DK, int DV>
+struct PKSmem {
+  float kc[PL][DK], qc[PL][DK], ac[PL][DK];
+  float vc[PL][DV];
+  float gb[PL];
+};
+
 template <int DK, int DV>
 union PrefillSmem {
   PSmem<DK, DV> p;
+  PKSmem<DK, DV> k;
   SmemM<DK, DV> m;
 };
 
@@ -2478,7 +2488,92 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
   return moved;
 }
 
+// Per-channel gates (KDA): the plain recurrence token by token on the state
+// registers, S <- Diag(a) S + k delta^T with delta = b (v - (Diag(a) S)^T k),
+// o = (Diag(a) S)^T q + delta (k.q): each lane holds 32 rows of 2 (NCC) columns,
+// the column sums close over the four lane groups.  (A chunkwise form would need
+// the per-channel decay inside every K K^T entry.)  Returns nonzero in some
+// thread if some token is not the identity.
 template <int DK, int DV>
+__device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps, float* Y, int tb0, int tb1,
+                                              int h) {
+  using G = GeoM<DK, DV>;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  const int col0 = w * G::CPW;
+  int moved = 0;
+  for (int t0 = tb0; t0 < tb1; t0 += PL) {
+    const int Lc = min(PL, tb1 - t0);
+    for (int f = tid; f < Lc * DK / 4; f += G::NT) {
+      const int t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
+      const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
+      const f32x4 av = *(const f32x4*)(A.a + r);
+      *(f32x4*)&ps.kc[t][d4] = *(const f32x4*)(A.k + r);
+      *(f32x4*)&ps.qc[t][d4] = *(const f32x4*)(A.q + r);
+      *(f32x4*)&ps.ac[t][d4] = av;
+      moved |= (av[0] != 1.f) | (av[1] != 1.f) | (av[2] != 1.f) | (av[3] != 1.f);
+    }
+    for (int f = tid; f < Lc * DV / 4; f += G::NT) {
+      const int t = f / (DV / 4), d4 = 4 * (f % (DV / 4));
+      *(f32x4*)&ps.vc[t][d4] = *(const f32x4*)(A.v + ((size_t)(t0 + t) * A.H + h) * DV + d4);
+    }
+    if (tid < Lc) {
+      const float bv = A.b[(size_t)(t0 + tid) * A.H + h];
+      ps.gb[tid] = bv;
+      moved |= bv != 0.f;
+    }
+    lds_barrier();
+    for (int t = 0; t < Lc; t++) {
+      float uu[G::NCC], ww[G::NCC], kq = 0.f;
+      f32x4 kr[G::NRC][2];
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) uu[c] = ww[c] = 0.f;
+#pragma unroll
+      for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+          const int r0 = 32 * rc + 16 * hf + 4 * Gq;        // the lane's rows r0 .. r0 + 3
+          const f32x4 a4 = *(const f32x4*)&ps.ac[t][r0], q4 = *(const f32x4*)&ps.qc[t][r0];
+          kr[rc][hf] = *(const f32x4*)&ps.kc[t][r0];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            kq = __builtin_fmaf(kr[rc][hf][i], q4[i], kq);
+#pragma unroll
+            for (int c = 0; c < G::NCC; c++) {
+              const int e = 8 * (c * G::NRC + rc) + 4 * hf + i;
+              Y[e] *= a4[i];
+              uu[c] = __builtin_fmaf(Y[e], kr[rc][hf][i], uu[c]);
+              ww[c] = __builtin_fmaf(Y[e], q4[i], ww[c]);
+            }
+          }
+        }
+      kq = g4_sum(kq);
+      const float bt = ps.gb[t];
+      float dl[G::NCC];
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) {
+        const int j = col0 + 16 * c + n16;
+        dl[c] = bt * (ps.vc[t][j] - g4_sum(uu[c]));
+        const float o = __builtin_fmaf(dl[c], kq, g4_sum(ww[c]));
+        if (Gq == 0) A.o[((size_t)(t0 + t) * A.H + h) * DV + j] = o;
+      }
+#pragma unroll
+      for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int c = 0; c < G::NCC; c++) {
+              const int e = 8 * (c * G::NRC + rc) + 4 * hf + i;
+              Y[e] = __builtin_fmaf(kr[rc][hf][i], dl[c], Y[e]);
+            }
+    }
+    lds_barrier();
+  }
+  return moved;
+}
+
+template <int DK, int DV, bool KDA>
 __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(KArgs A) {
   __shared__ PrefillSmem<DK, DV> sh;
   const int ci = (int)blockIdx.x / A.H, h = (int)blockIdx.x - ci * A.H;
@@ -2513,7 +2608,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
       }
     }
   }
-  const int moved = prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
+  const int moved = KDA ? prefill_tokens<DK, DV>(A, sh.k, Y, tb0, tb1, h) : prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
   // identity tokens only: the tile is left as it is (the decode step's rule)
   if (!__syncthreads_or(moved)) return;
   const int rho = (int)threadIdx.x / G::TPR;
@@ -2714,7 +2809,10 @@ struct LFetch {
 
 template <int DK, int DV>
 void launch_prefill(const KArgs& A, hipStream_t st) {
-  hipLaunchKernelGGL((k_prefill<DK, DV>), dim3((unsigned)A.n * (unsigned)A.H), dim3(GeoM<DK, DV>::NT), 0, st, A);
+  if (A.gate)
+    hipLaunchKernelGGL((k_prefill<DK, DV, true>), dim3((unsigned)A.n * (unsigned)A.H), dim3(GeoM<DK, DV>::NT), 0, st, A);
+  else
+    hipLaunchKernelGGL((k_prefill<DK, DV, false>), dim3((unsigned)A.n * (unsigned)A.H), dim3(GeoM<DK, DV>::NT), 0, st, A);
 }
 
 stq_status check_call(const stq_pool* p, const int32_t* slots, int32_t n) {
@@ -2860,7 +2958,7 @@ stq_status stq_prefill(stq_pool* p, const int32_t* slots, int32_t n, const int32
                        float* o, hipStream_t st) {
   stq_status s = check_call(p, slots, n);
   if (s != STQ_OK) return s;
-  if (p->unit != STQ_UNIT_HEAD || p->gate != STQ_GATE_HEAD) return STQ_ERR_UNSUPPORTED;
+  if (p->unit != STQ_UNIT_HEAD) return STQ_ERR_UNSUPPORTED;
   if (n == 0) return STQ_OK;
   if (!seq_start || !q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
   KArgs A = base_args(p, slots, n);

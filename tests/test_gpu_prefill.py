@@ -37,8 +37,8 @@ def _run(P, wl, slots, lens, edit=None):
     if edit:
         edit(ss, q, k, v, a, b)
     pre = P.image()
-    ref = P.orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, 0, 0, P.ref.W, image=pre,
-                           n_comp=P.ref.C)
+    ref = P.orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, P.ref.gate, 0, P.ref.W,
+                           image=pre, n_comp=P.ref.C)
     T = int(ss[-1])
     o = torch.full((T, wl.H, wl.dv), float("nan"), dtype=torch.float32, device="cuda")
     P.stq.stq_prefill(P.pool, P.slots_t(slots), dev(ss), dev(q), dev(k), dev(v), dev(a), dev(b), o)
@@ -49,7 +49,7 @@ def _run(P, wl, slots, lens, edit=None):
 
 def _state_ok(orc, ref, img, slots, S_fin, moved):
     """Worst ratio of |D(tile) - S_T| to its bound over the tiles that moved."""
-    D = orc.OraclePool(ref.n_slots, ref.H, ref.dk, ref.dv, ref.bits, ref.wt, 0, 0, ref.W, image=img,
+    D = orc.OraclePool(ref.n_slots, ref.H, ref.dk, ref.dv, ref.bits, ref.wt, ref.gate, 0, ref.W, image=img,
                        n_comp=ref.C).fetch(slots)
     worst = 0.0
     for c, s in enumerate(slots):
@@ -186,6 +186,33 @@ def test_prefill_window_pool(torch_cuda, orc, W, C):
             if C:
                 assert np.array_equal(g[4], r[4]), (c, h)
                 assert np.abs(g[5] - r[5]).max() <= 1e-4 * np.abs(r[5]).max(), (c, h)
+
+
+@pytest.mark.parametrize("dk,dv,zero", [(128, 128, False), (64, 128, True)])
+def test_prefill_per_channel_gate(torch_cuda, orc, dk, dv, zero):
+    """Per-channel (KDA) gates on per-head widths: the token-by-token path, with
+    the KDA half-life law (and whole zero channels when asked)."""
+    import dataclasses
+    say("case prefill per-channel gate", dk, dv, zero)
+    wl = Workload("C4", B=3, H=8)
+    wl.cfg = dataclasses.replace(wl.cfg, unit=0)
+    wl.dk, wl.dv = dk, dv
+    wl.row_weight = wl.row_weight[:, :dk].copy()
+    wl.r_prof, wl.c_prof = wl.r_prof[:, :dk].copy(), wl.c_prof[:, :dv].copy()
+    wl.half_life = wl.half_life[:, :dk].copy()
+    wl.bits = np.array([4, 6, 8, 16, 6, 4, 8, 6], np.int32)
+    P = Pair(orc, wl, n_slots=4)
+    slots = np.array([2, 0, 3], np.int32)
+    P.store(slots, wl.state(slots))
+    lens = [70, 0, 33]
+
+    def edit(ss, q, k, v, a, b):
+        if zero:
+            a[5, :, :7] = 0.0
+            a[ss[2] + 31, 2, :] = 0.0
+
+    out = _run(P, wl, slots, lens, edit if zero else None)
+    _check(P, wl, slots, lens, *out, moved=[L > 0 for L in lens])
 
 
 def test_prefill_unsupported_and_empty(torch_cuda, orc):
