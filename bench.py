@@ -134,7 +134,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 512; P3: 8)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 32; P3: 2)")
-    ap.add_argument("--workload", choices=sorted(BENCH) + ["P3"], default="C3")
+    ap.add_argument("--workload", choices=sorted(BENCH) + ["P3", "P4"], default="C3")
     ap.add_argument("--prompt-len", type=int, default=1024, help="P3: tokens per prompt")
     ap.add_argument("--prompts", type=int, default=64, help="P3: prompts per prefill call")
     ap.add_argument("--layers", type=int, default=None)
@@ -169,7 +169,7 @@ def main():
     from workloads import Workload
 
     key = args.workload
-    if key == "P3":
+    if key in ("P3", "P4"):
         return prefill_bench(args)
     spec = BENCH[key]
     dev = torch.device("cuda:0")
@@ -390,6 +390,7 @@ def split_timing(stq, torch, pools, slots, toks, o, L, K, Wu, wl, spec):
 
 PL = 32                     # tokens per chunk of the prefill kernel
 MFMA_F32_PEAK = 157.3       # TFLOP/s, dense binary32 matrix cores
+VALU_F32_PEAK = 157.3       # TFLOP/s, binary32 vector ALUs (the published figure counts packed pairs)
 
 
 def prefill_flops(n_tok, H, dk, dv):
@@ -402,14 +403,22 @@ def prefill_flops(n_tok, H, dk, dv):
 
 def prefill_bench(args):
     """P3: prefill ingest of a batch of prompts into the C3 pool (GDN head mix,
-    H = 32, d = 128): one step = one stq_prefill call over all prompts."""
+    H = 32, d = 128): one step = one stq_prefill call over all prompts.  P4: the
+    same with per-channel (KDA) gates of C4's half-life law on per-head widths
+    of the same mix (the token-by-token path)."""
+    import dataclasses
+
     import torch
 
     import quantized_linear_attention_amd as stq
     from workloads import Workload
     dev = torch.device("cuda:0")
     B, Lp = args.prompts, args.prompt_len
-    wl = Workload("C3", B=B)
+    kda = args.workload == "P4"
+    wl = Workload("C4" if kda else "C3", B=B)
+    if kda:
+        wl.cfg = dataclasses.replace(wl.cfg, unit=0)
+        wl.bits = Workload("C3").bits
     c, H, dk, dv = wl.cfg, wl.H, wl.dk, wl.dv
     T = B * Lp
     desc = stq.make_desc(B, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, 0, 0)
@@ -434,8 +443,12 @@ def prefill_bench(args):
     k = (k / k.norm(dim=-1, keepdim=True)).contiguous()
     b = (0.05 + 0.9 * torch.rand((T, H), generator=gen, device=dev)).contiguous()
     hl = torch.as_tensor(wl.half_life, dtype=torch.float32, device=dev)
-    hp = hl[None, :] * torch.exp(0.1 * torch.randn((T, H), generator=gen, device=dev))
-    a = torch.clamp(2.0 ** (-1.0 / hp), 0.9, 0.9999).contiguous()
+    if kda:
+        hp = hl[None] * torch.exp(0.1 * torch.randn((T, H, dk), generator=gen, device=dev))
+        a = (2.0 ** (-1.0 / hp)).contiguous()
+    else:
+        hp = hl[None, :] * torch.exp(0.1 * torch.randn((T, H), generator=gen, device=dev))
+        a = torch.clamp(2.0 ** (-1.0 / hp), 0.9, 0.9999).contiguous()
     ss = torch.arange(0, T + 1, Lp, dtype=torch.int32, device=dev)
     o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     K = 8 if args.steps is None else args.steps
@@ -454,7 +467,8 @@ def prefill_bench(args):
     per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(K)])
     total_ms = float(ev[0].elapsed_time(ev[K]))
     avg_ms = float(per.mean())
-    flops = prefill_flops(T, H, dk, dv)
+    # P4: 7 vector flops per state element and token (gate, two column sums, update)
+    flops = T * H * 7 * dk * dv if kda else prefill_flops(T, H, dk, dv)
     tflops = flops / (avg_ms * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
@@ -473,20 +487,23 @@ def prefill_bench(args):
         cpu = {"value": calls * ns * Ls * H / el, "unit": "request-head prompt tokens/s",
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": "%d calls x %d prompts of %d tokens, all %d heads, %.1f s" % (calls, ns, Ls, H, el)}
+    gname = "KDA per-channel gates" if kda else "GDN"
     line = {
         "metric": "request-head prompt tokens/s (prefill ingest, B=%d prompts x %d tokens, H=32, d=128, "
-                  "6-bit nominal GDN pool)" % (B, Lp),
+                  "6-bit nominal %s pool)" % (B, Lp, gname),
         "value": T * H * K / (total_ms * 1e-3),
         "unit": "request-head prompt tokens/s",
         "n_gpus": 1, "steps": K, "warmup": Wu, "ms_per_step": total_ms / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32 state and products, 4/6/8-bit + f16 final state",
         "data": "synthetic (seeded; states and prompts drawn on the GPU with the workload recipe)",
-        "config": {"workload": "prefill of %d prompts x %d tokens into the GDN pool H=32 d_k=d_v=128, heads "
-                               "{4b:9, 6b:16, 8b:6, fp16:1}" % (B, Lp),
+        "config": {"workload": "prefill of %d prompts x %d tokens into the %s pool H=32 d_k=d_v=128, heads "
+                               "{4b:9, 6b:16, 8b:6, fp16:1}" % (B, Lp, gname),
                    "global_batch": B, "prompt_len": Lp, "heads": H, "d_k": dk, "d_v": dv},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_F32_PEAK, "traffic": None, "kernel": "k_prefill<128, 128>",
+        "roofline": {"bound": "alu" if kda else "mfma", "achieved": tflops,
+                     "peak": VALU_F32_PEAK if kda else MFMA_F32_PEAK, "unit": "TFLOP/s",
+                     "frac": tflops / (VALU_F32_PEAK if kda else MFMA_F32_PEAK), "traffic": None,
+                     "kernel": "k_prefill<128, 128, %s>" % ("true" if kda else "false"),
                      "flops_per_launch": flops, "avg_launch_ms": avg_ms,
                      "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
                      "hbm_gbs": (T * H * (4 * (2 * dk + 2 * dv) + 8)) / (avg_ms * 1e-3) / 1e9},
