@@ -12,7 +12,9 @@ memory under prefix caching).  Pins:
     oracle's own store of fl32(S_T); requests are independent of each other;
   - window pools: with an empty window and no compensators, exactly the plain
     pool's prefill; otherwise the prompt starts from the folded state with its
-    compensators (checked by pure decay) and ends as the ingest's store.
+    compensators (checked by pure decay) and ends as the ingest's store;
+  - per-channel gates: each row decays by its own gates (b = 0), and one token
+    is the decode step.
 """
 import numpy as np
 import pytest
@@ -206,3 +208,40 @@ def test_window_pool_starts_from_folded_state_with_compensators():
         assert np.array_equal(Sf[c], S_folded[c] * 0.5 ** T)
     F.store([0, 1], Sf.astype(np.float32))
     assert np.array_equal(P.img, F.img)
+
+
+def _kda_head_pool(n_slots):
+    import dataclasses
+    wl = Workload("C4", B=n_slots, H=4)
+    wl.cfg = dataclasses.replace(wl.cfg, unit=0)
+    wl.bits = np.array([4, 6, 8, 16], np.int32)
+    P = oracle.OraclePool(n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, 1, 0, 0)
+    P.store(np.arange(n_slots), wl.state(np.arange(n_slots)))
+    return wl, P
+
+
+def test_per_channel_pure_decay():
+    """Per-channel gates, b = 0: row i decays by the product of its own gates."""
+    wl, P = _kda_head_pool(2)
+    S0 = P.fetch(np.arange(2)).astype(np.float64)
+    ss, q, k, v, a, b = wl.prompts([6, 3])
+    b[:] = 0
+    o, Sf = P.prefill([0, 1], ss, q, k, v, a, b, final_state=True)
+    for c in range(2):
+        t0, t1 = ss[c], ss[c + 1]
+        for h in range(wl.H):
+            ah = a[t0:t1, h].astype(np.float64)                 # [T][dk]
+            assert np.allclose(Sf[c, h], np.prod(ah, axis=0)[:, None] * S0[c, h], rtol=1e-13, atol=0)
+            for t in range(t1 - t0):
+                g = np.prod(ah[:t + 1], axis=0)
+                want = (g[:, None] * S0[c, h]).T @ q[t0 + t, h].astype(np.float64)
+                assert np.allclose(o[t0 + t, h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_per_channel_one_token_is_a_decode_step():
+    wl, P1 = _kda_head_pool(3)
+    P2 = oracle.OraclePool(3, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, 1, 0, 0, image=P1.img)
+    q, k, v, a, b = wl.token(0, n=3)
+    o1 = P1.step([1, 2, 0], q, k, v, a, b)
+    o2 = P2.prefill([1, 2, 0], np.arange(4, dtype=np.int32), q, k, v, a, b)
+    assert np.array_equal(P1.img, P2.img) and np.array_equal(o1, o2)
