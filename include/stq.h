@@ -304,6 +304,20 @@ stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                        const float* v_dev, const float* a_dev, const float* b_dev, float* o_dev,
                        hipStream_t stream);
 
+/* Prefill on plain binary32 states, no pool: S_dev [n][n_heads][d_k][d_v]
+ * (row-major tiles, the layout of stq_pool_fetch) is advanced in place over
+ * each request's tokens exactly as stq_prefill advances a tile's state
+ * (same paths, same layouts of seq_start, q, k, v, a, b, o; gate_kind
+ * STQ_GATE_HEAD or STQ_GATE_CHANNEL), and every token's readout is written.
+ * With stq_pool_fetch before and stq_pool_store after, it prefills pools that
+ * stq_prefill does not take (per-key-row units): the store then refits every
+ * listed tile, identity prompts included.  A request with no tokens leaves
+ * its state as it is.  STQ_ERR_ARG on bad sizes or null pointers. */
+stq_status stq_prefill_states(int32_t n, int32_t n_heads, int32_t d_k, int32_t d_v, int32_t gate_kind,
+                              float* S_dev, const int32_t* seq_start_dev, const float* q_dev,
+                              const float* k_dev, const float* v_dev, const float* a_dev,
+                              const float* b_dev, float* o_dev, hipStream_t stream);
+
 /* The decode step split in two, for overlapped writeback ([P4] "Las dos
  * ideas": the pages' serving system writes back on a separate stream so that
  * the state updates overlap the model's other work).  stq_decode_readout

@@ -52,6 +52,8 @@ def _load():
     L.stq_decode_step.restype = I
     L.stq_decode_step.argtypes = [P, P, I, P, P, P, P, P, P, St]
     L.stq_prefill.restype = I
+    L.stq_prefill_states.restype = I
+    L.stq_prefill_states.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, St]
     L.stq_decode_readout.restype = I
     L.stq_decode_readout.argtypes = [P, P, I, P, P, P, P, P, P, St]
     L.stq_decode_commit.restype = I
@@ -187,6 +189,17 @@ def stq_allocate_bits(err, half_life, n_pivots, budget_bits):
                                 int(n_pivots), float(budget_bits), bits.ctypes.data_as(ctypes.c_void_p),
                                 ctypes.byref(obj)), "stq_allocate_bits")
     return bits, obj.value
+
+
+def stq_prefill_states(S, seq_start, q, k, v, a, b, o, gate_kind=STQ_GATE_HEAD, stream=None):
+    """S: contiguous fp32 CUDA tensor [n][H][d_k][d_v], advanced in place."""
+    import torch
+    f = torch.float32
+    n, H, dk, dv = S.shape
+    _check(_L.stq_prefill_states(n, H, dk, dv, gate_kind, _dev(S, f, "S"), _dev(seq_start, torch.int32, "seq_start"),
+                                 _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"), _dev(a, f, "a"), _dev(b, f, "b"),
+                                 _dev(o, f, "o"), _stream(stream)),
+           "stq_prefill_states")
 
 
 def stq_decode_readout(pool, slots, q, k, v, a, b, o, stream=None):

@@ -2623,6 +2623,33 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   }
 }
 
+// Prefill on plain binary32 states S [n][H][d_k][d_v] in place (no pool): the
+// same chunk / token paths, S read into the lane layout and written back.
+template <int DK, int DV, bool KDA>
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_states(KArgs A) {
+  __shared__ PrefillSmem<DK, DV> sh;
+  using G = GeoM<DK, DV>;
+  const int ci = (int)blockIdx.x / A.H, h = (int)blockIdx.x - ci * A.H;
+  if (ci >= A.n) return;
+  const int tb0 = A.seq_start[ci], tb1 = A.seq_start[ci + 1];
+  if (tb1 <= tb0) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  float* S = A.S_out + ((size_t)ci * A.H + h) * DK * DV;
+  float Y[64];
+#pragma unroll
+  for (int e = 0; e < 64; e++) {
+    const int b = e >> 3, t = e & 7;
+    Y[e] = S[(size_t)erow(b % G::NRC, t, Gq) * DV + w * G::CPW + 16 * (b / G::NRC) + n16];
+  }
+  if (KDA) prefill_tokens<DK, DV>(A, sh.k, Y, tb0, tb1, h);
+  else prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
+#pragma unroll
+  for (int e = 0; e < 64; e++) {
+    const int b = e >> 3, t = e & 7;
+    S[(size_t)erow(b % G::NRC, t, Gq) * DV + w * G::CPW + 16 * (b / G::NRC) + n16] = Y[e];
+  }
+}
+
 __global__ void k_debug_rcp(float* out) {
   const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < 65536u) out[b] = rcp_bf16(bf16f(b));
@@ -2815,6 +2842,15 @@ void launch_prefill(const KArgs& A, hipStream_t st) {
     hipLaunchKernelGGL((k_prefill<DK, DV, false>), dim3((unsigned)A.n * (unsigned)A.H), dim3(GeoM<DK, DV>::NT), 0, st, A);
 }
 
+template <int DK, int DV>
+void launch_prefill_states(const KArgs& A, hipStream_t st) {
+  const unsigned g = (unsigned)A.n * (unsigned)A.H;
+  if (A.gate)
+    hipLaunchKernelGGL((k_prefill_states<DK, DV, true>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
+  else
+    hipLaunchKernelGGL((k_prefill_states<DK, DV, false>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
+}
+
 stq_status check_call(const stq_pool* p, const int32_t* slots, int32_t n) {
   if (!p) return STQ_ERR_ARG;
   if (n < 0 || n > p->n_slots) return STQ_ERR_ARG;
@@ -2972,6 +3008,26 @@ stq_status stq_prefill(stq_pool* p, const int32_t* slots, int32_t n, const int32
   else if (p->dk == 64 && p->dv == 64) launch_prefill<64, 64>(A, st);
   else if (p->dk == 64 && p->dv == 128) launch_prefill<64, 128>(A, st);
   else launch_prefill<128, 64>(A, st);
+  return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
+}
+stq_status stq_prefill_states(int32_t n, int32_t n_heads, int32_t d_k, int32_t d_v, int32_t gate_kind, float* S,
+                              const int32_t* seq_start, const float* q, const float* k, const float* v,
+                              const float* a, const float* b, float* o, hipStream_t st) {
+  if (n < 0 || n_heads < 1 || n_heads > 4096) return STQ_ERR_ARG;
+  if (!((d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128))) return STQ_ERR_ARG;
+  if (gate_kind != STQ_GATE_HEAD && gate_kind != STQ_GATE_CHANNEL) return STQ_ERR_ARG;
+  if (n == 0) return STQ_OK;
+  if (!S || !seq_start || !q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
+  KArgs A;
+  memset(&A, 0, sizeof(A));
+  A.n = n; A.H = n_heads; A.gate = gate_kind;
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  A.S_out = S;
+  A.seq_start = seq_start;
+  if (d_k == 128 && d_v == 128) launch_prefill_states<128, 128>(A, st);
+  else if (d_k == 64 && d_v == 64) launch_prefill_states<64, 64>(A, st);
+  else if (d_k == 64 && d_v == 128) launch_prefill_states<64, 128>(A, st);
+  else launch_prefill_states<128, 64>(A, st);
   return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
 }
 stq_status stq_decode_readout(stq_pool* p, const int32_t* slots, int32_t n, const float* q, const float* k,

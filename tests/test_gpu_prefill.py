@@ -232,3 +232,73 @@ def test_prefill_unsupported_and_empty(torch_cuda, orc):
     pre = P.image()
     stq.stq_prefill(P.pool, P.slots_t(np.zeros(0, np.int32)), ss, f(1), f(1), f(1), f(1), f(1), f(1))
     assert np.array_equal(P.image(), pre)
+
+
+@pytest.mark.parametrize("key,gate", [("C2", 0), ("C4", 1)])
+def test_prefill_states_against_recurrence(torch_cuda, orc, key, gate):
+    """stq_prefill_states on plain binary32 states: final states within the
+    binary32 evaluation error (1e-4 of the tile's largest |S_T|) of the
+    oracle's binary64 recurrence, readouts to the bar above."""
+    import torch
+    say("case prefill states", key, gate)
+    wl = Workload(key, B=3, H=8)
+    lens = [50, 0, 17]
+    slots = np.arange(3, dtype=np.int32)
+    S0 = wl.state(slots)
+    ss, q, k, v, a, b = wl.prompts(lens)
+    dev = lambda x: torch.as_tensor(x, device="cuda")
+    S = dev(S0).contiguous()
+    o = torch.zeros((int(ss[-1]), wl.H, wl.dv), dtype=torch.float32, device="cuda")
+    import quantized_linear_attention_amd as stq
+    stq.stq_prefill_states(S, dev(ss), dev(q), dev(k), dev(v), dev(a), dev(b), o, gate_kind=gate)
+    torch.cuda.synchronize()
+    # the oracle's recurrence from the same binary32 states: a pool of binary16
+    # heads only would round them, so run its update directly
+    T_all = []
+    for c in range(3):
+        Sx = S0[c].astype(np.float64)
+        for t in range(ss[c], ss[c + 1]):
+            for h in range(wl.H):
+                ah = a[t, h] if gate else a[t, h:h + 1]
+                Sx[h], oo = orc.update_f64(Sx[h], q[t, h], k[t, h], v[t, h], ah, b[t, h])
+                T_all.append((t, h, oo))
+        Sg = S.cpu().numpy()[c].astype(np.float64)
+        for h in range(wl.H):
+            assert np.abs(Sg[h] - Sx[h]).max() <= 1e-4 * np.abs(Sx[h]).max(), (c, h)
+    og = o.cpu().numpy()
+    o_ref = np.zeros(og.shape)
+    for t, h, oo in T_all:
+        o_ref[t, h] = oo
+    assert readout_ok(og.reshape(-1, 1, wl.H, wl.dv), o_ref.reshape(-1, 1, wl.H, wl.dv)) <= 1.0
+    assert np.array_equal(S.cpu().numpy()[1], S0[1])          # no tokens: untouched
+
+
+def test_prefill_states_per_key_row_pool(torch_cuda, orc):
+    """Per-key-row (C4) pools through fetch -> stq_prefill_states -> store,
+    against the oracle's prefill of the same pool."""
+    import torch
+    import quantized_linear_attention_amd as stq
+    say("case prefill states C4 pool")
+    wl = Workload("C4", B=3, H=8)
+    P = Pair(orc, wl, n_slots=4)
+    slots = np.array([3, 1, 0], np.int32)
+    P.store(slots, wl.state(slots))
+    lens = [41, 9, 30]
+    ss, q, k, v, a, b = wl.prompts(lens)
+    dev = lambda x: torch.as_tensor(x, device="cuda")
+    pre = P.image()
+    ref = orc.OraclePool(4, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1), wl.row_weight, 1, 1, 0, image=pre)
+    S = torch.empty((3, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    sl = P.slots_t(slots)
+    o = torch.empty((int(ss[-1]), wl.H, wl.dv), dtype=torch.float32, device="cuda")
+    stq.stq_pool_fetch(P.pool, sl, S)
+    stq.stq_prefill_states(S, dev(ss), dev(q), dev(k), dev(v), dev(a), dev(b), o, gate_kind=1)
+    stq.stq_pool_store(P.pool, sl, S)
+    torch.cuda.synchronize()
+    o_ref, S_fin = ref.prefill(slots, ss, q, k, v, a, b, final_state=True)
+    r = readout_ok(o.cpu().numpy().reshape(-1, 1, wl.H, wl.dv), o_ref.reshape(-1, 1, wl.H, wl.dv))
+    say("  readout worst ratio %.3g" % r)
+    assert r <= 1.0
+    res = compare_codes(orc, ref, P.image(), ref.img, slots)
+    say("  codes", res)
+    assert res["maxd"] <= 1 and res["mism"] <= 0.02 * res["codes"] and res["piv_bad"] == 0
