@@ -283,12 +283,15 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  *     state after token t (no requantization between tokens), and
  *   - writes the final state into the tile through R once.
  * A request with no tokens, or whose tokens are all the identity (a = 1 and
- * b = 0), leaves its tiles as they are (the decode step's identity rule).
+ * b = 0), leaves its tiles as they are (the decode step's identity rule; in
+ * a window pool, as they are after the fold below).
  * Layouts, token-major as a packed batch of prompts: q_dev, k_dev fp32
  * [tok][H][d_k]; v_dev [tok][H][d_v]; a_dev [tok][H] (per-channel gate:
- * [tok][H][d_k]); b_dev [tok][H]; o_dev [tok][H][d_v]; seq_start_dev int32 [n+1], non-decreasing (a decreasing
- * pair is an empty request).  All device pointers, owned by the caller.
- * The state runs in binary32 (products on the matrix cores in binary32):
+ * [tok][H][d_k]); b_dev [tok][H]; o_dev [tok][H][d_v]; seq_start_dev int32
+ * [n+1], non-decreasing (a decreasing pair is an empty request).  All device
+ * pointers, owned by the caller.
+ * The state runs in binary32 (the GDN path's products on the matrix cores in
+ * binary32, the per-channel path's on the vector ALUs):
  * S_T and o differ from the exact recurrence by binary32 rounding only, so
  * a final code can differ from R of the exact state where that state sits
  * within rounding of a code boundary.  Requests must name distinct slots.
@@ -328,7 +331,8 @@ stq_status stq_prefill_states(int32_t n, int32_t n_heads, int32_t d_k, int32_t d
  * reads: it must be ordered after the readout of the same slots (same
  * stream, or an event), and the next readout of those slots after the
  * commit.  The pair reads each tile twice (one read more than the fused
- * step): it shortens the time until o is available, not the bytes moved.
+ * step): it can make o available before the writeback where the memory is
+ * otherwise idle between layers; it adds bytes, never removes them.
  * Per-head units without a window only; otherwise STQ_ERR_UNSUPPORTED. */
 stq_status stq_decode_readout(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                               const float* q_dev, const float* k_dev, const float* v_dev,
