@@ -102,3 +102,23 @@ def test_prefill_rejects_on_host(stq):
     r = lib.stq_prefill(None, P(0x10000), 1, P(0x10000), P(0x10000), P(0x10000), P(0x10000),
                         P(0x10000), P(0x10000), P(0x10000), None)
     assert r == -1
+
+
+def test_new_entry_points_reject_on_host(stq):
+    """Bad sizes, kinds or handles are refused on the host before anything is enqueued."""
+    lib = ctypes.CDLL(stq.library_path())
+    P, I = ctypes.c_void_p, ctypes.c_int32
+    lib.stq_prefill_states.restype = I
+    lib.stq_prefill_states.argtypes = [I, I, I, I, I] + [P] * 8 + [P]
+    d = P(0x10000)
+    args = [d] * 8
+    for n, H, dk, dv, gate in [(-1, 2, 128, 128, 0), (1, 0, 128, 128, 0), (1, 4097, 128, 128, 0),
+                               (1, 2, 96, 128, 0), (1, 2, 128, 32, 0), (1, 2, 128, 128, 2)]:
+        assert lib.stq_prefill_states(n, H, dk, dv, gate, *args, None) == -1
+    assert lib.stq_prefill_states(1, 2, 128, 128, 0, None, *args[1:], None) == -1
+    assert lib.stq_prefill_states(0, 2, 128, 128, 0, *args, None) == 0          # nothing to do
+    for name, npt in (("stq_decode_readout", 7), ("stq_decode_commit", 6)):
+        f = getattr(lib, name)
+        f.restype = I
+        f.argtypes = [P, P, I] + [P] * npt + [P]
+        assert f(None, d, 1, *([d] * npt), None) == -1
