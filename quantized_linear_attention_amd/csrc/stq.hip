@@ -2198,7 +2198,7 @@ template <int DK, int DV>
 struct PKSmem {
   float kc[PL][DK], qc[PL][DK], ac[PL][DK];
   float vc[PL][DV];
-  float gb[PL];
+  float gb[PL], kq[PL];
 };
 
 template <int DK, int DV>
@@ -2295,15 +2295,18 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
       moved |= (an != 1.f) | (bn != 0.f);
     }
     lds_barrier();
-    // ---- gate products: thread s < PL runs down column s of rho, thread PL down gamma
-    if (tid < PL) {
+    // ---- gate products on the last wave (it has the fewest K K^T blocks): its
+    // lane s < PL runs down column s of rho, lane PL down gamma
+    const int gl0 = G::NT - 64;
+    if (tid >= gl0 && tid < gl0 + PL) {
+      const int sc = tid - gl0;
       float r = 1.f;
 #pragma unroll
       for (int t = 0; t < PL; t++) {
-        if (t > tid) r *= ps.ga[t];
-        ps.rt[t][tid] = t >= tid ? r : 0.f;
+        if (t > sc) r *= ps.ga[t];
+        ps.rt[t][sc] = t >= sc ? r : 0.f;
       }
-    } else if (tid == PL) {
+    } else if (tid == gl0 + PL) {
       float g = 1.f;
 #pragma unroll
       for (int t = 0; t < PL; t++) {
@@ -2522,8 +2525,15 @@ __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps
       moved |= bv != 0.f;
     }
     lds_barrier();
+    if (tid < Lc) {                                   // k.q of each token, once
+      float kq = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < DK; i++) kq = __builtin_fmaf(ps.kc[tid][i], ps.qc[tid][i], kq);
+      ps.kq[tid] = kq;
+    }
+    lds_barrier();
     for (int t = 0; t < Lc; t++) {
-      float uu[G::NCC], ww[G::NCC], kq = 0.f;
+      float uu[G::NCC], ww[G::NCC];
       f32x4 kr[G::NRC][2];
 #pragma unroll
       for (int c = 0; c < G::NCC; c++) uu[c] = ww[c] = 0.f;
@@ -2536,7 +2546,6 @@ __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps
           kr[rc][hf] = *(const f32x4*)&ps.kc[t][r0];
 #pragma unroll
           for (int i = 0; i < 4; i++) {
-            kq = __builtin_fmaf(kr[rc][hf][i], q4[i], kq);
 #pragma unroll
             for (int c = 0; c < G::NCC; c++) {
               const int e = 8 * (c * G::NRC + rc) + 4 * hf + i;
@@ -2546,7 +2555,7 @@ __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps
             }
           }
         }
-      kq = g4_sum(kq);
+      const float kq = ps.kq[t];
       const float bt = ps.gb[t];
       float dl[G::NCC];
 #pragma unroll
