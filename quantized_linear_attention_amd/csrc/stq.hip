@@ -2644,19 +2644,27 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   if (tb1 <= tb0) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
   float* S = A.S_out + ((size_t)ci * A.H + h) * DK * DV;
+  // the tile goes through LDS both ways (coalesced 16-byte accesses to memory)
+  float* st = &sh.p.kc[0][0];
+  static_assert(sizeof(PSmem<DK, DV>) >= sizeof(float) * DK * DV, "staging");
+  for (int f = tid; f < DK * DV / 4; f += G::NT) *(f32x4*)(st + 4 * f) = *(const f32x4*)(S + 4 * f);
+  lds_barrier();
   float Y[64];
 #pragma unroll
   for (int e = 0; e < 64; e++) {
     const int b = e >> 3, t = e & 7;
-    Y[e] = S[(size_t)erow(b % G::NRC, t, Gq) * DV + w * G::CPW + 16 * (b / G::NRC) + n16];
+    Y[e] = st[erow(b % G::NRC, t, Gq) * DV + w * G::CPW + 16 * (b / G::NRC) + n16];
   }
+  lds_barrier();
   if (KDA) prefill_tokens<DK, DV>(A, sh.k, Y, tb0, tb1, h);
   else prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
 #pragma unroll
   for (int e = 0; e < 64; e++) {
     const int b = e >> 3, t = e & 7;
-    S[(size_t)erow(b % G::NRC, t, Gq) * DV + w * G::CPW + 16 * (b / G::NRC) + n16] = Y[e];
+    st[erow(b % G::NRC, t, Gq) * DV + w * G::CPW + 16 * (b / G::NRC) + n16] = Y[e];
   }
+  lds_barrier();
+  for (int f = tid; f < DK * DV / 4; f += G::NT) *(f32x4*)(S + 4 * f) = *(const f32x4*)(st + 4 * f);
 }
 
 __global__ void k_debug_rcp(float* out) {
