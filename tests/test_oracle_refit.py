@@ -40,6 +40,56 @@ def test_rank1_closed_form(orc):
     assert orc.clip_events() == 0
 
 
+def load_refit_golden(name):
+    """A hand-derived refit example: rows of S, row weights w, row widths n,
+    and the expected E, stored sigma and c (as values) and codes Q."""
+    g = {"S": [], "Q": []}
+    for line in open(os.path.join(GOLD, name)):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, *rest = line.split()
+        if key in ("S", "Q"):
+            g[key].append([float(x) for x in rest])
+        else:
+            g[key] = [float(x) for x in rest]
+    return g
+
+
+REFIT_GOLDENS = ["refit_impact_weight_8bit.txt", "refit_row_factor_rne_8bit.txt",
+                 "refit_reciprocals_4bit.txt"]
+
+
+def check_refit_golden(refit, name):
+    """Run `refit` (oracle.refit's signature) on the golden's input; return the
+    list of outputs that differ from the hand derivation."""
+    g = load_refit_golden(name)
+    S = np.array(g["S"], np.float32)
+    w = np.array(g["w"], np.float32)
+    nb = np.array(g["n"], np.int32)
+    # the inputs are exact binary32 values
+    assert np.array_equal(S.astype(np.float64), np.array(g["S"])) and np.array_equal(w.astype(np.float64), g["w"])
+    sig, c, Q, E = refit(S, w, nb)
+    bad = []
+    if E != int(g["E"][0]):
+        bad.append("E")
+    if not np.array_equal(bf16(sig).astype(np.float64), g["sigma"]):
+        bad.append("sigma")
+    if not np.array_equal(bf16(c).astype(np.float64), g["c"]):
+        bad.append("c")
+    if not np.array_equal(Q, np.array(g["Q"], np.int64)):
+        bad.append("Q")
+    return bad
+
+
+@pytest.mark.parametrize("name", REFIT_GOLDENS)
+def test_refit_hand_derived(orc, name):
+    """Row-impact weights that differ per row, row factors that need bf16
+    round-to-nearest-even, and the reciprocal multiplies and exact-product
+    rounding of the column fit and the codes, each against a hand derivation."""
+    assert check_refit_golden(orc.refit, name) == []
+    assert orc.clip_events() == 0
+
+
 def _rand_tile(rng, dk, dv, spread=1.5):
     r = np.exp(rng.normal(0, spread, dk))
     c = np.exp(rng.normal(0, spread, dv))
