@@ -239,13 +239,18 @@ size_t stq_pool_bytes(const stq_pool_desc* desc);
  * enqueues on `stream` the header upload and the zeroing of all slots and
  * caches (an all-zero state: codes 0, scales 1, empty windows).  *out
  * receives a host handle.  The header's host staging copy lives in the
- * handle, so the upload may still be in flight when this returns. */
+ * handle, so the upload may still be in flight when this returns; the
+ * handle records an event after it (stq_pool_destroy waits for that event).
+ * STQ_ERR_HIP if the event, the upload or the zeroing launch fails. */
 stq_status stq_pool_create(const stq_pool_desc* desc, void* dev_buf, size_t bytes,
                            hipStream_t stream, stq_pool** out);
 
-/* Frees the host handle only (the device buffer stays the caller's).  Any
- * work enqueued through the handle may still be running; the handle itself
- * is not needed by it. */
+/* Frees the host handle only (the device buffer stays the caller's).  It
+ * first waits for the header upload that stq_pool_create enqueued (the
+ * upload reads the handle's staging copy); no other work is waited for:
+ * steps, stores and fetches enqueued through the handle may still be
+ * running, they do not read the handle.  STQ_ERR_HIP if that wait fails
+ * (the handle is freed all the same). */
 stq_status stq_pool_destroy(stq_pool* pool);
 
 /* Ingest: for each c < n, tile (slots_dev[c], h) := R(S_dev[c][h]) for every

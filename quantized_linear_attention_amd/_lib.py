@@ -98,12 +98,18 @@ def _stream(stream):
     return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
 
 
-def _dev(t, dtype, what):
-    import torch
+def _dev(t, dtype, what, numel=None, device=None):
+    """Device pointer of a contiguous CUDA tensor of `dtype`; with `numel`
+    and `device`, also checks its element count and device, so that no kernel
+    is handed a buffer shorter than the sizes it indexes."""
     if t is None:
         return None
     if not (t.is_cuda and t.is_contiguous() and t.dtype == dtype):
         raise StqError(-1, "%s must be a contiguous %s CUDA tensor" % (what, dtype))
+    if numel is not None and t.numel() != numel:
+        raise StqError(-1, "%s has %d elements, expected %d" % (what, t.numel(), numel))
+    if device is not None and t.device != device:
+        raise StqError(-1, "%s is on %s, the pool buffer on %s" % (what, t.device, device))
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -114,6 +120,16 @@ def stq_pool_bytes(desc):
 class _Pool:
     def __init__(self, handle, desc, buf):
         self.handle, self.desc, self.buf = handle, desc, buf
+        self.H, self.dk, self.dv = int(desc.n_heads), int(desc.d_k), int(desc.d_v)
+        self.gate, self.unit = int(desc.gate_kind), int(desc.unit_kind)
+        self.device = buf.device
+
+    def sizes(self, n):
+        """Element counts of the per-token tensors of a call on n requests."""
+        H, dk, dv = self.H, self.dk, self.dv
+        return {"q": n * H * dk, "k": n * H * dk, "v": n * H * dv, "o": n * H * dv,
+                "a": n * H * (dk if self.gate == STQ_GATE_CHANNEL else 1), "b": n * H,
+                "S": n * H * dk * dv}
 
     def __del__(self):
         if getattr(self, "handle", None):
@@ -137,40 +153,63 @@ def stq_pool_destroy(pool):
         pool.handle = None
 
 
-def _slots(slots):
+def _slots(slots, pool=None):
     import torch
-    return _dev(slots, torch.int32, "slots"), int(slots.numel())
+    return _dev(slots, torch.int32, "slots", device=None if pool is None else pool.device), int(slots.numel())
+
+
+def _token_args(pool, n, names, tensors):
+    """Pointers of the per-token tensors of a call on n requests (or n tokens),
+    each checked against the pool's sizes and device."""
+    import torch
+    want = pool.sizes(n)
+    return [_dev(t, torch.float32, nm, want[nm], pool.device) for nm, t in zip(names, tensors)]
 
 
 def stq_pool_store(pool, slots, S, stream=None):
-    import torch
-    sp, n = _slots(slots)
-    _check(_L.stq_pool_store(pool.handle, sp, n, _dev(S, torch.float32, "S"), _stream(stream)),
+    """S: fp32 [n][H][d_k][d_v] on the pool's device."""
+    sp, n = _slots(slots, pool)
+    _check(_L.stq_pool_store(pool.handle, sp, n, _token_args(pool, n, ["S"], [S])[0], _stream(stream)),
            "stq_pool_store")
 
 
 def stq_pool_fetch(pool, slots, S_out, stream=None):
-    import torch
-    sp, n = _slots(slots)
-    _check(_L.stq_pool_fetch(pool.handle, sp, n, _dev(S_out, torch.float32, "S_out"), _stream(stream)),
+    sp, n = _slots(slots, pool)
+    _check(_L.stq_pool_fetch(pool.handle, sp, n, _token_args(pool, n, ["S"], [S_out])[0], _stream(stream)),
            "stq_pool_fetch")
 
 
 def stq_decode_step(pool, slots, q, k, v, a, b, o, stream=None):
+    sp, n = _slots(slots, pool)
+    ptrs = _token_args(pool, n, "qkvabo", (q, k, v, a, b, o))
+    _check(_L.stq_decode_step(pool.handle, sp, n, *ptrs, _stream(stream)), "stq_decode_step")
+
+
+def _prompt_tokens(pool_or_dims, n, seq_start, q):
+    """Token count of a packed prompt batch, from q's size, and the checks that
+    need the start offsets: n + 1 entries, the last within the batch.  Reading
+    the last offset copies one int32 from the device (a synchronisation of
+    the current stream); the prefill is not on the per-token path."""
     import torch
-    f = torch.float32
-    sp, n = _slots(slots)
-    _check(_L.stq_decode_step(pool.handle, sp, n, _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"),
-                              _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"), _stream(stream)),
-           "stq_decode_step")
+    H, dk = pool_or_dims
+    if seq_start is None or seq_start.numel() != n + 1:
+        raise StqError(-1, "seq_start must have n + 1 = %d entries" % (n + 1))
+    if q is None or q.numel() % (H * dk):
+        raise StqError(-1, "q must be [tokens][H][d_k]")
+    tok = q.numel() // (H * dk)
+    _dev(seq_start, torch.int32, "seq_start", n + 1, q.device)
+    last = int(seq_start[-1].item()) if n else 0
+    if last > tok:
+        raise StqError(-1, "seq_start[n] = %d exceeds the %d tokens of q" % (last, tok))
+    return tok
 
 
 def stq_prefill(pool, slots, seq_start, q, k, v, a, b, o, stream=None):
     import torch
-    f = torch.float32
-    sp, n = _slots(slots)
-    _check(_L.stq_prefill(pool.handle, sp, n, _dev(seq_start, torch.int32, "seq_start"), _dev(q, f, "q"),
-                          _dev(k, f, "k"), _dev(v, f, "v"), _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"),
+    sp, n = _slots(slots, pool)
+    tok = _prompt_tokens((pool.H, pool.dk), n, seq_start, q)
+    ptrs = _token_args(pool, tok, "qkvabo", (q, k, v, a, b, o))
+    _check(_L.stq_prefill(pool.handle, sp, n, _dev(seq_start, torch.int32, "seq_start"), *ptrs,
                           _stream(stream)),
            "stq_prefill")
 
@@ -191,40 +230,47 @@ def stq_allocate_bits(err, half_life, n_pivots, budget_bits):
     return bits, obj.value
 
 
+class _Dims:
+    """Sizes of a plain-state prefill, laid out as a pool's would be."""
+    def __init__(self, H, dk, dv, gate, device):
+        self.H, self.dk, self.dv, self.gate, self.device = H, dk, dv, gate, device
+
+    sizes = _Pool.sizes
+
+
 def stq_prefill_states(S, seq_start, q, k, v, a, b, o, gate_kind=STQ_GATE_HEAD, stream=None):
     """S: contiguous fp32 CUDA tensor [n][H][d_k][d_v], advanced in place."""
     import torch
     f = torch.float32
+    if S is None or S.dim() != 4:
+        raise StqError(-1, "S must be [n][H][d_k][d_v]")
     n, H, dk, dv = S.shape
-    _check(_L.stq_prefill_states(n, H, dk, dv, gate_kind, _dev(S, f, "S"), _dev(seq_start, torch.int32, "seq_start"),
-                                 _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"), _dev(a, f, "a"), _dev(b, f, "b"),
-                                 _dev(o, f, "o"), _stream(stream)),
+    Sp = _dev(S, f, "S")
+    dims = _Dims(H, dk, dv, int(gate_kind), S.device)
+    tok = _prompt_tokens((H, dk), n, seq_start, q)
+    ptrs = _token_args(dims, tok, "qkvabo", (q, k, v, a, b, o))
+    _check(_L.stq_prefill_states(n, H, dk, dv, gate_kind, Sp, _dev(seq_start, torch.int32, "seq_start"), *ptrs,
+                                 _stream(stream)),
            "stq_prefill_states")
 
 
 def stq_decode_readout(pool, slots, q, k, v, a, b, o, stream=None):
-    import torch
-    f = torch.float32
-    sp, n = _slots(slots)
-    _check(_L.stq_decode_readout(pool.handle, sp, n, _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"),
-                                 _dev(a, f, "a"), _dev(b, f, "b"), _dev(o, f, "o"), _stream(stream)),
-           "stq_decode_readout")
+    sp, n = _slots(slots, pool)
+    ptrs = _token_args(pool, n, "qkvabo", (q, k, v, a, b, o))
+    _check(_L.stq_decode_readout(pool.handle, sp, n, *ptrs, _stream(stream)), "stq_decode_readout")
 
 
 def stq_decode_commit(pool, slots, q, k, v, a, b, stream=None):
-    import torch
-    f = torch.float32
-    sp, n = _slots(slots)
-    _check(_L.stq_decode_commit(pool.handle, sp, n, _dev(q, f, "q"), _dev(k, f, "k"), _dev(v, f, "v"),
-                                _dev(a, f, "a"), _dev(b, f, "b"), _stream(stream)),
-           "stq_decode_commit")
+    sp, n = _slots(slots, pool)
+    ptrs = _token_args(pool, n, "qkvab", (q, k, v, a, b))
+    _check(_L.stq_decode_commit(pool.handle, sp, n, *ptrs, _stream(stream)), "stq_decode_commit")
 
 
 def stq_window_flush(pool, slots, stream=None):
-    sp, n = _slots(slots)
+    sp, n = _slots(slots, pool)
     _check(_L.stq_window_flush(pool.handle, sp, n, _stream(stream)), "stq_window_flush")
 
 
 def stq_requant_fixed_scales(pool, slots, stream=None):
-    sp, n = _slots(slots)
+    sp, n = _slots(slots, pool)
     _check(_L.stq_requant_fixed_scales(pool.handle, sp, n, _stream(stream)), "stq_requant_fixed_scales")

@@ -2685,11 +2685,24 @@ struct stq_pool {
   uint32_t rows_stage;                  // per-key-row units: LDS bytes the step kernel stages
   uint8_t* dev;
   std::vector<uint8_t> header;  // host staging copy of the header
+  hipEvent_t upload = nullptr;  // recorded after the header upload that reads `header`
 };
 
 namespace {
 
 uint64_t ru256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+// Free a handle.  The header upload enqueued by create reads the handle's
+// staging copy: wait for it (recorded event) before that copy goes away.
+bool release(stq_pool* p) {
+  bool ok = true;
+  if (p->upload) {
+    ok = hipEventSynchronize(p->upload) == hipSuccess;
+    ok = hipEventDestroy(p->upload) == hipSuccess && ok;
+  }
+  delete p;
+  return ok;
+}
 uint64_t tile_stride(int n, int dk, int dv) {
   uint64_t b = (uint64_t)dk * dv * n / 8 + (n == 16 ? 0 : 2ull * (dk + dv));
   return ru256(b);
@@ -2941,22 +2954,27 @@ stq_status stq_pool_create(const stq_pool_desc* d, void* dev_buf, size_t bytes, 
       for (int i = 0; i < p->dk; i++) wr[(size_t)h * p->dk + i] = (uint8_t)b[i];
     }
   }
-  if (hipMemcpyAsync(p->dev, hb, p->hdr, hipMemcpyHostToDevice, stream) != hipSuccess) {
+  if (hipEventCreateWithFlags(&p->upload, hipEventDisableTiming) != hipSuccess) {
+    p->upload = nullptr;
     delete p;
+    return STQ_ERR_HIP;
+  }
+  if (hipMemcpyAsync(p->dev, hb, p->hdr, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipEventRecord(p->upload, stream) != hipSuccess) {
+    release(p);
     return STQ_ERR_HIP;
   }
   // zero state in every slot (codes 0, scales 1) and empty windows
   KArgs A = base_args(p, nullptr, p->n_slots);
   stq_status s = rows ? dispatch<LRows<RMODE_STORE>::T>(p, A, stream) : dispatch<LTile<MODE_STORE>::T>(p, A, stream);
-  if (s != STQ_OK) { delete p; return s; }
+  if (s != STQ_OK) { release(p); return s; }
   *out = p;
   return STQ_OK;
 }
 
 stq_status stq_pool_destroy(stq_pool* p) {
   if (!p) return STQ_ERR_ARG;
-  delete p;
-  return STQ_OK;
+  return release(p) ? STQ_OK : STQ_ERR_HIP;
 }
 
 stq_status stq_pool_store(stq_pool* p, const int32_t* slots, int32_t n, const float* S, hipStream_t st) {

@@ -122,3 +122,88 @@ def test_new_entry_points_reject_on_host(stq):
         f.restype = I
         f.argtypes = [P, P, I] + [P] * npt + [P]
         assert f(None, d, 1, *([d] * npt), None) == -1
+
+
+class _FakeCuda:
+    """Stands in for a CUDA tensor on a machine without a GPU: the binding's
+    size and device checks run before any pointer reaches the library."""
+    def __init__(self, numel, dtype, device="cuda:0"):
+        import torch
+        self._n, self.dtype, self.device = numel, dtype, torch.device(device)
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        return self._n
+
+    def data_ptr(self):
+        return 0x10000
+
+    def dim(self):
+        return 1
+
+
+def _fake_pool(stq, gate=0, window=0):
+    import torch
+    from quantized_linear_attention_amd import _lib
+    d = stq.make_desc(4, 2, 128, 64, [6, 8], np.ones(256), gate, 0, window)
+    return _lib._Pool(None, d, _FakeCuda(1 << 20, torch.uint8))
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_binding_rejects_short_or_misplaced_tensors(stq, gate):
+    """Every per-token tensor is checked against the pool's sizes (q, k: n H d_k;
+    v, o: n H d_v; a: n H or n H d_k by gate kind; b: n H; S: n H d_k d_v) and
+    the pool buffer's device before the library is called."""
+    import torch
+    f = torch.float32
+    pool = _fake_pool(stq, gate)
+    n, H, dk, dv = 3, 2, 128, 64
+    good = dict(q=n * H * dk, k=n * H * dk, v=n * H * dv, a=n * H * (dk if gate else 1), b=n * H, o=n * H * dv)
+    slots = _FakeCuda(n, torch.int32)
+    for name in good:
+        for wrong in (good[name] - 1, good[name] + 1):
+            args = {k: _FakeCuda(v, f) for k, v in good.items()}
+            args[name] = _FakeCuda(wrong, f)
+            with pytest.raises(stq.StqError, match=name):
+                stq.stq_decode_step(pool, slots, **args)
+            if name != "o":
+                with pytest.raises(stq.StqError, match=name):
+                    stq.stq_decode_commit(pool, slots, *[args[k] for k in "qkvab"])
+            with pytest.raises(stq.StqError, match=name):
+                stq.stq_decode_readout(pool, slots, **args)
+    # a per-head gate where the pool wants per-channel gates, and the reverse
+    other = n * H * (1 if gate else dk)
+    args = {k: _FakeCuda(v, f) for k, v in good.items()}
+    args["a"] = _FakeCuda(other, f)
+    with pytest.raises(stq.StqError, match="a has"):
+        stq.stq_decode_step(pool, slots, **args)
+    # another device than the pool buffer's
+    args = {k: _FakeCuda(v, f) for k, v in good.items()}
+    args["v"] = _FakeCuda(good["v"], f, "cuda:1")
+    with pytest.raises(stq.StqError, match="cuda:1"):
+        stq.stq_decode_step(pool, slots, **args)
+    with pytest.raises(stq.StqError, match="cuda:1"):
+        stq.stq_decode_step(pool, _FakeCuda(n, torch.int32, "cuda:1"), **{k: _FakeCuda(v, f) for k, v in good.items()})
+    # store / fetch: the whole state
+    for fn in (stq.stq_pool_store, stq.stq_pool_fetch):
+        with pytest.raises(stq.StqError, match="S has"):
+            fn(pool, slots, _FakeCuda(n * H * dk * dv - 1, f))
+
+
+def test_binding_rejects_bad_prompt_offsets(stq):
+    """Prefill: seq_start needs n + 1 entries; q must be whole tokens."""
+    import torch
+    f = torch.float32
+    pool = _fake_pool(stq)
+    slots = _FakeCuda(3, torch.int32)
+    tok = 10
+    sizes = dict(q=tok * 2 * 128, k=tok * 2 * 128, v=tok * 2 * 64, a=tok * 2, b=tok * 2, o=tok * 2 * 64)
+    args = {k: _FakeCuda(v, f) for k, v in sizes.items()}
+    with pytest.raises(stq.StqError, match="seq_start"):
+        stq.stq_prefill(pool, slots, _FakeCuda(3, torch.int32), **args)
+    args["q"] = _FakeCuda(sizes["q"] + 5, f)
+    with pytest.raises(stq.StqError, match="q must be"):
+        stq.stq_prefill(pool, slots, _FakeCuda(4, torch.int32), **args)
