@@ -111,7 +111,8 @@ BENCH = {
     "C3": {"layers": 4, "kernel": "k_tile<128, 128, 0>", "prof": "k_tile_step",
            "metric": "request-head decode steps/s (B=512, H=32, d=128, 6-bit nominal GDN pool)",
            "workload": "GDN serving pool B=512 H=32 d_k=d_v=128, heads {4b:9, 6b:16, 8b:6, fp16:1}",
-           "dtype": "f32 update, 4/6/8-bit + f16 state"},
+           "dtype": "f32 update and refit; the two matvecs on matrix cores with each f32 operand split into "
+                    "f16 hi + lo (f32 accumulation); 4/6/8-bit + f16 state"},
     "C4": {"layers": 8, "kernel": "k_rows_wide<128>", "prof": "k_rows_wide_step",
            "metric": "request-head decode steps/s (B=256, H=32, d=128, KDA per-channel gate, "
                      "per-key-row widths)",
@@ -125,7 +126,8 @@ BENCH = {
            "metric": "request-head decode steps/s (B=512, H=32, d=128, 4-bit GDN, window W=16)",
            "workload": "windowed GDN pool B=512 H=32 d_k=d_v=128, all heads 4-bit, W=16 "
                        "(binary32 window caches, one fold per 16 tokens)",
-           "dtype": "f32 update and window cache, 4-bit base state"},
+           "dtype": "f32 update and window cache; the base matvecs on matrix cores with each f32 operand "
+                    "split into f16 hi + lo (f32 accumulation); 4-bit base state"},
 }
 
 
@@ -138,7 +140,10 @@ def main():
     ap.add_argument("--prompt-len", type=int, default=1024, help="P3: tokens per prompt")
     ap.add_argument("--prompts", type=int, default=64, help="P3: prompts per prefill call")
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="P3/P4: seconds of oracle prefill timing")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="after the --warmup steps, keep stepping untimed until this much time has passed "
+                         "(clocks and caches settle; the count done is reported as warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n-comp", type=int, default=0,
                     help="window workloads: compensator rows per tile (0 = the workload as specified)")
@@ -225,9 +230,18 @@ def main():
         q, k, v, a, b = toks[(s // L) % NTOK]
         stq.stq_decode_step(pools[s % L], slots, q, k, v, a, b, o)
 
+    # untimed: the requested steps, then whole rounds over the layer pools (whole
+    # windows) until --warmup-seconds have passed
+    rnd = L * max(c.window, 16)
     for s in range(Wu):
         step(s)
     torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < args.warmup_seconds:
+        for s in range(Wu, Wu + rnd):
+            step(s)
+        Wu += rnd
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     if args.graph:
@@ -275,23 +289,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        oracle.build()
-        ns = 32 if key != "C4" else 16             # slots per oracle call
-        P = oracle.OraclePool(ns, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window, n_comp=C)
-        sl = np.arange(ns)
-        P.store(sl, wl.state(sl))
-        tk = [wl.token(t, ns) for t in range(NTOK)]
-        calls = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < args.cpu_seconds or (c.window and calls % c.window):
-            P.step(sl, *tk[calls % NTOK])
-            calls += 1
-        el = time.perf_counter() - t0
-        cpu = {"value": calls * ns * H / el, "unit": "request-head steps/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": "%d calls x %d tiles of the same workload (B=%d slots, all %d heads%s), %.1f s"
-                         % (calls, ns * H, ns, H, ", whole windows" if c.window else "", el)}
+        cpu = cpu_baseline(wl, bufs[0].cpu().numpy(), C, bytes_step)
 
     traffic = measured_traffic(key) if C == 0 else None
     line = {
@@ -318,6 +316,42 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def cpu_baseline(wl, image, C, bytes_step):
+    """The oracle on the full step of the same workload: every (request, head)
+    tile of one layer pool, starting from the GPU pool's own bytes (layer 0 as
+    the timed run left it).  All host threads: 1 untimed + 3 timed steps (a
+    window workload: one whole window of W steps, its fold included); then one
+    core: 1 timed step.  The oracle computes the update in binary64; the
+    figure is a reported baseline, not a target."""
+    import oracle
+    oracle.build()
+    c, B, H = wl.cfg, wl.B, wl.H
+    P = oracle.OraclePool(B, H, wl.dk, wl.dv, wl.bits, wl.row_weight, c.gate, c.unit, c.window,
+                          image=image, n_comp=C)
+    sl = np.arange(B)
+    n_timed = c.window if c.window else 3
+    tk = [wl.token(t) for t in range(min(n_timed + 1, 4))]
+    cores = oracle.num_threads()
+    P.step(sl, *tk[0])
+    t0 = time.perf_counter()
+    for t in range(n_timed):
+        P.step(sl, *tk[1 + t % (len(tk) - 1)])
+    el = time.perf_counter() - t0
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    P.step(sl, *tk[1])
+    el1 = time.perf_counter() - t1
+    oracle.set_num_threads(cores)
+    rate = n_timed * B * H / el
+    return {"value": rate, "unit": "request-head steps/s", "cores": cores, "kind": "oracle",
+            "gbs": rate / (B * H) * bytes_step / 1e9,
+            "one_core": {"value": B * H / el1, "unit": "request-head steps/s", "seconds": el1,
+                         "steps": 1},
+            "sample": "the full step: %d steps x %d tiles (B=%d, all %d heads%s) on %d threads in %.1f s "
+                      "after 1 untimed step; one core: 1 step in %.1f s"
+                      % (n_timed, B * H, B, H, ", one whole window" if c.window else "", cores, el, el1)}
 
 
 def split_timing(stq, torch, pools, slots, toks, o, L, K, Wu, wl, spec):
@@ -390,7 +424,17 @@ def split_timing(stq, torch, pools, slots, toks, o, L, K, Wu, wl, spec):
 
 PL = 32                     # tokens per chunk of the prefill kernel
 MFMA_F32_PEAK = 157.3       # TFLOP/s, dense binary32 matrix cores
-VALU_F32_PEAK = 157.3       # TFLOP/s, binary32 vector ALUs (the published figure counts packed pairs)
+# binary32 vector ALUs one lane-op at a time: 256 CUs x 4 SIMDs x 16 lanes x 2
+# (fma) x 2.4 GHz = 78.6 TFLOP/s (the published 157.3 counts packed pairs,
+# which this code does not issue)
+VALU_F32_PEAK = 78.6
+
+
+def method_flops(n_tok, H, dk, dv, per_channel):
+    """Flops the gated delta rule itself needs per token and head: u = S^T k,
+    o = S^T q and the rank-one update (2 d_k d_v each), plus the per-channel
+    gate's d_k d_v multiplies (a scalar gate folds into the products)."""
+    return n_tok * H * (6 + (1 if per_channel else 0)) * dk * dv
 
 
 def prefill_flops(n_tok, H, dk, dv):
@@ -467,8 +511,9 @@ def prefill_bench(args):
     per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(K)])
     total_ms = float(ev[0].elapsed_time(ev[K]))
     avg_ms = float(per.mean())
-    # P4: 7 vector flops per state element and token (gate, two column sums, update)
-    flops = T * H * 7 * dk * dv if kda else prefill_flops(T, H, dk, dv)
+    # the method's own work (the chunk form issues more: flops_issued)
+    flops = method_flops(T, H, dk, dv, kda)
+    issued = flops if kda else prefill_flops(T, H, dk, dv)
     tflops = flops / (avg_ms * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
@@ -504,7 +549,8 @@ def prefill_bench(args):
                      "peak": VALU_F32_PEAK if kda else MFMA_F32_PEAK, "unit": "TFLOP/s",
                      "frac": tflops / (VALU_F32_PEAK if kda else MFMA_F32_PEAK), "traffic": None,
                      "kernel": "k_prefill<128, 128, %s>" % ("true" if kda else "false"),
-                     "flops_per_launch": flops, "avg_launch_ms": avg_ms,
+                     "flops_per_launch": flops, "flops_issued_per_launch": issued,
+                     "issued_tflops": issued / (avg_ms * 1e-3) / 1e12, "avg_launch_ms": avg_ms,
                      "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
                      "hbm_gbs": (T * H * (4 * (2 * dk + 2 * dv) + 8)) / (avg_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,

@@ -12,7 +12,7 @@ _CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fexcess-precision=standard"
            "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
 
 __all__ = ["build", "lib", "refit", "dequant", "requant_fixed", "pack", "unpack",
-           "tile_bytes", "tile_stride", "update_f64", "pack_rows", "unpack_rows", "row_tile_bytes", "OraclePool", "num_threads", "clip_events"]
+           "tile_bytes", "tile_stride", "update_f64", "pack_rows", "unpack_rows", "row_tile_bytes", "OraclePool", "num_threads", "set_num_threads", "clip_events"]
 
 
 def build(force=False):
@@ -57,6 +57,7 @@ def lib():
         L.orc_prefill.argtypes = D + [P, P, I, P, P, P, P, P, P, P, P]
         L.orc_update_f64.argtypes = [I, I, P, P, P, P, P, I, ctypes.c_double, P, P]
         L.orc_num_threads.restype = I
+        L.orc_set_threads.argtypes = [I]
         L.orc_clip_events.restype = ctypes.c_long
         _lib = L
     return _lib
@@ -72,6 +73,11 @@ def _c(a, dt):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the oracle's parallel loops over tiles (timing only)."""
+    lib().orc_set_threads(int(n))
 
 
 def clip_events():

@@ -877,6 +877,16 @@ void orc_window_flush(DESC_ARGS, uint8_t* img, const int32_t* slots, int n) {
   }
 }
 
+/* Threads of the parallel loops over tiles (timing only; results do not
+ * depend on it). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
