@@ -220,17 +220,18 @@ def test_prefill_unsupported_and_empty(torch_cuda, orc):
     import quantized_linear_attention_amd as stq
     say("case prefill unsupported pools, n = 0")
     f = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda")
-    ss = torch.zeros(2, dtype=torch.int32, device="cuda")
-    for key in ("C4",):                            # per-key-row units
+    for key in ("C4",):                            # per-key-row units: one request, no tokens
         wl = Workload(key, B=1, H=2)
         P = Pair(orc, wl, n_slots=1)
+        ss = torch.zeros(2, dtype=torch.int32, device="cuda")
         with pytest.raises(stq.StqError) as e:
-            stq.stq_prefill(P.pool, P.slots_t([0]), ss, f(1), f(1), f(1), f(1), f(1), f(1))
+            stq.stq_prefill(P.pool, P.slots_t([0]), ss, f(0), f(0), f(0), f(0), f(0), f(0))
         assert e.value.status == -5
     wl = Workload("C2", B=1, H=2)
     P = Pair(orc, wl, n_slots=1)
     pre = P.image()
-    stq.stq_prefill(P.pool, P.slots_t(np.zeros(0, np.int32)), ss, f(1), f(1), f(1), f(1), f(1), f(1))
+    ss = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stq.stq_prefill(P.pool, P.slots_t(np.zeros(0, np.int32)), ss, f(0), f(0), f(0), f(0), f(0), f(0))
     assert np.array_equal(P.image(), pre)
 
 

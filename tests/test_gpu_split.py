@@ -93,9 +93,12 @@ def test_split_unsupported(torch_cuda, orc):
     for key in ("C4", "C5"):
         wl = Workload(key, B=1, H=2)
         P = Pair(orc, wl, n_slots=1)
+        dk, dv = wl.dk, wl.dv
+        q, k, v, o = f(2 * dk), f(2 * dk), f(2 * dv), f(2 * dv)
+        a, b = f(2 * (dk if wl.cfg.gate else 1)), f(2)
         with pytest.raises(stq.StqError) as e:
-            stq.stq_decode_readout(P.pool, P.slots_t([0]), f(1), f(1), f(1), f(1), f(1), f(1))
+            stq.stq_decode_readout(P.pool, P.slots_t([0]), q, k, v, a, b, o)
         assert e.value.status == -5
         with pytest.raises(stq.StqError) as e:
-            stq.stq_decode_commit(P.pool, P.slots_t([0]), f(1), f(1), f(1), f(1), f(1))
+            stq.stq_decode_commit(P.pool, P.slots_t([0]), q, k, v, a, b)
         assert e.value.status == -5
