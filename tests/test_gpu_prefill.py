@@ -9,15 +9,24 @@ S_T.  Bar (written here):
     each code is the nearest one to the exact state up to the binary32 error of
     the evaluation;
   - codes against the oracle's R(fl32(S_T)): every difference <= 1 step and at
-    most 2% of the codes differ (only codes whose exact value lies within that
-    binary32 error of a rounding boundary, or rows whose bf16 scale does, can);
+    most 1e-4 of the codes differ (only codes whose exact value lies within
+    that binary32 error of a rounding boundary, or rows whose bf16 scale does,
+    can; the error is about (T/L)(d_k + L) unit roundoffs of the tile's scale,
+    1e-5 at T = 300, so a code sits that close to a boundary about once in 1e5:
+    0-27 differing codes of up to 2.5 million were measured);
+  - row and column scales (as the steps they define) each within one bf16
+    step, at most 1e-3 of them differing: a scale's input is a row or column
+    absmax, which carries the evaluation's error relative to the tile's scale
+    while being smaller than it, and sits on a 2^-8-relative bf16 grid, so it
+    lands within that error of a rounding boundary more often than a code
+    does (measured: at most 2 of 15,872);
   - empty requests and requests of identity tokens leave their tiles' bytes
     (window pools: their folded windows are compared like the rest).
 """
 import numpy as np
 import pytest
 
-from gpu_util import Pair, compare_codes, readout_ok, say
+from gpu_util import Pair, agg_text, compare_codes, readout_ok, say
 from workloads import Workload
 
 pytestmark = pytest.mark.gpu
@@ -70,6 +79,18 @@ def _state_ok(orc, ref, img, slots, S_fin, moved):
     return worst
 
 
+CODE_MAX = 1e-4
+SCALE_MAX = 1e-3
+
+
+def _assert_prefill_codes(res):
+    assert res["maxd"] <= 1
+    assert res["mism"] <= CODE_MAX * max(res["codes"], 1)
+    assert res["piv_bad"] == 0
+    assert res["scale_mism"] <= SCALE_MAX * max(res["scales"], 1)
+    assert res["scale_steps"] <= 1
+
+
 def _check(P, wl, slots, lens, pre, img, ref, o, o_ref, S_fin, ss, moved):
     T = int(ss[-1])
     if T:
@@ -83,9 +104,8 @@ def _check(P, wl, slots, lens, pre, img, ref, o, o_ref, S_fin, ss, moved):
     mv = [s for c, s in enumerate(slots) if moved[c] or ref.W]
     if mv:
         res = compare_codes(P.orc, ref, img, ref.img, mv)
-        say("  codes", res)
-        assert res["maxd"] <= 1 and res["mism"] <= 0.02 * res["codes"]
-        assert res["piv_bad"] == 0
+        say("  " + agg_text(res))
+        _assert_prefill_codes(res)
     H = wl.H
     for c, s in enumerate(slots):
         if not moved[c] and not ref.W:
@@ -301,5 +321,5 @@ def test_prefill_states_per_key_row_pool(torch_cuda, orc):
     say("  readout worst ratio %.3g" % r)
     assert r <= 1.0
     res = compare_codes(orc, ref, P.image(), ref.img, slots)
-    say("  codes", res)
-    assert res["maxd"] <= 1 and res["mism"] <= 0.02 * res["codes"] and res["piv_bad"] == 0
+    say("  " + agg_text(res))
+    _assert_prefill_codes(res)

@@ -244,3 +244,26 @@ def test_refit_of_decode_drift_is_small(orc, n):
     print("R(D(R(S))) drift n=%d: %.4f of codes moved, max |dQ| %d"
           % (n, moved, np.abs(Q2 - Q).max()))
     assert moved < 0.25
+
+
+def test_refit_of_decoded_tile_is_not_idempotent(orc):
+    """Why no exact 'refit of a decoded tile keeps its codes' invariant exists
+    under these readings, even holding the row scales: the column scale is
+    rounded UP to bf16 from the column's absmax, and a decoded column's absmax
+    sits below the one it was fitted to.  Worked by hand on a 1 x 1, 8-bit tile:
+      S = 1: s = 1, E = 0; M = fl(1/127) = 8454660 * 2^-30 -> t = 130 * 2^-14,
+        Q = rne(1 * fl(16384/130)) = rne(126.03) = 126;
+      D: fl(130 * 2^-14) * 126 = 16380 * 2^-14 = 4095/4096;
+      refit of 4095/4096: s = bf16(sqrt(4095/4096)) = bf16(0.99988) = 1 (same row
+        scale), M = fl(4095/4096 * fl(1/127)) = 2^-7 * 1.00763 -> t' = 129 * 2^-14,
+        Q' = rne(4095/4096 * fl(16384/129)) = rne(126.98) = 127.
+    The row scale is unchanged, yet c and Q both move.  The exact invariant that
+    does hold, requantizing against the stored scales, is checked in
+    test_dequant_exact_and_fixed_scale_roundtrip."""
+    sig, c, Q, E = orc.refit(np.array([[1.0]], np.float32), np.ones(1, np.float32), 8)
+    assert E == 0 and bf16(sig)[0] == 1.0 and bf16(c)[0] == 130 * 2.0 ** -14 and Q[0, 0] == 126
+    D = orc.dequant(sig, c, Q, 8)
+    assert D[0, 0] == np.float32(4095 / 4096)
+    sig2, c2, Q2, E2 = orc.refit(D, np.ones(1, np.float32), 8)
+    assert E2 == 0 and bf16(sig2)[0] == 1.0                       # row scale held
+    assert bf16(c2)[0] == 129 * 2.0 ** -14 and Q2[0, 0] == 127     # column scale and code moved
