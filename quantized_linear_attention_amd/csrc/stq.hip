@@ -687,6 +687,7 @@ struct WSmem {
   // not written before the fold's last read, whenever it fits there
   static constexpr bool IN_PART = WMAX * DK <= DK * GeoM<DK, DV>::PSTR;
   float kap[IN_PART ? 4 : WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i)
+  float vt[DV] __attribute__((aligned(16)));                         // the token's v (fold of a filling token)
 };
 
 // LDS of the readout-and-append kernel
@@ -752,7 +753,13 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
 #pragma unroll
   for (int q = 0; q < NS; q++) pin(sgl[q]);
   pin(sg); pin(kk); pin(qq);
-  if (t >= W) return;                          // full: only the fold may touch it
+  if (t + 1 >= W) {
+    // this token fills the window: the fold kernel that runs next does its
+    // readout, update and refit in one pass over the base and the cache.  The
+    // count W marks the token as pending there (W - 1 entries are cached).
+    if (tid == 0 && t + 1 == W) *cntp = W;
+    return;
+  }
   const float Gt = t ? Gc[t - 1] * a : a;      // binary32 running product
   float sc, inv;
   {
@@ -884,10 +891,18 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
 }
 
 // Fold of a tile's open window: S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T, refit,
-// window emptied.  Folds windows holding at least `need` tokens.
-template <int DK, int DV, int N, bool COMP>
+// window emptied.  ns: tokens in the window.  TOK: the window holds ns = W - 1
+// tokens and token x of the call fills it.  That token runs here, on the
+// materialised state: with G_t = fl(G_{ns} a) and g_i = G_t sigma_i,
+//   u_t = b (v - sum_i g_i k_i Y_ij),  o_t = sum_i g_i q_i Y_ij + (k.q) u_t,
+//   Y_ij += (k_i / g_i) u_t,j,
+// Y = S / (G_{ns} sigma) before the token and S / (G_t sigma) after it: the
+// readout kernel's window formula and the fold's materialised state, written
+// as one pass.  The token's (G_t, k_t, u_t) go to the cache as an append
+// would write them, then the window is emptied.
+template <int DK, int DV, int N, bool COMP, bool TOK = false>
 __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK, DV>& ws, uint8_t* tile,
-                                            uint8_t* cache, int h, int ns) {
+                                            uint8_t* cache, int h, int ns, size_t x = 0) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
   constexpr bool PIV = (N == 16);
@@ -903,10 +918,21 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   float* Kc = (float*)(cache + 256);
   float* Uc = Kc + (size_t)W * DK;
   float* kap = WSmem<DK, DV>::IN_PART ? sm.part : ws.kap;
-  // ns: tokens in the window (read by the caller), 1 <= ns <= W.  The base's
-  // compensators ride along as nc more tokens s = ns + c: k = e_row, G = 1
-  // relative to the window's start, u = the kept row (W + C <= 32)
-  const float Gt = Gc[ns - 1];
+  // ns: tokens in the window (read by the caller), 1 <= ns <= W (TOK: 0 <= ns
+  // = W - 1).  The base's compensators ride along as nc more tokens s = ns +
+  // c: k = e_row, G = 1 relative to the window's start, u = the kept row
+  // (W + C <= 32)
+  float Gt = ns ? Gc[ns - 1] : 1.f;
+  float kk = 0.f, qq = 0.f, vt = 0.f, bb = 0.f;
+  if constexpr (TOK) {
+    const size_t xu = (size_t)__builtin_amdgcn_readfirstlane((int)x);
+    const float a = ld_const(A.a + xu);          // the tile's gate and b: scalar loads
+    bb = ld_const(A.b + xu);
+    kk = A.k[xu * DK + rho];
+    qq = A.q[xu * DK + rho];
+    if (tid < DV) vt = A.v[xu * DV + tid];
+    Gt = ns ? Gt * a : a;                        // binary32 running product, as the readout's
+  }
   const int nc = PIV || !COMP ? 0 : A.C;
   const int32_t* cidx = (const int32_t*)(cache + 192);
   const float* cval = (const float*)(cache + 256 + 4 * (size_t)W * (DK + DV));
@@ -942,6 +968,24 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
     sg4[it] = on && !PIV ? *(const u32x2*)(scl + r0) : u32x2{0x3F803F80u, 0x3F803F80u};
   }
   if (rsub == 0) sm.gg[rho] = Gt * bf16f(sgr);
+  if constexpr (TOK) {
+    // the token's per-row factors: g k, g q and k / g (kappa, rowh: free until
+    // the refit), and k.q; v to LDS; the token's k and G to the cache now (an
+    // entry past the ones read below)
+    float kq = 0.f;
+    if (rsub == 0) {
+      const float g = Gt * bf16f(sgr);
+      sm.kappa[0][rho] = g * kk;
+      sm.kappa[1][rho] = g * qq;
+      sm.rowh[rho] = kk / g;
+      kq = kk * qq;
+      Kc[(size_t)ns * DK + rho] = kk;
+    }
+    if (tid < DV) ws.vt[tid] = vt;
+    if (tid == 0) Gc[ns] = Gt;
+    kq = wave_sum(kq);
+    if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
+  }
 #pragma unroll
   for (int it = 0; it < KP; it++) {
     const int j = tid + it * G::NT;
@@ -989,9 +1033,66 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
       for (int c = 0; c < G::NCC; c++) {
         const int e0 = 8 * (c * G::NRC + rc) + 4 * hf;
 #pragma unroll
-        for (int i = 0; i < 4; i++) Y[e0 + i] = PIV ? Gt * C[c][i] : C[c][i];
+        for (int i = 0; i < 4; i++) Y[e0 + i] = C[c][i];
       }
     }
+  if constexpr (TOK) {
+    float kqs = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
+    float pu[G::NCC], pw[G::NCC], dl[G::NCC];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) pu[c] = pw[c] = 0.f;
+    // one 16-row block of factors at a time: each block's LDS reads wait for
+    // the previous block's sums, so they are not all hoisted (registers)
+    int fo = 4 * erow(0, 0, Gq);
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++) {
+        const int bo = fo + 4 * (32 * rc + 16 * hf);
+        const f32x4 fk4 = *(const f32x4*)((const uint8_t*)sm.kappa[0] + bo);
+        const f32x4 fq4 = *(const f32x4*)((const uint8_t*)sm.kappa[1] + bo);
+#pragma unroll
+        for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int e = 8 * (c * G::NRC + rc) + 4 * hf + i;
+            pu[c] = __builtin_fmaf(fk4[i], Y[e], pu[c]);
+            pw[c] = __builtin_fmaf(fq4[i], Y[e], pw[c]);
+          }
+        asm volatile("" : "+v"(fo) : "v"(pu[0]), "v"(pw[G::NCC - 1]));
+      }
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) {
+      const int j = w * G::CPW + 16 * c + n16;
+      dl[c] = bb * (ws.vt[j] - g4_sum(pu[c]));  // the same bits in the four lane quads
+      const float wq = g4_sum(pw[c]);
+      if (Gq == 0) {
+        A.o[x * DV + j] = __builtin_fmaf(dl[c], kqs, wq);
+        Uc[(size_t)ns * DV + j] = dl[c];                    // the token's entry, as an append writes it
+      }
+    }
+    int ko = 4 * erow(0, 0, Gq);
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++) {
+        const f32x4 kc4 = *(const f32x4*)((const uint8_t*)sm.rowh + ko + 4 * (32 * rc + 16 * hf));
+#pragma unroll
+        for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int e = 8 * (c * G::NRC + rc) + 4 * hf + i;
+            Y[e] = __builtin_fmaf(kc4[i], dl[c], Y[e]);
+          }
+        asm volatile("" : "+v"(ko) : "v"(Y[8 * rc + 4 * hf]));
+      }
+  }
+  if constexpr (PIV) {                           // a binary16 pivot tile refits S itself
+#pragma unroll
+    for (int e = 0; e < 64; e++) Y[e] = Gt * Y[e];
+  }
   if (tid == 0) *cntp = 0;
   if constexpr (WSmem<DK, DV>::IN_PART) lds_barrier();     // kappa reads done before the partials
   if (COMP) comp_extract<DK, DV>(sm, Y, true, cache, W, A.C, !PIV);
@@ -1020,10 +1121,12 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   }
 }
 
-// Fold.  STEP (after a decode step): a workgroup reads the window counts of
-// FPW tiles of the call, one per lane, and folds the full ones in turn; an
-// empty launch costs one wave of small workgroups.  Flush: one tile per
-// workgroup, any non-empty window.
+// Fold.  STEP (after the readout kernel of a decode step): a workgroup reads
+// the window counts of FPW tiles of the call, one per lane; a count of W marks
+// a tile whose window this call's token fills (the readout kernel left the
+// token to this kernel), and the workgroup runs the token on those tiles in
+// turn (window_fold<..., TOK>).  An empty launch costs one wave of small
+// workgroups.  Flush: one tile per workgroup, any non-empty window.
 constexpr int FPW = 16;
 template <int DK, int DV, bool STEP, bool COMP>
 __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_window_fold(KArgs A) {
@@ -1031,7 +1134,6 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   __shared__ WSmem<DK, DV> ws;
   const int T = A.n * A.H;
   const int t0 = STEP ? (int)blockIdx.x * FPW : tile_of_block(T);
-  const int need = STEP ? A.W : 1;
   uint64_t mask;
   int cnt = 0;                                   // lane i: window count of tile t0 + i
   {
@@ -1042,7 +1144,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
       if ((unsigned)slot < (unsigned)A.n_slots)
         cnt = *(const int32_t*)(A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride);
     }
-    mask = __ballot(cnt >= need && cnt > 0);
+    mask = __ballot(STEP ? cnt == A.W : cnt > 0);
   }
   bool first = true;
   while (mask) {
@@ -1056,11 +1158,20 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     const int ns = __builtin_amdgcn_readlane(cnt, i);
     if (!first) __syncthreads();               // the previous fold's LDS reads are done
     first = false;
-    switch (A.head_bits[h]) {
-      case 4: window_fold<DK, DV, 4, COMP>(A, sm, ws, tile, cache, h, ns); break;
-      case 6: window_fold<DK, DV, 6, COMP>(A, sm, ws, tile, cache, h, ns); break;
-      case 8: window_fold<DK, DV, 8, COMP>(A, sm, ws, tile, cache, h, ns); break;
-      default: window_fold<DK, DV, 16, COMP>(A, sm, ws, tile, cache, h, ns); break;
+    if constexpr (STEP) {
+      switch (A.head_bits[h]) {
+        case 4: window_fold<DK, DV, 4, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+        case 6: window_fold<DK, DV, 6, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+        case 8: window_fold<DK, DV, 8, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+        default: window_fold<DK, DV, 16, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+      }
+    } else {
+      switch (A.head_bits[h]) {
+        case 4: window_fold<DK, DV, 4, COMP>(A, sm, ws, tile, cache, h, ns); break;
+        case 6: window_fold<DK, DV, 6, COMP>(A, sm, ws, tile, cache, h, ns); break;
+        case 8: window_fold<DK, DV, 8, COMP>(A, sm, ws, tile, cache, h, ns); break;
+        default: window_fold<DK, DV, 16, COMP>(A, sm, ws, tile, cache, h, ns); break;
+      }
     }
   }
 }
@@ -2837,10 +2948,11 @@ void launch_window(const KArgs& A, bool step, hipStream_t st) {
     else
       hipLaunchKernelGGL((k_window_read<DK, DV, false>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), lds, st, A);
     const unsigned T = (unsigned)A.n * (unsigned)A.H;
+    const unsigned g = (T + FPW - 1) / FPW;
     if (A.C > 0)
-      hipLaunchKernelGGL((k_window_fold<DK, DV, true, true>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
+      hipLaunchKernelGGL((k_window_fold<DK, DV, true, true>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
     else
-      hipLaunchKernelGGL((k_window_fold<DK, DV, true, false>), dim3((T + FPW - 1) / FPW), dim3(GeoM<DK, DV>::NT), 0, st, A);
+      hipLaunchKernelGGL((k_window_fold<DK, DV, true, false>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
   } else if (A.C > 0) {
     hipLaunchKernelGGL((k_window_fold<DK, DV, false, true>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
   } else {
