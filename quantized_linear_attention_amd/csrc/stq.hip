@@ -690,6 +690,10 @@ struct WSmem {
   float vt[DV] __attribute__((aligned(16)));                         // the token's v (fold of a filling token)
 };
 
+// bytes per staged u row of the readout kernel (d_v + 16 floats: padding
+// that spreads the rows read together over the LDS banks)
+constexpr int wread_urs(int dv) { return 4 * (dv + 16); }
+
 // LDS of the readout-and-append kernel
 template <int DK, int DV>
 struct WRead {
@@ -715,6 +719,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
   uint8_t* codes = tile;
   const uint16_t* scl = (const uint16_t*)(tile + DK * DV * N / 8);
   const int W = A.W;
+  constexpr int URS = wread_urs(DV);
   int32_t* cntp = (int32_t*)cache;
   float* Gc = (float*)(cache + 4);
   float* Kc = (float*)(cache + 256);
@@ -791,20 +796,29 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
       if (off < nk)
         __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Kc + off), (lptr_t)((uint8_t*)cst + c * 1024), 16, 0, 2);
     }
-    for (int c = wu; c < (nu + 1023) / 1024; c += G::NW) {
-      const int off = c * 1024 + 16 * l;
-      if (off < nu)
-        __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + off),
-                                         (lptr_t)((uint8_t*)cst + W * DK * 4 + c * 1024), 16, 0, 2);
-    }
+    // u rows go to a padded stride (d_v + 16 floats): the combine loop's four
+    // lane quads read four rows at one column, which would otherwise share
+    // banks.  One load per row (LPR lanes of 16 bytes each), RPI rows per wave
+    // and pass; a lane's data lands at the uniform base + 16 * lane.
+    constexpr int LPR = DV / 4, RPI = 64 / LPR;
+    uint8_t* ub = (uint8_t*)cst + W * DK * 4;
+    for (int c = wu; c * RPI < t; c += G::NW)
+#pragma unroll
+      for (int k = 0; k < RPI; k++) {
+        const int r = c * RPI + k;
+        if (r < t && l / LPR == k)
+          __builtin_amdgcn_global_load_lds((gptr_t)(Uc + (size_t)r * DV + 4 * (l % LPR)),
+                                           (lptr_t)(ub + r * URS - 16 * LPR * k), 16, 0, 2);
+      }
     // the compensator values [C][d_v] follow the W cached u rows, here and in memory
-    const int ncb = nc * DV * 4;
-    for (int c = wu; COMP && c < (ncb + 1023) / 1024; c += G::NW) {
-      const int off = c * 1024 + 16 * l;
-      if (off < ncb)
-        __builtin_amdgcn_global_load_lds((gptr_t)((const uint8_t*)Uc + W * DV * 4 + off),
-                                         (lptr_t)((uint8_t*)cst + W * (DK + DV) * 4 + c * 1024), 16, 0, 2);
-    }
+    for (int c = wu; COMP && c * RPI < nc; c += G::NW)
+#pragma unroll
+      for (int k = 0; k < RPI; k++) {
+        const int r = c * RPI + k;
+        if (r < nc && l / LPR == k)
+          __builtin_amdgcn_global_load_lds((gptr_t)(Uc + (size_t)(W + r) * DV + 4 * (l % LPR)),
+                                           (lptr_t)(ub + (W + r) * URS - 16 * LPR * k), 16, 0, 2);
+      }
   }
   // (G_t/G_s) k_s.k_t and (G_t/G_s) k_s.q_t, 8 consecutive lanes per token
   constexpr int DP = (WMAX + G::NT / 8 - 1) / (G::NT / 8);    // passes
@@ -868,7 +882,7 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
     const int ur = !on ? 0 : (s < t ? s : W + s - t);
 #pragma unroll
     for (int c = 0; c < G::NCC; c++) {
-      const float u = on ? cst[W * DK + ur * DV + w * G::CPW + 16 * c + n16] : 0.f;
+      const float u = on ? cst[W * DK + ur * (URS / 4) + w * G::CPW + 16 * c + n16] : 0.f;
       pk[c] = __builtin_fmaf(fk, u, pk[c]);
       pq[c] = __builtin_fmaf(fq, u, pq[c]);
     }
@@ -1099,11 +1113,11 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   refit_store<DK, DV, N, false, true>(sm, Y, tile, wgt);
 }
 
-// readout and append of every tile of the call
-template <int DK, int DV, bool COMP>
-__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(7))) void k_window_read(KArgs A) {
-  __shared__ WRead<DK, DV> sm;
-  extern __shared__ float cst_[];               // W (d_k + d_v) floats: the staged window cache
+// readout and append of every tile of the call.  NARROW: every head of the
+// pool is 4-bit (the pages' window variant); that path fits 7 waves per SIMD
+// without spilling.  Other pools take the full kernel at 6 waves.
+template <int DK, int DV, bool COMP, bool NARROW>
+__device__ __forceinline__ void window_read_tile(const KArgs& A, WRead<DK, DV>& sm, float* cst) {
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
@@ -1113,12 +1127,20 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
   uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
   const size_t x = (size_t)ci * A.H + h;
-  switch (A.head_bits[h]) {
-    case 4: window_read<DK, DV, 4, COMP>(A, sm, cst_, tile, cache, x); break;
-    case 6: window_read<DK, DV, 6, COMP>(A, sm, cst_, tile, cache, x); break;
-    case 8: window_read<DK, DV, 8, COMP>(A, sm, cst_, tile, cache, x); break;
-    default: window_read<DK, DV, 16, COMP>(A, sm, cst_, tile, cache, x); break;
+  const int n = A.head_bits[h];
+  if (NARROW || n == 4) {
+    window_read<DK, DV, 4, COMP>(A, sm, cst, tile, cache, x);
+  } else if constexpr (!NARROW) {
+    if (n == 6) window_read<DK, DV, 6, COMP>(A, sm, cst, tile, cache, x);
+    else if (n == 8) window_read<DK, DV, 8, COMP>(A, sm, cst, tile, cache, x);
+    else window_read<DK, DV, 16, COMP>(A, sm, cst, tile, cache, x);
   }
+}
+template <int DK, int DV, bool COMP, bool NARROW>
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(NARROW ? 7 : 6))) void k_window_read(KArgs A) {
+  __shared__ WRead<DK, DV> sm;
+  extern __shared__ float cst_[];               // W (d_k + d_v) floats: the staged window cache
+  window_read_tile<DK, DV, COMP, NARROW>(A, sm, cst_);
 }
 
 // Fold.  STEP (after the readout kernel of a decode step): a workgroup reads
@@ -2940,13 +2962,14 @@ stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st)
 }
 // window mode: readout and append, then the fold of full windows (or, for a flush, of any open one)
 template <int DK, int DV>
-void launch_window(const KArgs& A, bool step, hipStream_t st) {
+void launch_window(const KArgs& A, bool step, bool narrow, hipStream_t st) {
   if (step) {
-    const size_t lds = ((size_t)A.W * (DK + DV) + (size_t)A.C * DV) * 4;
-    if (A.C > 0)
-      hipLaunchKernelGGL((k_window_read<DK, DV, true>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), lds, st, A);
-    else
-      hipLaunchKernelGGL((k_window_read<DK, DV, false>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), lds, st, A);
+    const size_t lds = (size_t)A.W * DK * 4 + (size_t)(A.W + A.C) * wread_urs(DV);
+    const dim3 rg(grid_of(A.n, A.H)), rb(GeoM<DK, DV>::NT);
+    if (A.C > 0 && narrow) hipLaunchKernelGGL((k_window_read<DK, DV, true, true>), rg, rb, lds, st, A);
+    else if (A.C > 0) hipLaunchKernelGGL((k_window_read<DK, DV, true, false>), rg, rb, lds, st, A);
+    else if (narrow) hipLaunchKernelGGL((k_window_read<DK, DV, false, true>), rg, rb, lds, st, A);
+    else hipLaunchKernelGGL((k_window_read<DK, DV, false, false>), rg, rb, lds, st, A);
     const unsigned T = (unsigned)A.n * (unsigned)A.H;
     const unsigned g = (T + FPW - 1) / FPW;
     if (A.C > 0)
@@ -2960,10 +2983,12 @@ void launch_window(const KArgs& A, bool step, hipStream_t st) {
   }
 }
 stq_status dispatch_window(const stq_pool* p, const KArgs& A, bool step, hipStream_t st) {
-  if (p->dk == 128 && p->dv == 128) launch_window<128, 128>(A, step, st);
-  else if (p->dk == 64 && p->dv == 64) launch_window<64, 64>(A, step, st);
-  else if (p->dk == 64 && p->dv == 128) launch_window<64, 128>(A, step, st);
-  else launch_window<128, 64>(A, step, st);
+  bool narrow = true;                            // only 4-bit heads
+  for (int h = 0; h < p->H; h++) narrow = narrow && p->bits[h] == 4;
+  if (p->dk == 128 && p->dv == 128) launch_window<128, 128>(A, step, narrow, st);
+  else if (p->dk == 64 && p->dv == 64) launch_window<64, 64>(A, step, narrow, st);
+  else if (p->dk == 64 && p->dv == 128) launch_window<64, 128>(A, step, narrow, st);
+  else launch_window<128, 64>(A, step, narrow, st);
   return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
 }
 template <bool REQ>
