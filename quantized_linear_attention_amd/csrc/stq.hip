@@ -991,7 +991,7 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
       const float g = Gt * bf16f(sgr);
       sm.kappa[0][rho] = g * kk;
       sm.kappa[1][rho] = g * qq;
-      sm.rowh[rho] = kk / g;
+      sm.rowh[rho] = kk * __builtin_amdgcn_rcpf(g);
       kq = kk * qq;
       Kc[(size_t)ns * DK + rho] = kk;
     }
@@ -1006,9 +1006,11 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
     if (j < ns * (DK / 4)) {
       const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
       f32x4 o4;
+      // v_rcp_f32 (1 ulp) rather than an IEEE division: the fold is on the
+      // decode path, whose codes are held to a mismatch rate, not bit-exactness
 #pragma unroll
       for (int e = 0; e < 4; e++)
-        o4[e] = kv[it][e] / (gs[it] * bf16f((sg4[it][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+        o4[e] = kv[it][e] * __builtin_amdgcn_rcpf(gs[it] * bf16f((sg4[it][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
       *(f32x4*)&kap[s * DK + r0] = o4;
     }
   }
