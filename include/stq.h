@@ -304,9 +304,11 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  * stq_window_flush does); the prompt then runs from the base plus its
  * compensator rows, and the final state is written as stq_pool_store writes
  * one (compensator rows taken again, window empty).
- * Supported: per-head units (GDN gate: the chunkwise form on the matrix
- * cores; per-channel gate: the recurrence token by token); per-key-row units
- * return STQ_ERR_UNSUPPORTED. */
+ * Every pool kind: GDN gate by the chunkwise form on the matrix cores,
+ * per-channel gate by the recurrence token by token; per-key-row units run
+ * the state in record-row order (rows sorted by width, k, q and gates read
+ * through the head's record -> row permutation) and write the final state
+ * through R for per-key-row widths, packed into the row records on chip. */
 stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
                        const int32_t* seq_start_dev, const float* q_dev, const float* k_dev,
                        const float* v_dev, const float* a_dev, const float* b_dev, float* o_dev,
@@ -317,10 +319,9 @@ stq_status stq_prefill(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  * each request's tokens exactly as stq_prefill advances a tile's state
  * (same paths, same layouts of seq_start, q, k, v, a, b, o; gate_kind
  * STQ_GATE_HEAD or STQ_GATE_CHANNEL), and every token's readout is written.
- * With stq_pool_fetch before and stq_pool_store after, it prefills pools that
- * stq_prefill does not take (per-key-row units): the store then refits every
- * listed tile, identity prompts included.  A request with no tokens leaves
- * its state as it is.  STQ_ERR_ARG on bad sizes or null pointers. */
+ * It is also a direct check of the evaluation: the state after the prompt,
+ * before any requantization.  A request with no tokens leaves its state as
+ * it is.  STQ_ERR_ARG on bad sizes or null pointers. */
 stq_status stq_prefill_states(int32_t n, int32_t n_heads, int32_t d_k, int32_t d_v, int32_t gate_kind,
                               float* S_dev, const int32_t* seq_start_dev, const float* q_dev,
                               const float* k_dev, const float* v_dev, const float* a_dev,

@@ -2372,7 +2372,9 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 
 // The chunks of one request, tokens tb0 .. tb1-1 (tb0 < tb1), on Y; returns
 // nonzero in some thread if some token is not the identity.
-template <int DK, int DV>
+// PERM: the state's rows are record rows of a per-key-row tile (sorted by
+// width); K and Q are read through the record -> row permutation of the head.
+template <int DK, int DV, bool PERM = false>
 __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps, float* Y, int tb0, int tb1,
                                               int h) {
   using G = GeoM<DK, DV>;
@@ -2393,9 +2395,20 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
       const int f = tid + u * G::NT, t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
       kn[u] = qn[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (t < n) {
-        const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
-        kn[u] = *(const f32x4*)(A.k + r);
-        qn[u] = *(const f32x4*)(A.q + r);
+        if constexpr (PERM) {                           // original rows of record rows d4 .. d4+3
+          const size_t r = ((size_t)(t0 + t) * A.H + h) * DK;
+          const uint32_t pr = *(const uint32_t*)(A.row_perm + (size_t)h * DK + d4);
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const uint32_t row = (pr >> (8 * i)) & 0xFFu;
+            kn[u][i] = A.k[r + row];
+            qn[u][i] = A.q[r + row];
+          }
+        } else {
+          const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
+          kn[u] = *(const f32x4*)(A.k + r);
+          qn[u] = *(const f32x4*)(A.q + r);
+        }
       }
     }
     an = 1.f;
@@ -2632,7 +2645,7 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
 // the column sums close over the four lane groups.  (A chunkwise form would need
 // the per-channel decay inside every K K^T entry.)  Returns nonzero in some
 // thread if some token is not the identity.
-template <int DK, int DV>
+template <int DK, int DV, bool PERM = false>
 __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps, float* Y, int tb0, int tb1,
                                               int h) {
   using G = GeoM<DK, DV>;
@@ -2643,10 +2656,25 @@ __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps
     const int Lc = min(PL, tb1 - t0);
     for (int f = tid; f < Lc * DK / 4; f += G::NT) {
       const int t = f / (DK / 4), d4 = 4 * (f % (DK / 4));
-      const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
-      const f32x4 av = *(const f32x4*)(A.a + r);
-      *(f32x4*)&ps.kc[t][d4] = *(const f32x4*)(A.k + r);
-      *(f32x4*)&ps.qc[t][d4] = *(const f32x4*)(A.q + r);
+      f32x4 av, kv, qv;
+      if constexpr (PERM) {                           // record rows d4 .. d4+3 through the permutation
+        const size_t r = ((size_t)(t0 + t) * A.H + h) * DK;
+        const uint32_t pr = *(const uint32_t*)(A.row_perm + (size_t)h * DK + d4);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const uint32_t row = (pr >> (8 * i)) & 0xFFu;
+          av[i] = A.a[r + row];
+          kv[i] = A.k[r + row];
+          qv[i] = A.q[r + row];
+        }
+      } else {
+        const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
+        av = *(const f32x4*)(A.a + r);
+        kv = *(const f32x4*)(A.k + r);
+        qv = *(const f32x4*)(A.q + r);
+      }
+      *(f32x4*)&ps.kc[t][d4] = kv;
+      *(f32x4*)&ps.qc[t][d4] = qv;
       *(f32x4*)&ps.ac[t][d4] = av;
       moved |= (av[0] != 1.f) | (av[1] != 1.f) | (av[2] != 1.f) | (av[3] != 1.f);
     }
@@ -2715,6 +2743,224 @@ __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps
     lds_barrier();
   }
   return moved;
+}
+
+// ------------------------------------------------------------------------
+// Prefill into per-key-row tiles.  The state runs in the prefill's lane layout
+// with its rows in record order (sorted by width); the chunk's K, Q and
+// per-channel gates are read through the record -> row permutation.  The
+// tile is decoded from its records (staged in LDS) and written back by R for
+// per-key-row widths, packed into records in LDS and stored with 16-byte
+// accesses: no binary32 copy of the state leaves the workgroup.
+// ------------------------------------------------------------------------
+template <int DK, int DV>
+struct RowsRefitSmem {
+  SmemM<DK, DV> m;
+  uint32_t stage[DK * DV / 2 + 4] __attribute__((aligned(16)));   // code region (all-binary16 bound) + the
+                                                                   // word the last field's read takes
+};
+template <int DK, int DV>
+union PrefillRowsSmem {
+  PrefillSmem<DK, DV> pre;
+  RowsRefitSmem<DK, DV> r;
+};
+
+// Y := D(tile) of a per-key-row tile, rows in record order: stage the code
+// region in LDS, then each element's field (code j of a record is bits
+// n j .. n j + n - 1 of it, little-endian) to its value: fl(fl(sigma c) Q),
+// binary16 on pivot rows.
+template <int DK, int DV>
+__device__ __forceinline__ void decode_rows_state(const KArgs& A, uint8_t* stage, const uint8_t* tile, int h, float* Y) {
+  using G = GeoM<DK, DV>;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  const int* cntp = A.row_cnt + 4 * h;
+  const int c4 = cntp[0], c6 = c4 + cntp[1], c8 = c6 + cntp[2];
+  const int CB = (DV / 8) * (4 * cntp[0] + 6 * cntp[1] + 8 * cntp[2] + 16 * cntp[3]);
+  const uint16_t* scl = (const uint16_t*)(tile + CB);
+  const uint8_t* perm = A.row_perm + (size_t)h * DK;
+  for (int off = 16 * tid; off < CB; off += 16 * G::NT) *(u32x4*)(stage + off) = *(const u32x4*)(tile + off);
+  float cc[G::NCC];
+#pragma unroll
+  for (int c = 0; c < G::NCC; c++) cc[c] = bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 64; e++) {
+    const int b = e >> 3, t = e & 7, c = b / G::NRC;
+    const int p = erow(b % G::NRC, t, Gq), j = w * G::CPW + 16 * c + n16;
+    int n, off;
+    rec_at<DV>(p, c4, c6, c8, n, off);
+    const uint32_t bit = (uint32_t)off * 8u + (uint32_t)(n * j);
+    const uint32_t* wd = (const uint32_t*)(stage + 4 * (bit >> 5));
+    const uint32_t f = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(wd[1], wd[0], bit & 31u), 0, n);
+    if (n == 16) {
+      Y[e] = (float)__builtin_bit_cast(f16, (uint16_t)f);
+    } else {
+      const float sg = bf16f(scl[perm[p]]);
+      Y[e] = (sg * cc[c]) * (float)((int)f - (1 << (n - 1)));
+    }
+  }
+  __syncthreads();                                 // the staged codes are overwritten next
+}
+
+// R of the binary32 state Y (record row order, g = 1) into a per-key-row
+// tile, with the ingest's exact arithmetic: row factor bf16(sqrt(fl(m w)))
+// (correctly rounded), exponent normalisation, X = Y fl(1/sigma), column scale
+// bf16 rounded up of max over non-pivot rows of fl(|X| fl(1/qmax(n_i))),
+// codes = nearest integer of the exact product X fl(1/c); pivot rows
+// binary16 of Y.  The fields of a lane quad (columns j .. j+3 of one row) are
+// gathered by DPP and written as one group into the staged records, then the
+// code region is stored with 16-byte accesses.
+template <int DK, int DV>
+__device__ __forceinline__ void refit_store_rows(const KArgs& A, RowsRefitSmem<DK, DV>& rs, float* Y, uint8_t* tile,
+                                                 int h) {
+  using G = GeoM<DK, DV>;
+  SmemM<DK, DV>& sm = rs.m;
+  uint8_t* stage = (uint8_t*)rs.stage;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  const int* cntp = A.row_cnt + 4 * h;
+  const int c4 = cntp[0], c6 = c4 + cntp[1], c8 = c6 + cntp[2];
+  const int CB = (DV / 8) * (4 * cntp[0] + 6 * cntp[1] + 8 * cntp[2] + 16 * cntp[3]);
+  uint16_t* scl = (uint16_t*)(tile + CB);
+  const uint8_t* perm = A.row_perm + (size_t)h * DK;
+  // ---- row partial absmax over the lane's columns, merged with lane n ^ 8 ----
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        float m = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < G::NCC; cc++)
+          m = __builtin_fmaxf(m, __builtin_fabsf(Y[8 * (cc * G::NRC + rc) + 4 * hf + i]));
+        const uint32_t mb = __float_as_uint(m);
+        const uint32_t mp = __builtin_elementwise_max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x128, 0xF, 0xF, false));
+        sm.part[(erow(rc, 4 * hf, Gq) + i) * G::PSTR + w * 8 + (n16 & 7)] = __uint_as_float(mp);
+      }
+  lds_barrier();
+  // ---- row stage: TPR threads per record row ----
+  const int rho = tid / G::TPR, rsub = tid % G::TPR;
+  uint32_t mxb = 0u;
+  constexpr int PPT = G::NP / G::TPR;
+#pragma unroll
+  for (int p = 0; p < PPT; p++) mxb = __builtin_elementwise_max(mxb, __float_as_uint(sm.part[rho * G::PSTR + rsub * PPT + p]));
+  if (G::TPR == 2) mxb = __builtin_elementwise_max(mxb, (uint32_t)dppi<0xB1>((int)mxb));
+  int n, roff;
+  rec_at<DV>(rho, c4, c6, c8, n, roff);
+  const int irow = perm[rho];
+  const float pw = __uint_as_float(mxb) * A.weights[(size_t)h * DK + irow];
+  uint32_t s = 0x3F80u;
+  int epk = 0;
+  if (n != 16 && pw > 0.f) {
+    s = bf16_rne(__builtin_sqrtf(pw));
+    epk = (((int)((s >> 7) & 0xFFu) - 127) << 8) + 1;
+  }
+  if (rsub != 0) epk = 0;
+  if (rsub == 0) {
+    sm.rowh[rho] = rcp_bf16(bf16f(s));
+    sm.kappa[0][rho] = n == 4 ? 1.0f / 7.0f : n == 6 ? 1.0f / 31.0f : n == 8 ? 1.0f / 127.0f : 0.f;
+  }
+  epk = wave_sum_i(epk);
+  if (l == 0) sm.epk[w] = epk;
+  lds_barrier();
+  int et = 0;
+#pragma unroll
+  for (int ww = 0; ww < G::NW; ww++) et += sm.epk[ww];
+  et = __builtin_amdgcn_readfirstlane(et);
+  const int E = (et & 0xFF) ? mean_exp(et >> 8, et & 0xFF) : 0;
+  if (rsub == 0) scl[irow] = (uint16_t)bf16_adj(s, -E);
+  // ---- column refit over the non-pivot rows ----
+  float cmx[G::NCC];
+#pragma unroll
+  for (int cc = 0; cc < G::NCC; cc++) cmx[cc] = 0.f;
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      const f32x4 hr = *(const f32x4*)&sm.rowh[erow(rc, 4 * hf, Gq)];
+      const f32x4 rq = *(const f32x4*)&sm.kappa[0][erow(rc, 4 * hf, Gq)];
+#pragma unroll
+      for (int cc = 0; cc < G::NCC; cc++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int e = 8 * (cc * G::NRC + rc) + 4 * hf + i;
+          Y[e] = Y[e] * hr[i];                       // pivot rows: hr = 1
+          cmx[cc] = __builtin_fmaxf(cmx[cc], __builtin_fabsf(Y[e]) * rq[i]);
+        }
+    }
+  float rcv[G::NCC];
+#pragma unroll
+  for (int cc = 0; cc < G::NCC; cc++) {
+    const float M = g4_max_pos(cmx[cc]);
+    uint32_t tt = 0x3F80u;
+    if (c8 > 0 && M > 0.f) {
+      tt = bf16_ru_pos(M);
+      if (tt < 0x0080u) tt = 0x0080u;
+    }
+    rcv[cc] = rcp_bf16(bf16f(tt));
+    if (Gq == 0) scl[DK + w * G::CPW + 16 * cc + n16] = (uint16_t)bf16_adj(tt, E);
+  }
+  // ---- fields and groups ----
+#pragma unroll
+  for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int p = erow(rc, 4 * hf, Gq) + i;
+        int nw, off;
+        rec_at<DV>(p, c4, c6, c8, nw, off);
+#pragma unroll
+        for (int cc = 0; cc < G::NCC; cc++) {
+          const int e = 8 * (cc * G::NRC + rc) + 4 * hf + i;
+          const int j = w * G::CPW + 16 * cc + n16;
+          uint32_t f;
+          if (nw == 16) {
+            f = (uint32_t)__builtin_bit_cast(uint16_t, (f16)__builtin_fminf(__builtin_fmaxf(Y[e], -65504.f), 65504.f));
+          } else {
+            const float mg = 8388608.0f + (float)(1 << (nw - 1));   // 2^23 + 2^(n-1): the field in the low bits
+            f = __float_as_uint(__builtin_fmaf(Y[e], rcv[cc], mg)) & ((1u << nw) - 1u);
+          }
+          // columns j .. j+3 sit in lanes n16 .. n16+3 of this lane's quad
+          const uint32_t f1 = (uint32_t)dppi<0x39>((int)f);   // quad lane + 1
+          const uint32_t f2 = (uint32_t)dppi<0x4E>((int)f);   // + 2
+          const uint32_t f3 = (uint32_t)dppi<0x93>((int)f);   // + 3
+          if ((n16 & 3) == 0) {
+            uint8_t* gp = stage + off + (j >> 2) * (nw >> 1);
+            if (nw == 4) {
+              *(uint16_t*)gp = (uint16_t)(f | (f1 << 4) | (f2 << 8) | (f3 << 12));
+            } else if (nw == 6) {
+              const uint32_t g = f | (f1 << 6) | (f2 << 12) | (f3 << 18);
+              gp[0] = (uint8_t)g; gp[1] = (uint8_t)(g >> 8); gp[2] = (uint8_t)(g >> 16);
+            } else if (nw == 8) {
+              *(uint32_t*)gp = f | (f1 << 8) | (f2 << 16) | (f3 << 24);
+            } else {
+              *(u32x2*)gp = u32x2{f | (f1 << 16), f2 | (f3 << 16)};
+            }
+          }
+        }
+      }
+  __syncthreads();
+  for (int off = 16 * tid; off < CB; off += 16 * G::NT) *(u32x4*)(tile + off) = *(const u32x4*)(stage + off);
+}
+
+template <int DK, int DV, bool KDA>
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_rows(KArgs A) {
+  __shared__ PrefillRowsSmem<DK, DV> sh;
+  const int ci = (int)blockIdx.x / A.H, h = (int)blockIdx.x - ci * A.H;
+  if (ci >= A.n) return;
+  const int slot = ld_const(A.slots + ci);
+  if ((unsigned)slot >= (unsigned)A.n_slots) return;
+  uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + ld_const(A.head_off + h);
+  const int tb0 = A.seq_start[ci], tb1 = A.seq_start[ci + 1];
+  if (tb1 <= tb0) return;                            // no tokens: the tile is left as it is
+  float Y[64];
+  decode_rows_state<DK, DV>(A, (uint8_t*)sh.r.stage, tile, h, Y);
+  const int moved = KDA ? prefill_tokens<DK, DV, true>(A, sh.pre.k, Y, tb0, tb1, h)
+                        : prefill_chunks<DK, DV, true>(A, sh.pre.p, Y, tb0, tb1, h);
+  // identity tokens only: the tile is left as it is (the decode step's rule)
+  if (!__syncthreads_or(moved)) return;
+  refit_store_rows<DK, DV>(A, sh.r, Y, tile, h);
 }
 
 template <int DK, int DV, bool KDA>
@@ -3004,11 +3250,12 @@ struct LFetch {
 };
 
 template <int DK, int DV>
-void launch_prefill(const KArgs& A, hipStream_t st) {
-  if (A.gate)
-    hipLaunchKernelGGL((k_prefill<DK, DV, true>), dim3((unsigned)A.n * (unsigned)A.H), dim3(GeoM<DK, DV>::NT), 0, st, A);
-  else
-    hipLaunchKernelGGL((k_prefill<DK, DV, false>), dim3((unsigned)A.n * (unsigned)A.H), dim3(GeoM<DK, DV>::NT), 0, st, A);
+void launch_prefill(const KArgs& A, bool rows, hipStream_t st) {
+  const dim3 g((unsigned)A.n * (unsigned)A.H), b(GeoM<DK, DV>::NT);
+  if (rows && A.gate) hipLaunchKernelGGL((k_prefill_rows<DK, DV, true>), g, b, 0, st, A);
+  else if (rows) hipLaunchKernelGGL((k_prefill_rows<DK, DV, false>), g, b, 0, st, A);
+  else if (A.gate) hipLaunchKernelGGL((k_prefill<DK, DV, true>), g, b, 0, st, A);
+  else hipLaunchKernelGGL((k_prefill<DK, DV, false>), g, b, 0, st, A);
 }
 
 template <int DK, int DV>
@@ -3168,7 +3415,6 @@ stq_status stq_prefill(stq_pool* p, const int32_t* slots, int32_t n, const int32
                        float* o, hipStream_t st) {
   stq_status s = check_call(p, slots, n);
   if (s != STQ_OK) return s;
-  if (p->unit != STQ_UNIT_HEAD) return STQ_ERR_UNSUPPORTED;
   if (n == 0) return STQ_OK;
   if (!seq_start || !q || !k || !v || !a || !b || !o) return STQ_ERR_ARG;
   KArgs A = base_args(p, slots, n);
@@ -3178,10 +3424,11 @@ stq_status stq_prefill(stq_pool* p, const int32_t* slots, int32_t n, const int32
   }
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
   A.seq_start = seq_start;
-  if (p->dk == 128 && p->dv == 128) launch_prefill<128, 128>(A, st);
-  else if (p->dk == 64 && p->dv == 64) launch_prefill<64, 64>(A, st);
-  else if (p->dk == 64 && p->dv == 128) launch_prefill<64, 128>(A, st);
-  else launch_prefill<128, 64>(A, st);
+  const bool rows = p->unit == STQ_UNIT_ROW;
+  if (p->dk == 128 && p->dv == 128) launch_prefill<128, 128>(A, rows, st);
+  else if (p->dk == 64 && p->dv == 64) launch_prefill<64, 64>(A, rows, st);
+  else if (p->dk == 64 && p->dv == 128) launch_prefill<64, 128>(A, rows, st);
+  else launch_prefill<128, 64>(A, rows, st);
   return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
 }
 stq_status stq_prefill_states(int32_t n, int32_t n_heads, int32_t d_k, int32_t d_v, int32_t gate_kind, float* S,

@@ -39,15 +39,15 @@ def torch_cuda():
     return torch
 
 
-def _run(P, wl, slots, lens, edit=None):
+def _run(P, wl, slots, lens, edit=None, prompts=None):
     import torch
     dev = lambda x: torch.as_tensor(x, device="cuda")
-    ss, q, k, v, a, b = wl.prompts(lens)
+    ss, q, k, v, a, b = wl.prompts(lens) if prompts is None else prompts
     if edit:
         edit(ss, q, k, v, a, b)
     pre = P.image()
-    ref = P.orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, P.ref.gate, 0, P.ref.W,
-                           image=pre, n_comp=P.ref.C)
+    ref = P.orc.OraclePool(P.n_slots, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1), wl.row_weight,
+                           P.ref.gate, P.ref.unit, P.ref.W, image=pre, n_comp=P.ref.C)
     T = int(ss[-1])
     o = torch.full((T, wl.H, wl.dv), float("nan"), dtype=torch.float32, device="cuda")
     P.stq.stq_prefill(P.pool, P.slots_t(slots), dev(ss), dev(q), dev(k), dev(v), dev(a), dev(b), o)
@@ -58,7 +58,7 @@ def _run(P, wl, slots, lens, edit=None):
 
 def _state_ok(orc, ref, img, slots, S_fin, moved):
     """Worst ratio of |D(tile) - S_T| to its bound over the tiles that moved."""
-    D = orc.OraclePool(ref.n_slots, ref.H, ref.dk, ref.dv, ref.bits, ref.wt, ref.gate, 0, ref.W, image=img,
+    D = orc.OraclePool(ref.n_slots, ref.H, ref.dk, ref.dv, ref.bits, ref.wt, ref.gate, ref.unit, ref.W, image=img,
                        n_comp=ref.C).fetch(slots)
     worst = 0.0
     for c, s in enumerate(slots):
@@ -68,12 +68,12 @@ def _state_ok(orc, ref, img, slots, S_fin, moved):
             S = S_fin[c, h]
             Q, sg, cs, nb = ref.decode_tile(int(s), h, img)
             eps = 1e-4 * np.abs(S).max()
-            if int(ref.bits[h]) == 16:
-                half = np.abs(S) * 2.0 ** -11 + 2.0 ** -25
-            else:
-                sig = (sg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-                col = (cs.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-                half = 0.5 * sig[:, None] * col[None, :] * (1 + 1e-6)
+            # per row: half a code step sigma_i c_j, binary16 pivot rows half an ulp
+            sig = (sg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            col = (cs.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            half = 0.5 * sig[:, None] * col[None, :] * (1 + 1e-6)
+            piv = np.asarray(nb) == 16
+            half[piv] = (np.abs(S) * 2.0 ** -11 + 2.0 ** -25)[piv]
             err = np.abs(D[c, h].astype(np.float64) - S)
             worst = max(worst, float((err / (half + eps)).max()))
     return worst
@@ -243,10 +243,12 @@ def test_prefill_unsupported_and_empty(torch_cuda, orc):
     for key in ("C4",):                            # per-key-row units: one request, no tokens
         wl = Workload(key, B=1, H=2)
         P = Pair(orc, wl, n_slots=1)
-        ss = torch.zeros(2, dtype=torch.int32, device="cuda")
-        with pytest.raises(stq.StqError) as e:
-            stq.stq_prefill(P.pool, P.slots_t([0]), ss, f(0), f(0), f(0), f(0), f(0), f(0))
-        assert e.value.status == -5
+        P.store(np.array([0]), wl.state(np.array([0])))
+        pre = P.image()
+        ss = torch.zeros(2, dtype=torch.int32, device="cuda")      # an empty request (buffers for one token)
+        H, dk, dv = wl.H, wl.dk, wl.dv
+        stq.stq_prefill(P.pool, P.slots_t([0]), ss, f(H * dk), f(H * dk), f(H * dv), f(H * dk), f(H), f(H * dv))
+        assert np.array_equal(P.image(), pre)
     wl = Workload("C2", B=1, H=2)
     P = Pair(orc, wl, n_slots=1)
     pre = P.image()
@@ -323,3 +325,74 @@ def test_prefill_states_per_key_row_pool(torch_cuda, orc):
     res = compare_codes(orc, ref, P.image(), ref.img, slots)
     say("  " + agg_text(res))
     _assert_prefill_codes(res)
+
+
+# ---- per-key-row units (unit = key row): stq_prefill straight into the row records ----
+
+def _rows_workload(dk, dv, gate, B, H, seed):
+    """Per-key-row widths that reach every run boundary (the C4 proportions, a
+    lone quantized row among pivots, one width only, all pivots, random)."""
+    from types import SimpleNamespace
+    from test_gpu_parity import _row_width_patterns
+    rng = np.random.default_rng(seed)
+    pats = _row_width_patterns(dk, rng)
+    bits = pats[rng.integers(0, len(pats), H)]
+    bits[0] = pats[5]                              # the C4 mix
+    wl = Workload("C4", B=B, H=H)
+    wl.dk, wl.dv = dk, dv
+    wl.bits = bits
+    wl.row_weight = np.clip(np.exp(rng.normal(0, 1.15, (H, dk))), 0.1, 10).astype(np.float32)
+    wl.cfg = SimpleNamespace(**{**wl.cfg.__dict__, "gate": gate, "unit": 1})
+    prof = np.exp(rng.normal(0, 1.5, (1, H, dk, 1))) * np.exp(rng.normal(0, 1.5, (1, H, 1, dv)))
+    S0 = (0.1 * rng.standard_normal((B, H, dk, dv)) * prof).astype(np.float32)
+    return wl, S0
+
+
+def _rows_prompts(wl, lens, gate, seed):
+    rng = np.random.default_rng(seed)
+    T, H, dk, dv = sum(lens), wl.H, wl.dk, wl.dv
+    ss = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = rng.standard_normal((T, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((T, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv))
+    b = rng.uniform(0.05, 0.95, (T, H))
+    a = (2.0 ** (-1.0 / (10.0 ** rng.uniform(0, 4, (T, H, dk))))) if gate else rng.uniform(0.9, 0.9999, (T, H))
+    f = lambda x: x.astype(np.float32)
+    return ss, f(q), f(k), f(v), f(a), f(b)
+
+
+@pytest.mark.parametrize("dk,dv,gate", [(128, 128, 1), (128, 128, 0), (64, 128, 1), (128, 64, 1), (64, 64, 0)])
+def test_prefill_rows_parity(torch_cuda, orc, dk, dv, gate):
+    """Per-key-row pools through stq_prefill (no binary32 staging): ragged
+    prompts, tails inside a chunk, an empty request; per-channel (KDA) and
+    per-head gates."""
+    say("case prefill rows", dk, dv, "KDA" if gate else "GDN")
+    B, H = 4, 6
+    wl, S0 = _rows_workload(dk, dv, gate, B, H, 900 + dk + dv + gate)
+    P = Pair(orc, wl, n_slots=B + 1)
+    slots = np.array([4, 0, 2, 1], np.int32)
+    P.store(slots, S0)
+    lens = [45, 0, 33, 70]
+    out = _run(P, wl, slots, lens, prompts=_rows_prompts(wl, lens, gate, 17 + dk + gate))
+    _check(P, wl, slots, lens, *out, moved=[L > 0 for L in lens])
+
+
+@pytest.mark.parametrize("gate", [1, 0])
+def test_prefill_rows_exact_scaling(torch_cuda, orc, gate):
+    """Gates of 1/2 and b = 0: the final state is D(tile) times an exact power
+    of two in both binary32 and binary64, so the per-key-row refit of the
+    kernel must write the oracle's bytes exactly (row and column scales,
+    codes in every width, binary16 pivot rows)."""
+    say("case prefill rows exact", "KDA" if gate else "GDN")
+    B, H, dk, dv = 2, 6, 128, 128
+    wl, S0 = _rows_workload(dk, dv, gate, B, H, 950 + gate)
+    P = Pair(orc, wl, n_slots=B)
+    slots = np.array([1, 0], np.int32)
+    P.store(slots, S0)
+    lens = [3, 40]
+    ss, q, k, v, a, b = _rows_prompts(wl, lens, gate, 5)
+    a[:] = 0.5
+    b[:] = 0.0
+    pre, img, ref, o, o_ref, S_fin, ss2 = _run(P, wl, slots, lens, prompts=(ss, q, k, v, a, b))
+    assert not np.array_equal(img, pre)            # the tiles were rewritten
+    np.testing.assert_array_equal(img, ref.img)
