@@ -136,7 +136,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 512; P3: 8)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 32; P3: 2)")
-    ap.add_argument("--workload", choices=sorted(BENCH) + ["P3", "P4"], default="C3")
+    ap.add_argument("--workload", choices=sorted(BENCH) + ["P3", "P4", "P5"], default="C3")
     ap.add_argument("--prompt-len", type=int, default=1024, help="P3: tokens per prompt")
     ap.add_argument("--prompts", type=int, default=64, help="P3: prompts per prefill call")
     ap.add_argument("--layers", type=int, default=None)
@@ -174,7 +174,7 @@ def main():
     from workloads import Workload
 
     key = args.workload
-    if key in ("P3", "P4"):
+    if key in ("P3", "P4", "P5"):
         return prefill_bench(args)
     spec = BENCH[key]
     dev = torch.device("cuda:0")
@@ -449,7 +449,8 @@ def prefill_bench(args):
     """P3: prefill ingest of a batch of prompts into the C3 pool (GDN head mix,
     H = 32, d = 128): one step = one stq_prefill call over all prompts.  P4: the
     same with per-channel (KDA) gates of C4's half-life law on per-head widths
-    of the same mix (the token-by-token path)."""
+    of the same mix (the token-by-token path).  P5: P4's prompts into the C4
+    pool itself (per-key-row widths: records decoded and refitted on chip)."""
     import dataclasses
 
     import torch
@@ -458,14 +459,15 @@ def prefill_bench(args):
     from workloads import Workload
     dev = torch.device("cuda:0")
     B, Lp = args.prompts, args.prompt_len
-    kda = args.workload == "P4"
+    kda = args.workload in ("P4", "P5")
+    rows = args.workload == "P5"
     wl = Workload("C4" if kda else "C3", B=B)
-    if kda:
+    if kda and not rows:
         wl.cfg = dataclasses.replace(wl.cfg, unit=0)
         wl.bits = Workload("C3").bits
     c, H, dk, dv = wl.cfg, wl.H, wl.dk, wl.dv
     T = B * Lp
-    desc = stq.make_desc(B, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, 0, 0)
+    desc = stq.make_desc(B, H, dk, dv, np.asarray(wl.bits).reshape(-1), wl.row_weight, c.gate, c.unit, 0, 0)
     buf = torch.empty(stq.stq_pool_bytes(desc), dtype=torch.uint8, device=dev)
     pool = stq.stq_pool_create(desc, buf)
     slots = torch.arange(B, dtype=torch.int32, device=dev)
@@ -520,7 +522,7 @@ def prefill_bench(args):
         import oracle
         oracle.build()
         ns, Ls = 2, 64
-        P = oracle.OraclePool(ns, H, dk, dv, wl.bits, wl.row_weight, c.gate, c.unit, 0)
+        P = oracle.OraclePool(ns, H, dk, dv, np.asarray(wl.bits).reshape(-1), wl.row_weight, c.gate, c.unit, 0)
         P.store(np.arange(ns), wl.state(np.arange(ns)))
         pr = wl.prompts([Ls] * ns)
         calls = 0
@@ -533,22 +535,24 @@ def prefill_bench(args):
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": "%d calls x %d prompts of %d tokens, all %d heads, %.1f s" % (calls, ns, Ls, H, el)}
     gname = "KDA per-channel gates" if kda else "GDN"
+    mix = ("per-key-row widths {4b:30%, 6b:50%, 8b:19%, fp16:1%}" if rows
+           else "heads {4b:9, 6b:16, 8b:6, fp16:1}")
     line = {
         "metric": "request-head prompt tokens/s (prefill ingest, B=%d prompts x %d tokens, H=32, d=128, "
-                  "6-bit nominal %s pool)" % (B, Lp, gname),
+                  "6-bit nominal %s pool%s)" % (B, Lp, gname, ", per-key-row widths" if rows else ""),
         "value": T * H * K / (total_ms * 1e-3),
         "unit": "request-head prompt tokens/s",
         "n_gpus": 1, "steps": K, "warmup": Wu, "ms_per_step": total_ms / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32 state and products, 4/6/8-bit + f16 final state",
         "data": "synthetic (seeded; states and prompts drawn on the GPU with the workload recipe)",
-        "config": {"workload": "prefill of %d prompts x %d tokens into the %s pool H=32 d_k=d_v=128, heads "
-                               "{4b:9, 6b:16, 8b:6, fp16:1}" % (B, Lp, gname),
+        "config": {"workload": "prefill of %d prompts x %d tokens into the %s pool H=32 d_k=d_v=128, %s"
+                               % (B, Lp, gname, mix),
                    "global_batch": B, "prompt_len": Lp, "heads": H, "d_k": dk, "d_v": dv},
         "roofline": {"bound": "alu" if kda else "mfma", "achieved": tflops,
                      "peak": VALU_F32_PEAK if kda else MFMA_F32_PEAK, "unit": "TFLOP/s",
                      "frac": tflops / (VALU_F32_PEAK if kda else MFMA_F32_PEAK), "traffic": None,
-                     "kernel": "k_prefill<128, 128, %s>" % ("true" if kda else "false"),
+                     "kernel": "%s<128, 128, %s>" % ("k_prefill_rows" if rows else "k_prefill", "true" if kda else "false"),
                      "flops_per_launch": flops, "flops_issued_per_launch": issued,
                      "issued_tflops": issued / (avg_ms * 1e-3) / 1e12, "avg_launch_ms": avg_ms,
                      "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
