@@ -113,7 +113,7 @@ BENCH = {
            "workload": "GDN serving pool B=512 H=32 d_k=d_v=128, heads {4b:9, 6b:16, 8b:6, fp16:1}",
            "dtype": "f32 update and refit; the two matvecs on matrix cores with each f32 operand split into "
                     "f16 hi + lo (f32 accumulation); 4/6/8-bit + f16 state"},
-    "C4": {"layers": 8, "kernel": "k_rows_wide<128>", "prof": "k_rows_wide_step",
+    "C4": {"layers": 8, "kernel": "k_rows_mf<128>", "prof": "k_rows_mf_step",
            "metric": "request-head decode steps/s (B=256, H=32, d=128, KDA per-channel gate, "
                      "per-key-row widths)",
            "workload": "KDA pool B=256 H=32 d_k=d_v=128, per-channel gate, key rows "

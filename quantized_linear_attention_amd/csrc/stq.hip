@@ -6,7 +6,8 @@
 // v_mfma_f32_16x16x32_f16 straight from the unpacked fp16 codes and the
 // rank-one update on v_mfma_f32_16x16x4_f32, so the vector ALUs only unpack,
 // refit and pack.  Per-key-row tiles (mixed widths inside a tile) stage their
-// row records through LDS and run on the vector ALUs.  Codes are loaded and
+// row records through LDS; their decode step runs the same contractions on
+// the matrix cores with block-diagonal operands.  Codes are loaded and
 // stored with one 16-byte access per lane per chunk (1 KiB contiguous per
 // wave).
 #include <hip/hip_runtime.h>
@@ -1873,46 +1874,68 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
 }
 
 // ------------------------------------------------------------------------
-// Per-key-row widths with d_v = 128: the 64 lanes of a wave span one record
-// row (columns 2l, 2l+1), so each step of the loops below is one row whose
-// width and record offset are wave-uniform values.  A wave owns 32
-// consecutive record rows.  The binary16 pivot rows, the last records,
-// leave the unrolled loops: their readout terms and their update run row by
-// row at the end of the first and the last phase.
+// Per-key-row decode step on the matrix cores (d_v = 128).
+//
+// Wave w owns record rows 32w .. 32w+31 and lane l the value columns 2l
+// (chain 0) and 2l+1 (chain 1).  The lane keeps
+// its codes of one column as binary16 pairs of consecutive rows,
+// P2[c][m] = (Q[2m][c], Q[2m+1][c]), so four pairs are the B fragment
+// (8 rows x 1 column) of v_mfma_f32_16x16x32_f16.  The lanes 16 kg + n of
+// the four lane groups hold different columns, so the A fragment is block
+// diagonal: the row factors (g k hi, lo, g q hi, lo) fill row quad kg of A
+// for lane group kg only, and every lane receives the four partial sums of
+// its own column.  The rank-one update runs on v_mfma_f32_16x16x4_f32 the
+// same way (kappa in row quad kg of A, the lane's own delta in B); its output
+// fragment is four consecutive rows of the lane's column.  Widths are
+// dispatched per 8-row group with one scalar branch: records are sorted by
+// width, so all but at most three groups of a tile share one width.
 // ------------------------------------------------------------------------
 template <int DK>
-struct GeoW {
+struct GeoRM {
   static constexpr int DV = 128;
   static constexpr int NW = DK / 32;        // waves, 32 record rows each
   static constexpr int NT = 64 * NW;
-  static constexpr int NR = 32;             // steps (rows) per wave
-  static constexpr int TPR = NT / DK;       // threads per row in the row stage
   static constexpr int PSTR = 36;           // row partials: 32 lane pairs per row, padded
   static constexpr int NCH = DK * DV * 2 / (16 * NT);   // 16-byte chunks per thread, binary16 bound
-  static_assert(TPR == 2, "row stage");
 };
 
 template <int DK>
-struct WRSmem {
-  float red[GeoW<DK>::NW][2][128] __attribute__((aligned(16)));   // per wave: column partials
-  f32x2 ab[DK] __attribute__((aligned(16)));      // by record row: (g k, g q); 0 on pivot rows
+struct RMSmem {
+  float red[GeoRM<DK>::NW][2][128] __attribute__((aligned(16)));   // per wave: column partials of u, w
+  float cmx[GeoRM<DK>::NW][128] __attribute__((aligned(16)));      // per wave: column maxima (no barrier
+                                                                   // separates them from the reads of red)
+  f16 afr[DK / 8][4][8] __attribute__((aligned(16)));   // matvec A: [row group][kh, kl, qh, ql][row]
+  f16 azero[4][4][8] __attribute__((aligned(16)));      // the zero A fragments of the other lane groups
+  float kapT[GeoRM<DK>::NW][4][8] __attribute__((aligned(16)));   // kappa as [wave][row % 4][row / 4]
+  float kzero[8] __attribute__((aligned(16)));
   f32x2 abp[DK] __attribute__((aligned(16)));     // (g k, g q) of the pivot rows
   float kappa[DK] __attribute__((aligned(16)));   // k / g (k on pivot rows)
   float gg[DK] __attribute__((aligned(16)));      // g = gate * row scale (1 on zero-gate rows)
   float rowh[DK] __attribute__((aligned(16)));    // new X factor
-  float rq[DK] __attribute__((aligned(16)));      // 1 / QMAX of the row's width
+  float rq[DK] __attribute__((aligned(16)));      // 1 / QMAX of the row's width (0 on pivots)
   float zf[DK] __attribute__((aligned(16)));      // 1 on quantized rows whose gate is zero
-  float kqp[GeoW<DK>::NW];
-  int notone[GeoW<DK>::NW];
-  int esum[GeoW<DK>::NW];
-  int ecnt[GeoW<DK>::NW];
+  float nat[5][DK] __attribute__((aligned(16)));  // k, q, a, sigma, row weight in the original row order
+  float kqp[GeoRM<DK>::NW];
+  int notone[GeoRM<DK>::NW];
+  int esum[GeoRM<DK>::NW];
+  int ecnt[GeoRM<DK>::NW];
 };
 
+// width shared by the 8 record rows p0 .. p0+7 (4, 6, 8, or 16 for binary16
+// pivots), 0 when they mix widths
+__device__ __forceinline__ int group_kind(int p0, int c4, int c6, int c8) {
+  if (p0 + 8 <= c4) return 4;
+  if (p0 >= c4 && p0 + 8 <= c6) return 6;
+  if (p0 >= c6 && p0 + 8 <= c8) return 8;
+  if (p0 >= c8) return 16;
+  return 0;
+}
+
 template <int DK>
-__global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_wide(KArgs A) {
-  using G = GeoW<DK>;
+__global__ __launch_bounds__((GeoRM<DK>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_mf(KArgs A) {
+  using G = GeoRM<DK>;
   constexpr int DV = 128;
-  __shared__ WRSmem<DK> rs;
+  __shared__ RMSmem<DK> rs;
   extern __shared__ u32x4 stage_[];               // the tile's codes, later the row partials
   uint8_t* stage = (uint8_t*)stage_;
   float* part = (float*)stage_;
@@ -1925,14 +1948,20 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
   const size_t x = (size_t)ci * A.H + h;
 
-  const int tid = threadIdx.x, l = tid & 63;
+  const int tid = threadIdx.x, l = tid & 63, n16 = l & 15, kg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ws0 = 32 * w;                          // first record row of the wave
+  const bool own = (n16 >> 2) == kg;               // the lane's A rows are its own group's
   const int* cntp = A.row_cnt + 4 * h;
   const int c4 = cntp[0], c6 = c4 + cntp[1], c8 = c6 + cntp[2];
   const int CB = c4 * 64 + cntp[1] * 96 + cntp[2] * 128 + cntp[3] * 256;
   const int o6 = -32 * c4, o8 = -32 * (c4 + c6), o16 = -32 * (c4 + c6) - 128 * c8;   // record offset - width * 16 * p
   uint16_t* scl = (uint16_t*)(tile + CB);
+  // width kinds of the wave's four 8-row groups, one byte each, computed once
+  int kinds = 0;
+#pragma unroll
+  for (int sg = 0; sg < 4; sg++) kinds |= group_kind(ws0 + 8 * sg, c4, c6, c8) << (8 * sg);
+  asm volatile("" : "+s"(kinds));
 
   // ---- every global read first ----
   u32x4 chunk[G::NCH];
@@ -1941,16 +1970,23 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
     const int off = 16 * (tid + i * G::NT);
     if (off < CB) chunk[i] = *(const u32x4*)(tile + off);
   }
-  const int rho = tid >> 1, rsub = tid & 1;        // row stage: record row rho
+  const int rho = tid >> 1, rsub = tid & 1;        // per-row work: record row rho
   const int irow = A.row_perm[(size_t)h * DK + rho];
   const int pn = rho < c4 ? 4 : (rho < c6 ? 6 : (rho < c8 ? 8 : 16));
-  float kk = 0.f, qq = 0.f, ai = 1.f, sgr = 1.f;
-  if (rsub == 0) {
-    kk = A.k[x * DK + irow];
-    qq = A.q[x * DK + irow];
-    ai = A.gate ? A.a[x * DK + irow] : A.a[x];
-    sgr = pn == 16 ? 1.f : bf16f(scl[irow]);
+  // the per-row vectors in their own order (no wait on the permutation):
+  // threads [0, d_k) read k, q and the row weight, threads [d_k, 2 d_k) the
+  // gate and the row scale
+  const int ir = tid & (DK - 1);
+  float n0, n1, n2 = 0.f;
+  if (tid < DK) {
+    n0 = A.k[x * DK + ir];
+    n1 = A.q[x * DK + ir];
+    n2 = A.weights[(size_t)h * DK + ir];
+  } else {
+    n0 = A.gate ? A.a[x * DK + ir] : 1.f;
+    n1 = bf16f(scl[ir]);
   }
+  const float a_h = A.gate ? 1.f : A.a[x];
   const uint32_t cw = *(const uint32_t*)(scl + DK + 2 * l);
   const f32x2 vv = *(const f32x2*)(A.v + x * DV + 2 * l);
   const float bb = A.b[x];
@@ -1959,17 +1995,42 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
     const int off = 16 * (tid + i * G::NT);
     if (off < CB) *(u32x4*)(stage + off) = chunk[i];
   }
+  rs.nat[tid < DK ? 0 : 2][ir] = n0;
+  rs.nat[tid < DK ? 1 : 3][ir] = n1;
+  if (tid < DK) rs.nat[4][ir] = n2;
+  if (tid < 64) ((float*)rs.azero)[tid] = 0.f;
+  if (tid < 8) rs.kzero[tid] = 0.f;
+  lds_barrier();
+  float kk = 0.f, qq = 0.f, ai = 1.f, sgr = 1.f;
+  if (rsub == 0) {
+    kk = rs.nat[0][irow];
+    qq = rs.nat[1][irow];
+    ai = A.gate ? rs.nat[2][irow] : a_h;
+    sgr = pn == 16 ? 1.f : rs.nat[3][irow];
+  }
   // A zero (or subnormal) gate drops a quantized row's old state, S'_i = k_i delta:
   // the row is carried with factor gf = 1 and its codes are cleared before the
   // update.  Pivot rows update as S' = g v + k delta (kappa = k, no division).
   const float g = ai * sgr;
   const bool zg = rsub == 0 && pn != 16 && !(g >= 0x1p-126f);
   const float gf = zg ? 1.f : g;
+  // binary16 range of the wave's matvec operand: scale by the largest g of its rows
+  float sc, inv;
+  fp16_scale(wave_max_pos(rsub == 0 && pn != 16 ? g : 0.f), sc, inv);
   float kq = 0.f;
   if (rsub == 0) {
-    rs.ab[rho] = pn == 16 ? f32x2{0.f, 0.f} : f32x2{g * kk, g * qq};
+    const float gs = pn == 16 ? 0.f : g * sc;
+    const float al = gs * kk, be = gs * qq;
+    const f16 ah = (f16)al, bh = (f16)be;
+    f16* af = &rs.afr[rho >> 3][0][rho & 7];
+    af[0] = ah;
+    af[8] = (f16)(al - (float)ah);
+    af[16] = bh;
+    af[24] = (f16)(be - (float)bh);
     rs.abp[rho] = f32x2{g * kk, g * qq};
-    rs.kappa[rho] = pn == 16 ? kk : kk * __builtin_amdgcn_rcpf(gf);
+    const float kap = pn == 16 ? kk : kk * __builtin_amdgcn_rcpf(gf);
+    rs.kappa[rho] = kap;
+    rs.kapT[w][rho & 3][(rho >> 2) & 7] = pn == 16 ? 0.f : kap;
     rs.gg[rho] = gf;
     rs.zf[rho] = zg ? 1.f : 0.f;
     kq = kk * qq;
@@ -1979,83 +2040,109 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   const bool zgw = __ballot(zg) != 0;
   if (l == 0) { rs.kqp[w] = kq; rs.notone[w] = (ne1 ? 1 : 0) | (zgw ? 2 : 0); }
   const float cc0 = bf16f(cw & 0xFFFFu), cc1 = bf16f(cw >> 16);
-  lds_barrier();
+  lds_wave_fence();                      // the A fragments and kappa of the wave's rows are its own lanes'
 
-  // ---- unpack and the two reductions over the rows: (a S)^T k, (a S)^T q ----
-  // Record rows from c8 on are binary16 pivots: the unrolled loops run them as
-  // 8-bit rows with zero weights (ab, rq) and a store sink, and the row loops
-  // after them do their real work.
-  const int rN = __builtin_amdgcn_readfirstlane(min(max(c8 - ws0, 0), G::NR));   // quantized rows of the wave
-  f16x2 P[G::NR];
-  float U0 = 0.f, U1 = 0.f, W0 = 0.f, W1 = 0.f;
+  // ---- unpack into column pairs, per 8-row group ----
+  // Record rows from c8 on are binary16 pivots: a group that holds them with
+  // other rows decodes them as 8-bit fields under zero weights (A, kappa, rq),
+  // and the pivot loops below do their real work.
+  const int rN = __builtin_amdgcn_readfirstlane(min(max(c8 - ws0, 0), 32));   // quantized rows of the wave
+  f16x2 P2[2][16];
   {
     int k4 = c4, k6 = c6, k8 = c8;
-    asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));   // per-phase scalar run bounds
-    uint32_t sbase = (uint32_t)(uintptr_t)stage;      // LDS address of the staged codes
-    const uint32_t soff = (uint32_t)(uintptr_t)stage;
-    // the 32 steps; dec(r) returns the lane's two codes of record row ws0 + r
-    auto steps = [&](auto dec, uint32_t& sb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < G::NR; r++) {
-        P[r] = dec(r, sb);
-        const f32x2 abr = rs.ab[ws0 + r];
-        const float q0 = (float)P[r][0], q1 = (float)P[r][1];
-        U0 = __builtin_fmaf(q0, abr[0], U0);
-        U1 = __builtin_fmaf(q1, abr[0], U1);
-        W0 = __builtin_fmaf(q0, abr[1], W0);
-        W1 = __builtin_fmaf(q1, abr[1], W1);
-        // four steps at a time (the next four steps' loads wait for these sums):
-        // enough LDS reads in flight, and the scheduler cannot hoist all 32
-        // steps' loads (which spills)
-        if ((r & 3) == 3) asm volatile("" : "+v"(sb) : "v"(U0), "v"(U1), "v"(W0), "v"(W1));
-      }
-    };
-    // A wave whose 32 rows share one width (no pivots) decodes with that
-    // width's constant record stride and field layout
-    const int uw = ws0 + G::NR <= k4 ? 4 : (ws0 >= k4 && ws0 + G::NR <= k6 ? 6 : (ws0 >= k6 && ws0 + G::NR <= k8 ? 8 : 0));
+    asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));   // per-group scalar run bounds
     const uint32_t k64 = vconst(0x64006400u);
-    if (uw == 4) {
-      // 64-byte records, the lane's byte l: fields at bits 0 and 4
-      const uint32_t a0 = 64 * ws0 + l;
-      const f16x2 kb = as_h2(0xE408E408u);            // -(1024 + 8)
-      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
-        const uint32_t b = *(const uint8_t*)(stage + ((sb + a0 + 64 * r) - soff));
-        return as_h2(((b | (b << 12)) & 0x000F000Fu) | k64) + kb;
-      }, sbase);
-    } else if (uw == 6) {
-      // 96-byte records: the lane's 12 bits start at bit 12 l
-      const uint32_t a0 = 64 * k4 + 96 * (ws0 - k4) + 4 * ((12 * l) >> 5), sh = (12 * l) & 31;
-      const f16x2 kb = as_h2(0xE420E420u);            // -(1024 + 32)
-      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
-        const uint32_t* sw = (const uint32_t*)(stage + ((sb + a0 + 96 * r) - soff));
-        const uint32_t g = __builtin_amdgcn_alignbit(sw[1], sw[0], sh);   // bits 12.. are the next lanes'
-        return as_h2(((g << 10) & 0x003F0000u) | ((g & 0x3Fu) | k64)) + kb;
-      }, sbase);
-    } else if (uw == 8) {
-      // 128-byte records, the lane's 16 bits at byte 2 l
-      const uint32_t a0 = 64 * k4 + 96 * (k6 - k4) + 128 * (ws0 - k6) + 2 * l;
-      const f16x2 kb = as_h2(0xE480E480u);            // -(1024 + 128)
-      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
-        const uint32_t hw = *(const uint16_t*)(stage + ((sb + a0 + 128 * r) - soff));
-        return as_h2(__builtin_amdgcn_perm(0x64646464u, hw, 0x04010400u)) + kb;
-      }, sbase);
-    } else {
-      steps([&](int r, uint32_t sb) __attribute__((always_inline)) {
-        // the lane's two codes start at bit 2 n l of the record: one 64-bit window, two fields
-        const int p = ws0 + r;
-        const int n = 4 + (p >= k4 ? 2 : 0) + (p >= k6 ? 2 : 0);
-        const int rec = 64 * p + 32 * max(p - k4, 0) + 32 * max(p - k6, 0);
-        const uint32_t bit = (uint32_t)(2 * n) * (uint32_t)l;
-        const uint32_t* sw = (const uint32_t*)(stage + ((sb + rec + 4 * (bit >> 5)) - soff));
-        const uint32_t g = __builtin_amdgcn_alignbit(sw[1], sw[0], bit);
-        const uint32_t f0 = __builtin_amdgcn_ubfe(g, 0, n), f1 = __builtin_amdgcn_ubfe(g, n, n);
-        const uint32_t kb = (0xE400u + (1u << (n - 1))) * 0x10001u;   // -(1024 + 2^(n-1)), both halves
-        return as_h2(f0 | (f1 << 16) | 0x64006400u) + as_h2(kb);
-      }, sbase);
+    // 4-bit: byte l of two records 64 bytes apart -> bytes 0 and 2
+    const uint32_t sel4 = (uint32_t)(l & 3) | 0x0C00u | ((uint32_t)(4 + (l & 3)) << 16) | 0x0C000000u;
+    // 8-bit: bytes 2l, 2l + 1 of two records 128 bytes apart
+    const uint32_t h1 = 2u * (uint32_t)(l & 1);
+    const uint32_t sel8 = h1 | ((h1 + 1u) << 8) | ((h1 + 4u) << 16) | ((h1 + 5u) << 24);
+    // 6-bit: the lane's 12 bits start at bit 12 l
+    const uint32_t sh6 = (12u * (uint32_t)l) & 31u;
+    const int d6 = 4 * ((12 * l) >> 5);
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const int p0 = ws0 + 8 * s;
+      const int kind = (kinds >> (8 * s)) & 0xFF;
+      if (kind == 4) {
+        const f16x2 off = as_h2(0xE408E408u);           // -(1024 + 8)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const uint32_t* a = (const uint32_t*)(stage + 64 * (p0 + 2 * q) + (l & ~3));
+          const uint32_t xx = __builtin_amdgcn_perm(a[16], a[0], sel4);
+          P2[0][4 * s + q] = as_h2((xx & 0x000F000Fu) | k64) + off;
+          P2[1][4 * s + q] = as_h2(((xx >> 4) & 0x000F000Fu) | k64) + off;
+        }
+      } else if (kind == 6) {
+        const f16x2 off = as_h2(0xE420E420u);           // -(1024 + 32)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const uint32_t* a = (const uint32_t*)(stage + 64 * k4 + 96 * (p0 + 2 * q - k4) + d6);
+          const uint32_t g0 = __builtin_amdgcn_alignbit(a[1], a[0], sh6);
+          const uint32_t g1 = __builtin_amdgcn_alignbit(a[25], a[24], sh6);
+          const uint32_t xx = (g0 & 0xFFFu) | (g1 << 16);
+          P2[0][4 * s + q] = as_h2((xx & 0x003F003Fu) | k64) + off;
+          P2[1][4 * s + q] = as_h2(((xx >> 6) & 0x003F003Fu) | k64) + off;
+        }
+      } else if (kind == 8) {
+        const f16x2 off = as_h2(0xE480E480u);           // -(1024 + 128)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const uint32_t* a = (const uint32_t*)(stage + 64 * k4 + 96 * (k6 - k4) + 128 * (p0 + 2 * q - k6) + 4 * (l >> 1));
+          const uint32_t xx = __builtin_amdgcn_perm(a[32], a[0], sel8);
+          P2[0][4 * s + q] = as_h2(__builtin_amdgcn_perm(0x64646464u, xx, 0x04020400u)) + off;
+          P2[1][4 * s + q] = as_h2(__builtin_amdgcn_perm(0x64646464u, xx, 0x04030401u)) + off;
+        }
+      } else if (kind == 16) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) P2[0][4 * s + q] = P2[1][4 * s + q] = as_h2(0u);
+      } else {
+        // mixed widths: the lane's two codes start at bit 2 n l of the record
+        uint32_t f0[8], f1[8];
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+          const int p = p0 + r;
+          const int n = 4 + (p >= k4 ? 2 : 0) + (p >= k6 ? 2 : 0);
+          const int rec = 64 * p + 32 * max(p - k4, 0) + 32 * max(p - k6, 0);
+          const uint32_t bit = (uint32_t)(2 * n) * (uint32_t)l;
+          const uint32_t* sw = (const uint32_t*)(stage + rec + 4 * (bit >> 5));
+          const uint32_t gw = __builtin_amdgcn_alignbit(sw[1], sw[0], bit);
+          f0[r] = __builtin_amdgcn_ubfe(gw, 0, n);
+          f1[r] = __builtin_amdgcn_ubfe(gw, n, n);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int pa = p0 + 2 * q, pb = pa + 1;
+          const int na = 4 + (pa >= k4 ? 2 : 0) + (pa >= k6 ? 2 : 0);
+          const int nb = 4 + (pb >= k4 ? 2 : 0) + (pb >= k6 ? 2 : 0);
+          // -(1024 + 2^(n-1)) in each half
+          const uint32_t kb = (0xE400u + (1u << (na - 1))) | ((0xE400u + (1u << (nb - 1))) << 16);
+          P2[0][4 * s + q] = as_h2(f0[2 * q] | (f0[2 * q + 1] << 16) | k64) + as_h2(kb);
+          P2[1][4 * s + q] = as_h2(f1[2 * q] | (f1[2 * q + 1] << 16) | k64) + as_h2(kb);
+        }
+      }
+    }
+  }
+
+  // ---- (a S)^T k and (a S)^T q on the matrix cores ----
+  f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+  {
+    const f16* ab = own ? &rs.afr[ws0 >> 3][n16 & 3][0] : &rs.azero[0][0][0];
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const f16x8 af = *(const f16x8*)(ab + 32 * s);
+      const f16x8 b0 = __builtin_shufflevector(__builtin_shufflevector(P2[0][4 * s], P2[0][4 * s + 1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(P2[0][4 * s + 2], P2[0][4 * s + 3], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+      const f16x8 b1 = __builtin_shufflevector(__builtin_shufflevector(P2[1][4 * s], P2[1][4 * s + 1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(P2[1][4 * s + 2], P2[1][4 * s + 3], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+      D0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b0, D0, 0, 0, 0);
+      D1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b1, D1, 0, 0, 0);
     }
   }
   float Up0 = 0.f, Up1 = 0.f, Wp0 = 0.f, Wp1 = 0.f;
-  for (int r = rN; r < G::NR; r++) {               // binary16 pivot rows
+  for (int r = rN; r < 32; r++) {                  // binary16 pivot rows
     const int p = ws0 + r;
     const f16x2 v2 = as_h2(*(const uint32_t*)(stage + 256 * p + o16 + 4 * l));
     const f32x2 abr = rs.abp[p];
@@ -2064,8 +2151,12 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
     Wp0 = __builtin_fmaf((float)v2[0], abr[1], Wp0);
     Wp1 = __builtin_fmaf((float)v2[1], abr[1], Wp1);
   }
-  *(f32x2*)&rs.red[w][0][2 * l] = f32x2{__builtin_fmaf(cc0, U0, Up0), __builtin_fmaf(cc1, U1, Up1)};
-  *(f32x2*)&rs.red[w][1][2 * l] = f32x2{__builtin_fmaf(cc0, W0, Wp0), __builtin_fmaf(cc1, W1, Wp1)};
+  {
+    const float U0 = (D0[0] + D0[1]) * inv, W0 = (D0[2] + D0[3]) * inv;
+    const float U1 = (D1[0] + D1[1]) * inv, W1 = (D1[2] + D1[3]) * inv;
+    *(f32x2*)&rs.red[w][0][2 * l] = f32x2{__builtin_fmaf(cc0, U0, Up0), __builtin_fmaf(cc1, U1, Up1)};
+    *(f32x2*)&rs.red[w][1][2 * l] = f32x2{__builtin_fmaf(cc0, W0, Wp0), __builtin_fmaf(cc1, W1, Wp1)};
+  }
   lds_barrier();
   int flags = 0;
   float kqs = 0.f;
@@ -2083,24 +2174,47 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   if (bb == 0.f && allone) return;      // identity update: keep the encoding
   if (flags & 2) {                       // some gate is zero (rare): clear those rows' codes
 #pragma unroll
-    for (int r = 0; r < G::NR; r++)
-      if (rs.zf[ws0 + r] != 0.f) P[r] = f16x2{(f16)0.f, (f16)0.f};
+    for (int m = 0; m < 16; m++) {
+      const uint32_t mk = (rs.zf[ws0 + 2 * m] != 0.f ? 0u : 0xFFFFu) | (rs.zf[ws0 + 2 * m + 1] != 0.f ? 0u : 0xFFFF0000u);
+      P2[0][m] = as_h2(h2_bits(P2[0][m]) & mk);
+      P2[1][m] = as_h2(h2_bits(P2[1][m]) & mk);
+    }
   }
 
-  // ---- rank-one update, Y = S' / g; row partial maxima over lane pairs ----
-  float Y[2 * G::NR];
-  opaque(P);                             // each use converts inside its own v_fma_mix_f32
+  // ---- rank-one update on the matrix cores, Y = S' / g; row partial maxima ----
+  float Y[2][32];
+  opaque(&P2[0][0]);                     // each use converts inside its own v_fma_mix_f32
+  {
+    const float* kb = own ? &rs.kapT[w][n16 & 3][0] : rs.kzero;
+    const f32x4 ka = *(const f32x4*)kb, kc = *(const f32x4*)(kb + 4);
+    const float kap[8] = {ka[0], ka[1], ka[2], ka[3], kc[0], kc[1], kc[2], kc[3]};
+#pragma unroll
+    for (int t = 0; t < 8; t++)
+#pragma unroll
+      for (int c = 0; c < 2; c++) {
+        const float ccc = c ? cc1 : cc0;
+        f32x4 C;
+        // fma with a +0 addend: one v_fma_mix_f32 per code, straight from fp16
+        C[0] = __builtin_fmaf((float)P2[c][2 * t][0], ccc, 0.0f);
+        C[1] = __builtin_fmaf((float)P2[c][2 * t][1], ccc, 0.0f);
+        C[2] = __builtin_fmaf((float)P2[c][2 * t + 1][0], ccc, 0.0f);
+        C[3] = __builtin_fmaf((float)P2[c][2 * t + 1][1], ccc, 0.0f);
+        C = __builtin_amdgcn_mfma_f32_16x16x4f32(kap[t], c ? d1 : d0, C, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) Y[c][4 * t + i] = C[i];
+      }
+  }
   float* partl = part + ws0 * G::PSTR + (l >> 1);
 #pragma unroll
-  for (int r = 0; r < G::NR; r++) {
-    const float kr = rs.kappa[ws0 + r];
-    Y[2 * r] = __builtin_fmaf((float)P[r][0], cc0, kr * d0);
-    Y[2 * r + 1] = __builtin_fmaf((float)P[r][1], cc1, kr * d1);
-    uint32_t m = __float_as_uint(__builtin_fmaxf(__builtin_fabsf(Y[2 * r]), __builtin_fabsf(Y[2 * r + 1])));
+  for (int r = 0; r < 32; r++) {
+    // max(|Y0|, |Y1|) as one instruction: the matrix-core results need no
+    // NaN quieting first (fmaxf would add one per operand)
+    uint32_t m;
+    asm("v_max_f32_e64 %0, |%1|, |%2|" : "=v"(m) : "v"(Y[0][r]), "v"(Y[1][r]));
     m = __builtin_elementwise_max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, true));
     partl[r * G::PSTR] = __uint_as_float(m);
   }
-  lds_barrier();
+  lds_wave_fence();                      // row rho's partials come from the wave that reduces them
 
   // ---- row refit (one thread pair per record row) ----
   uint32_t mxb = 0u;
@@ -2112,7 +2226,7 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   }
   mxb = __builtin_elementwise_max(mxb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mxb, 0xB1, 0xF, 0xF, false));
   const float gr = (pn != 16 && !(ai * sgr >= 0x1p-126f)) ? 1.f : ai * sgr;   // the row's factor gf, again
-  const float pw = (gr * __uint_as_float(mxb)) * A.weights[(size_t)h * DK + irow];
+  const float pw = (gr * __uint_as_float(mxb)) * rs.nat[4][irow];
   uint32_t s = 0x3F80u;
   int epk = 0;
   if (pn != 16 && pw > 0.f) {
@@ -2126,29 +2240,58 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   }
   epk = wave_sum_i(epk);
   if (l == 0) { rs.esum[w] = epk >> 8; rs.ecnt[w] = epk & 0xFF; }
-  lds_barrier();
+  lds_wave_fence();                      // X factors of the wave's rows are its own lanes'
+
+  // ---- column refit: X = Y h; a group of one width takes its absmax first ----
+  float cm0 = 0.f, cm1 = 0.f;
+  {
+    int k4 = c4, k6 = c6, k8 = c8;
+    asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));
+#pragma unroll
+    for (int sg = 0; sg < 4; sg++) {
+      const int p0 = ws0 + 8 * sg;
+      const int kind = (kinds >> (8 * sg)) & 0xFF;
+      if (kind == 16) continue;
+      const f32x4 ha = *(const f32x4*)&rs.rowh[p0], hb = *(const f32x4*)&rs.rowh[p0 + 4];
+      const float hr[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+#pragma unroll
+      for (int r = 0; r < 8; r++) {
+        Y[0][8 * sg + r] *= hr[r];
+        Y[1][8 * sg + r] *= hr[r];
+      }
+      if (kind == 0) {
+        const f32x4 qa = *(const f32x4*)&rs.rq[p0], qb = *(const f32x4*)&rs.rq[p0 + 4];
+        const float rq[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+          cm0 = __builtin_fmaxf(cm0, __builtin_fabsf(Y[0][8 * sg + r]) * rq[r]);
+          cm1 = __builtin_fmaxf(cm1, __builtin_fabsf(Y[1][8 * sg + r]) * rq[r]);
+        }
+      } else {
+        // fl(|X| / qmax-product) is monotonic in |X|: one product per group
+        float g0 = 0.f, g1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+          g0 = __builtin_fmaxf(g0, __builtin_fabsf(Y[0][8 * sg + r]));
+          g1 = __builtin_fmaxf(g1, __builtin_fabsf(Y[1][8 * sg + r]));
+        }
+        const float rk = kind == 4 ? 1.0f / 7.0f : (kind == 6 ? 1.0f / 31.0f : 1.0f / 127.0f);
+        cm0 = __builtin_fmaxf(cm0, g0 * rk);
+        cm1 = __builtin_fmaxf(cm1, g1 * rk);
+      }
+    }
+  }
+  *(f32x2*)&rs.cmx[w][2 * l] = f32x2{cm0, cm1};
+  lds_barrier();                         // exponent sums and column maxima of every wave
   int es = 0, ec = 0;
 #pragma unroll
   for (int ww = 0; ww < G::NW; ww++) { es += rs.esum[ww]; ec += rs.ecnt[ww]; }
   const int E = ec ? mean_exp(es, ec) : 0;
   if (rsub == 0) scl[irow] = (uint16_t)bf16_adj(s, -E);
-
-  // ---- column refit ----
-  float cm0 = 0.f, cm1 = 0.f;
-#pragma unroll
-  for (int r = 0; r < G::NR; r++) {
-    const float hr = rs.rowh[ws0 + r], rq = rs.rq[ws0 + r];
-    Y[2 * r] = Y[2 * r] * hr;
-    Y[2 * r + 1] = Y[2 * r + 1] * hr;
-    cm0 = __builtin_fmaxf(cm0, __builtin_fabsf(Y[2 * r]) * rq);
-    cm1 = __builtin_fmaxf(cm1, __builtin_fabsf(Y[2 * r + 1]) * rq);
-  }
-  *(f32x2*)&rs.red[w][0][2 * l] = f32x2{cm0, cm1};
-  lds_barrier();
-  f32x2 M2 = *(const f32x2*)&rs.red[0][0][2 * l];
+  f32x2 M2 = *(const f32x2*)&rs.cmx[0][2 * l];
 #pragma unroll
   for (int ww = 1; ww < G::NW; ww++) {
-    const f32x2 o2 = *(const f32x2*)&rs.red[ww][0][2 * l];
+    const f32x2 o2 = *(const f32x2*)&rs.cmx[ww][2 * l];
     M2[0] = __builtin_fmaxf(M2[0], o2[0]);
     M2[1] = __builtin_fmaxf(M2[1], o2[1]);
   }
@@ -2166,43 +2309,66 @@ __global__ __launch_bounds__((GeoW<DK>::NT)) __attribute__((amdgpu_waves_per_eu(
   }
   if (w == 0) *(uint32_t*)(scl + DK + 2 * l) = cb[0] | (cb[1] << 16);
 
-  // ---- requantize into the staged records ----
-  const int q4 = l & 3, pq = q4 < 2 ? q4 : 2;      // 6-bit: lane q4 of a quad writes 16-bit piece pq
-  const int L6w = 6 * (l >> 2) + 2 * pq;
-  const uint32_t sh6 = 20 + 4 * pq;
-  const int sink = CB + 16;                        // 128 bytes past the codes: stores of pivot steps
-  int k4 = c4, k6 = c6, k8 = c8;
-  asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));
-  float mg4 = Fmt<4>::MAGIC, mg6 = Fmt<6>::MAGIC, mg8 = Fmt<8>::MAGIC;
-  asm volatile("" : "+s"(mg4), "+s"(mg6), "+s"(mg8));   // scalar operands of the fma
-#pragma unroll
-  for (int r = 0; r < G::NR; r++) {
-    const int p = ws0 + r;
-    if (p < k4) {
-      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], mg4));
-      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], mg4));
+  // ---- requantize into the staged records, per 8-row group ----
+  {
+    const int q4 = l & 3, pq = q4 < 2 ? q4 : 2;    // 6-bit: lane q4 of a quad writes 16-bit piece pq
+    const int L6w = 6 * (l >> 2) + 2 * pq;
+    const uint32_t sh6 = 20 + 4 * pq;
+    const int sink = CB + 16;                      // past the codes: stores of pivot rows in mixed groups
+    int k4 = c4, k6 = c6, k8 = c8;
+    asm volatile("" : "+s"(k4), "+s"(k6), "+s"(k8));
+    float mg4 = Fmt<4>::MAGIC, mg6 = Fmt<6>::MAGIC, mg8 = Fmt<8>::MAGIC;
+    asm volatile("" : "+s"(mg4), "+s"(mg6), "+s"(mg8));   // scalar operands of the fma
+    auto put4 = [&](int p, int r) __attribute__((always_inline)) {
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[0][r], rc[0], mg4));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[1][r], rc[1], mg4));
       stage[64 * p + l] = (uint8_t)(y0 | (y1 << 4));
-    } else if (p < k6) {
+    };
+    auto put6 = [&](int p, int r) __attribute__((always_inline)) {
       // a lane quad holds two 3-byte groups: 12 bits per lane, written as three 16-bit pieces
-      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], mg6));
-      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], mg6));
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[0][r], rc[0], mg6));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[1][r], rc[1], mg6));
       const uint32_t g12 = y0 | (y1 << 6);
       const uint32_t ga = (uint32_t)__builtin_amdgcn_mov_dpp((int)g12, 0xA4, 0xF, 0xF, true);   // lane pq
       const uint32_t gb = (uint32_t)__builtin_amdgcn_mov_dpp((int)g12, 0xF9, 0xF, 0xF, true);   // lane pq + 1
       *(uint16_t*)(stage + 96 * p + o6 + L6w) = (uint16_t)__builtin_amdgcn_alignbit(gb, ga << 20, sh6);
-    } else {
-      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[2 * r], rc[0], mg8));
-      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[2 * r + 1], rc[1], mg8));
-      *(uint16_t*)(stage + (p < k8 ? 128 * p + o8 : sink) + 2 * l) = (uint16_t)(y0 | (y1 << 8));
+    };
+    auto put8 = [&](int off, int r) __attribute__((always_inline)) {
+      const uint32_t y0 = __float_as_uint(__builtin_fmaf(Y[0][r], rc[0], mg8));
+      const uint32_t y1 = __float_as_uint(__builtin_fmaf(Y[1][r], rc[1], mg8));
+      *(uint16_t*)(stage + off + 2 * l) = (uint16_t)(y0 | (y1 << 8));
+    };
+#pragma unroll
+    for (int sg = 0; sg < 4; sg++) {
+      const int p0 = ws0 + 8 * sg;
+      const int kind = (kinds >> (8 * sg)) & 0xFF;
+      if (kind == 4) {
+#pragma unroll
+        for (int r = 0; r < 8; r++) put4(p0 + r, 8 * sg + r);
+      } else if (kind == 6) {
+#pragma unroll
+        for (int r = 0; r < 8; r++) put6(p0 + r, 8 * sg + r);
+      } else if (kind == 8) {
+#pragma unroll
+        for (int r = 0; r < 8; r++) put8(128 * (p0 + r) + o8, 8 * sg + r);
+      } else if (kind == 0) {
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+          const int p = p0 + r;
+          if (p < k4) put4(p, 8 * sg + r);
+          else if (p < k6) put6(p, 8 * sg + r);
+          else put8(p < k8 ? 128 * p + o8 : sink, 8 * sg + r);
+        }
+      }
     }
   }
-  for (int r = rN; r < G::NR; r++) {               // binary16 pivot rows: S' = g v + k delta
+  for (int r = rN; r < 32; r++) {                  // binary16 pivot rows: S' = g v + k delta
     const int p = ws0 + r;
     const int off = 256 * p + o16 + 4 * l;
     const f16x2 v2 = as_h2(*(const uint32_t*)(tile + off));   // the tile's bytes are unchanged until the store
-    const float kr = rs.kappa[p], gr = rs.gg[p];
-    const float s0 = __builtin_fminf(__builtin_fmaxf(__builtin_fmaf((float)v2[0], gr, kr * d0), -65504.f), 65504.f);
-    const float s1 = __builtin_fminf(__builtin_fmaxf(__builtin_fmaf((float)v2[1], gr, kr * d1), -65504.f), 65504.f);
+    const float kr = rs.kappa[p], gq = rs.gg[p];
+    const float s0 = __builtin_fminf(__builtin_fmaxf(__builtin_fmaf((float)v2[0], gq, kr * d0), -65504.f), 65504.f);
+    const float s1 = __builtin_fminf(__builtin_fmaxf(__builtin_fmaf((float)v2[1], gq, kr * d1), -65504.f), 65504.f);
     *(uint32_t*)(stage + off) = h2_bits(f16x2{(f16)s0, (f16)s1});
   }
   lds_barrier();
@@ -3199,9 +3365,9 @@ struct LRows {
 stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st) {
   const unsigned g = grid_of(A.n, A.H);
   if (p->dv == 128 && p->dk == 128)
-    hipLaunchKernelGGL((k_rows_wide<128>), dim3(g), dim3(GeoW<128>::NT), A.stage_bytes, st, A);
+    hipLaunchKernelGGL((k_rows_mf<128>), dim3(g), dim3(GeoRM<128>::NT), A.stage_bytes, st, A);
   else if (p->dv == 128)
-    hipLaunchKernelGGL((k_rows_wide<64>), dim3(g), dim3(GeoW<64>::NT), A.stage_bytes, st, A);
+    hipLaunchKernelGGL((k_rows_mf<64>), dim3(g), dim3(GeoRM<64>::NT), A.stage_bytes, st, A);
   else if (p->dk == 128)
     hipLaunchKernelGGL((k_rows_step<128, 64>), dim3(g), dim3(GeoR<128, 64>::NT), A.stage_bytes, st, A);
   else

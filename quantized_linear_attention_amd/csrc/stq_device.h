@@ -80,6 +80,10 @@ template <> struct Fmt<16> { static constexpr int QMAX = 0;   static constexpr f
 // operations, not for its vector-memory ones (stores in flight stay in
 // flight; a fenced __syncthreads would wait for them).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Order LDS traffic inside one wave: its LDS operations run in issue order, so
+// once its own writes have completed, any lane of the wave reads what another
+// lane wrote (the clobber keeps the compiler from moving accesses across).
+__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Load from memory that no kernel writes while it runs (call tables, pool
 // header): the constant address space lets it go through the scalar cache.
