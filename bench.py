@@ -13,7 +13,8 @@ pool (stq_prefill; one step = one call over all prompts).
 
 Prints one JSON line with throughput, the dominant kernel's roofline figure
 (algorithmic bytes / average kernel duration, from HIP events on the launch
-stream) and the CPU oracle timed on a bounded sample of the same workload.
+stream, one event per round over the layer pools; p10/p90 are over those
+rounds) and the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -118,10 +119,12 @@ BENCH = {
                      "per-key-row widths)",
            "workload": "KDA pool B=256 H=32 d_k=d_v=128, per-channel gate, key rows "
                        "{4b:30%, 6b:50%, 8b:19%, fp16:1%}",
-           "dtype": "f32 update, per-key-row 4/6/8-bit + f16 state"},
+           "dtype": "f32 update and refit; the two matvecs on matrix cores with each f32 operand split into "
+                    "f16 hi + lo (f32 accumulation), the rank-one update on f32 matrix cores; per-key-row "
+                    "4/6/8-bit + f16 state"},
     "C5": {"layers": 2,
-           "kernel": "k_window_read<128, 128, false> + k_window_fold<128, 128, true, false>",
-           "regex": "k_window_(read<128, 128, false>|fold<128, 128, true, false>)",
+           "kernel": "k_window_read<128, 128, false, true> + k_window_fold<128, 128, true, false>",
+           "regex": "k_window_(read<128, 128, false, true>|fold<128, 128, true, false>)",
            "prof": "k_window_step",
            "metric": "request-head decode steps/s (B=512, H=32, d=128, 4-bit GDN, window W=16)",
            "workload": "windowed GDN pool B=512 H=32 d_k=d_v=128, all heads 4-bit, W=16 "
@@ -267,17 +270,24 @@ def main():
         per = np.array([ev[r].elapsed_time(ev[r + 1]) / G for r in range(R)])
         Wu += G
     else:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        # one event per round over the layer pools (at least 4 launches): an
+        # event between every two launches adds a packet and a gap that a
+        # serving loop does not have (about 6 us per C3 launch)
+        M = max(L, 4)
+        K = -(-K // M) * M
+        R = K // M
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
         torch.cuda.synchronize()
         start.record()
-        for s in range(K):
-            ev[s].record()
-            step(Wu + s)
-        ev[K].record()
+        for r in range(R):
+            ev[r].record()
+            for s in range(r * M, (r + 1) * M):
+                step(Wu + s)
+        ev[R].record()
         stop.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(stop)
-        per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(K)])
+        per = np.array([ev[r].elapsed_time(ev[r + 1]) / M for r in range(R)])
     avg_ms = float(per.mean())
     if c.window:
         # launch s is token (Wu + s) // L of its pool: window position that mod W
@@ -309,7 +319,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "traffic_gbs": None if traffic is None else traffic / (avg_ms * 1e-3) / 1e9,
-                     "kernel": spec["kernel"].replace("false>", "true>") if C else spec["kernel"],
+                     "kernel": spec["kernel"].replace("read<128, 128, false,", "read<128, 128, true,")
+                                             .replace("fold<128, 128, true, false>", "fold<128, 128, true, true>")
+                               if C else spec["kernel"],
                      "bytes_per_launch": bytes_step,
                      "avg_launch_ms": avg_ms, "p10_ms": float(np.percentile(per, 10)),
                      "p90_ms": float(np.percentile(per, 90))},
