@@ -48,6 +48,7 @@ struct KArgs {
   float* S_out;              // fetch
   uint32_t stage_bytes;      // per-key-row step: LDS bytes of the staged codes / row partials
   const int32_t* seq_start;  // prefill: request c owns tokens seq_start[c] .. seq_start[c+1]-1
+  uint32_t hmul;             // ceil(2^32 / H) when tile index * hmul / 2^32 is exact for every tile, else 0
 };
 
 // LDS of the per-key-row ingest / decode / fixed-scale kernel
@@ -59,6 +60,12 @@ struct Smem {
   int esum[Geo<DK, DV>::NW];
   int ecnt[Geo<DK, DV>::NW];
 };
+
+// Request of tile tau (tiles are request-major): one scalar high multiply by
+// the host's reciprocal of H where that is exact (req_recip), else a division.
+__device__ __forceinline__ int req_of(const KArgs& A, int tau) {
+  return A.hmul ? (int)__umulhi((unsigned)tau, A.hmul) : tau / A.H;
+}
 
 // XCD-aware tile order: workgroups are dealt round-robin over the 8 XCDs, so
 // give XCD x the contiguous tile range [x*per, (x+1)*per): every XCD then
@@ -658,7 +665,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
-  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int ci = req_of(A, tau), h = tau - ci * A.H;
   const int slot = A.slots ? ld_const(A.slots + ci) : ci;
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + ld_const(A.head_off + h);
@@ -1124,7 +1131,7 @@ __device__ __forceinline__ void window_read_tile(const KArgs& A, WRead<DK, DV>& 
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
-  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int ci = req_of(A, tau), h = tau - ci * A.H;
   const int slot = A.slots[ci];
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
@@ -1164,7 +1171,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   {
     const int i = threadIdx.x & 63, tau = t0 + i;
     if (i < (STEP ? FPW : 1) && tau < T) {
-      const int ci = tau / A.H, h = tau - ci * A.H;
+      const int ci = req_of(A, tau), h = tau - ci * A.H;
       const int slot = A.slots[ci];
       if ((unsigned)slot < (unsigned)A.n_slots)
         cnt = *(const int32_t*)(A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride);
@@ -1176,7 +1183,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     const int i = __builtin_ctzll(mask);
     mask &= mask - 1;
     const int tau = t0 + i;
-    const int ci = tau / A.H, h = tau - ci * A.H;
+    const int ci = req_of(A, tau), h = tau - ci * A.H;
     const int slot = A.slots[ci];
     uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
     uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
@@ -1473,7 +1480,7 @@ __global__ __launch_bounds__((Geo<DK, DV>::NT)) void k_rows(KArgs A) {
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
-  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int ci = req_of(A, tau), h = tau - ci * A.H;
   const int slot = A.slots ? A.slots[ci] : ci;
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
@@ -1592,7 +1599,7 @@ __global__ __launch_bounds__((GeoR<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
-  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int ci = req_of(A, tau), h = tau - ci * A.H;
   const int slot = A.slots ? A.slots[ci] : ci;
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
@@ -1942,7 +1949,7 @@ __global__ __launch_bounds__((GeoRM<DK>::NT)) __attribute__((amdgpu_waves_per_eu
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
-  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int ci = req_of(A, tau), h = tau - ci * A.H;
   const int slot = A.slots ? A.slots[ci] : ci;
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
@@ -2425,7 +2432,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) void k_fetch(KArgs A) {
   const int T = A.n * A.H;
   const int tau = tile_of_block(T);
   if (tau >= T) return;
-  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int ci = req_of(A, tau), h = tau - ci * A.H;
   const int slot = A.slots[ci];
   if ((unsigned)slot >= (unsigned)A.n_slots) return;
   uint8_t* tile = A.pool + A.slots_off + (uint64_t)slot * A.slot_bytes + A.head_off[h];
@@ -2445,7 +2452,7 @@ __global__ __launch_bounds__(128) void k_comp_add(KArgs A, int DK, int DV) {
   const int T = A.n * A.H;
   const int tau = (int)blockIdx.x;
   if (tau >= T) return;
-  const int ci = tau / A.H, h = tau - ci * A.H;
+  const int ci = req_of(A, tau), h = tau - ci * A.H;
   const int slot = A.slots[ci];
   if ((unsigned)slot >= (unsigned)A.n_slots || A.head_bits[h] == 16) return;
   const uint8_t* cache = A.pool + A.cache_off + ((uint64_t)slot * A.H + h) * A.cache_stride;
@@ -3311,12 +3318,20 @@ void layout(const stq_pool_desc* d, stq_pool* p) {
 void put32(uint8_t* b, uint32_t v) { memcpy(b, &v, 4); }
 void put64(uint8_t* b, uint64_t v) { memcpy(b, &v, 8); }
 
+// floor(tau * ceil(2^32 / H) / 2^32) = floor(tau / H) whenever tau * (ceil(2^32 / H) H - 2^32) < 2^32,
+// which holds for every tau < n H when n H * H <= 2^32 (the excess is below H)
+uint32_t req_recip(long n, int H) {
+  if (H < 2 || (uint64_t)n * (uint64_t)H * (uint64_t)H > (1ull << 32)) return 0;
+  return (uint32_t)(((1ull << 32) + (uint64_t)H - 1) / (uint64_t)H);
+}
+
 KArgs base_args(const stq_pool* p, const int32_t* slots, int n) {
   KArgs A;
   memset(&A, 0, sizeof(A));
   A.pool = p->dev;
   A.slots = slots;
   A.n = n; A.H = p->H; A.n_slots = p->n_slots; A.gate = p->gate; A.W = p->W; A.C = p->C;
+  A.hmul = req_recip(n, p->H);
   A.slots_off = p->slots_off; A.slot_bytes = p->slot_bytes;
   A.cache_off = p->cache_off; A.cache_stride = p->cache_stride;
   A.head_bits = (const int32_t*)(p->dev + 64);
@@ -3608,6 +3623,7 @@ stq_status stq_prefill_states(int32_t n, int32_t n_heads, int32_t d_k, int32_t d
   KArgs A;
   memset(&A, 0, sizeof(A));
   A.n = n; A.H = n_heads; A.gate = gate_kind;
+  A.hmul = req_recip(n, n_heads);
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
   A.S_out = S;
   A.seq_start = seq_start;

@@ -185,15 +185,17 @@ def _row_width_patterns(dk, rng):
     return np.stack([rng.permutation(p) for p in pats]).astype(np.int32)
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
-def test_rows_step_shapes(torch_cuda, orc, dk, dv):
-    """Per-key-row widths with the per-channel gate at every tile shape: two
-    teacher-forced steps (the oracle steps from the GPU's bytes each time)."""
+@pytest.mark.parametrize("dk,dv,gate", [(128, 128, 1), (64, 64, 1), (64, 128, 1), (128, 64, 1),
+                                         (128, 128, 0), (64, 128, 0)])
+def test_rows_step_shapes(torch_cuda, orc, dk, dv, gate):
+    """Per-key-row widths at every tile shape, with the per-channel gate and
+    (d_v = 128) the per-head gate: two teacher-forced steps (the oracle steps
+    from the GPU's bytes each time)."""
     from types import SimpleNamespace
-    say("case rows step", dk, dv)
-    rng = np.random.default_rng(100 + dk + dv)
+    say("case rows step", dk, dv, "gate", gate)
+    rng = np.random.default_rng(100 + dk + dv + 7 * gate)
     H, B = 8, 6
-    cfg = SimpleNamespace(gate=1, unit=1, window=0)
+    cfg = SimpleNamespace(gate=gate, unit=1, window=0)
     wl = SimpleNamespace(B=B, H=H, dk=dk, dv=dv, cfg=cfg, bits=_row_width_patterns(dk, rng),
                          row_weight=np.clip(np.exp(rng.normal(0, 1.15, (H, dk))), 0.1, 10).astype(np.float32))
     P = Pair(orc, wl, n_slots=B + 2)
@@ -204,18 +206,18 @@ def test_rows_step_shapes(torch_cuda, orc, dk, dv):
     worst = new_agg()
     for t in range(2):
         img = P.image()
-        ref = orc.OraclePool(B + 2, H, dk, dv, wl.bits.reshape(-1), wl.row_weight, 1, 1, 0, image=img)
+        ref = orc.OraclePool(B + 2, H, dk, dv, wl.bits.reshape(-1), wl.row_weight, gate, 1, 0, image=img)
         q = rng.standard_normal((B, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
         k = rng.standard_normal((B, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
         v = rng.standard_normal((B, H, dv))
-        a = 2.0 ** (-1.0 / (10.0 ** rng.uniform(0, 4, (B, H, dk))))
+        a = 2.0 ** (-1.0 / (10.0 ** rng.uniform(0, 4, (B, H, dk) if gate else (B, H))))
         b = rng.uniform(0.05, 0.95, (B, H))
         o = P.gpu_step(slots, f(q), f(k), f(v), f(a), f(b))
         o_ref = ref.step(slots, f(q), f(k), f(v), f(a), f(b))
         r = compare_codes(orc, ref, P.image(), ref.img, slots)
         add_agg(worst, r, readout_ok(o, o_ref))
-    say("  rows %dx%d: code mismatch %d of %d (max |dQ| %d), scale mismatch %d of %d, pivot mismatch %d of %d, "
-        "readout %.3f" % (dk, dv, worst["mism"], worst["codes"], worst["maxd"], worst["scale_mism"],
+    say("  rows %dx%d gate %d: code mismatch %d of %d (max |dQ| %d), scale mismatch %d of %d, pivot mismatch %d of %d, "
+        "readout %.3f" % (dk, dv, gate, worst["mism"], worst["codes"], worst["maxd"], worst["scale_mism"],
                           worst["scales"], worst["piv_mism"], worst["piv"], worst["o"]))
     _assert_codes(worst)
     assert worst["o"] <= 1.0
