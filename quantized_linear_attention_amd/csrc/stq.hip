@@ -2104,26 +2104,26 @@ __global__ __launch_bounds__((GeoRM<DK>::NT)) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int q = 0; q < 4; q++) P2[0][4 * s + q] = P2[1][4 * s + q] = as_h2(0u);
       } else {
-        // mixed widths: the lane's two codes start at bit 2 n l of the record
-        uint32_t f0[8], f1[8];
+        // mixed widths: the lane's two codes start at bit 2 n l of the record;
+        // the width and the record offset advance row by row from the group's
+        // first row
+        uint32_t f0[8], f1[8], kh[8];
+        int rec = 64 * p0 + 32 * max(p0 - k4, 0) + 32 * max(p0 - k6, 0);
 #pragma unroll
         for (int r = 0; r < 8; r++) {
           const int p = p0 + r;
           const int n = 4 + (p >= k4 ? 2 : 0) + (p >= k6 ? 2 : 0);
-          const int rec = 64 * p + 32 * max(p - k4, 0) + 32 * max(p - k6, 0);
           const uint32_t bit = (uint32_t)(2 * n) * (uint32_t)l;
           const uint32_t* sw = (const uint32_t*)(stage + rec + 4 * (bit >> 5));
           const uint32_t gw = __builtin_amdgcn_alignbit(sw[1], sw[0], bit);
           f0[r] = __builtin_amdgcn_ubfe(gw, 0, n);
           f1[r] = __builtin_amdgcn_ubfe(gw, n, n);
+          kh[r] = 0xE400u + (1u << (n - 1));        // -(1024 + 2^(n-1)) as binary16
+          rec += 16 * n;
         }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          const int pa = p0 + 2 * q, pb = pa + 1;
-          const int na = 4 + (pa >= k4 ? 2 : 0) + (pa >= k6 ? 2 : 0);
-          const int nb = 4 + (pb >= k4 ? 2 : 0) + (pb >= k6 ? 2 : 0);
-          // -(1024 + 2^(n-1)) in each half
-          const uint32_t kb = (0xE400u + (1u << (na - 1))) | ((0xE400u + (1u << (nb - 1))) << 16);
+          const uint32_t kb = kh[2 * q] | (kh[2 * q + 1] << 16);
           P2[0][4 * s + q] = as_h2(f0[2 * q] | (f0[2 * q + 1] << 16) | k64) + as_h2(kb);
           P2[1][4 * s + q] = as_h2(f1[2 * q] | (f1[2 * q + 1] << 16) | k64) + as_h2(kb);
         }

@@ -63,11 +63,15 @@ __device__ __forceinline__ uint32_t vconst(uint32_t k) {
   asm volatile("" : "+v"(k));
   return k;
 }
-// floor((2*s + n) / (2n)), n > 0
+// floor((2*s + n) / (2n)), n > 0, |2s + n| < 2^24: the binary32 estimate
+// (v_rcp_f32, relative error near 2^-22) is within one of the floor, and one
+// integer remainder test corrects it (no integer division)
 __device__ __forceinline__ int mean_exp(int s, int n) {
-  int num = 2 * s + n, den = 2 * n;
-  int q = num / den, r = num % den;
-  return (r != 0 && r < 0) ? q - 1 : q;
+  const int num = 2 * s + n, den = 2 * n;
+  int q = (int)__builtin_floorf((float)num * __builtin_amdgcn_rcpf((float)den));
+  const int r = num - q * den;
+  q += (r >= den ? 1 : 0) - (r < 0 ? 1 : 0);
+  return q;
 }
 
 template <int N> struct Fmt;
