@@ -7,9 +7,9 @@ and a free-running report of how the quantized trajectories drift.
   zero rows and columns change nothing else (zero rows have no exponent,
   zero columns scale 1), so the stored values must be the derivation's.
 - The per-key-row KDA step at B = 256 and the windowed step at B = 512 over a
-  whole window (16 tokens, the fold included): the launches the benchmark
-  times, with sampled tiles re-stepped by the oracle from the GPU's bytes
-  (teacher-forced), to the fused step's bar.
+  whole window (16 tokens, the fold included), also with four compensator rows
+  per tile: the launches the benchmark times, with sampled tiles re-stepped by
+  the oracle from the GPU's bytes (teacher-forced), to the fused step's bar.
 - Free-running over C3's 64 tokens: the GPU pool and the oracle's pool each
   advance on their own from the same ingested state, next to the exact
   binary64 recurrence without any quantization.  Reported (per-step error
@@ -139,6 +139,55 @@ def test_full_c5_window_sampled(torch_cuda, orc):
     say("  full C5: readout %.3f, cache u %.2e, fold: %s" % (worst_o, worst_u, agg_text(agg)))
     assert worst_o <= 1.0
     assert worst_u <= 1e-4
+    _assert_codes(agg)
+
+
+def test_full_c5_compensators_sampled(torch_cuda, orc):
+    """The windowed 4-bit pool at B = 512, W = 16, with four compensator rows
+    per tile (the pages' outlier terms riding the window's update path): a
+    whole window, the fold included, with 16 sampled slots re-stepped by the
+    oracle from the GPU's bytes at every token: readout, cached Gamma and k
+    bit-exact, cached u within 1e-4, the kept rows' indices exact and values
+    within 1e-5 relative; at the fold the new base's codes to the fused
+    step's bar."""
+    say("case full C5 with compensators sampled")
+    wl = Workload("C5")
+    W, C = wl.cfg.window, 4
+    P = Pair(orc, wl, n_comp=C)
+    slots = np.arange(wl.B)
+    P.store(slots, wl.state(slots))
+    rng = np.random.default_rng(53)
+    agg = new_agg()
+    worst_o = worst_u = worst_c = 0.0
+    for t in range(W):
+        pre = P.image()
+        q, k, v, a, b = wl.token(t)
+        o = P.gpu_step(slots, q, k, v, a, b)
+        post = P.image()
+        samp = np.sort(rng.choice(wl.B, 16, replace=False))
+        ref = orc.OraclePool(wl.B, wl.H, wl.dk, wl.dv, wl.bits, wl.row_weight, window=W, image=pre, n_comp=C)
+        o_ref = ref.step(samp, q[samp], k[samp], v[samp], a[samp], b[samp])
+        worst_o = max(worst_o, readout_ok(o[samp], o_ref))
+        for s in samp[:4]:
+            for h in range(wl.H):
+                cg, Gg, Kg, Ug, ig, vg = ref.cache_view(int(s), h, post)
+                cr, Gr, Kr, Ur, ir, vr = ref.cache_view(int(s), h)
+                assert cg == cr == (t + 1) % W
+                np.testing.assert_array_equal(Gg[:cg], Gr[:cr])
+                np.testing.assert_array_equal(Kg[:cg], Kr[:cr])
+                if cg:
+                    worst_u = max(worst_u, float(np.abs(Ug[:cg] - Ur[:cr]).max() / np.abs(Ur[:cr]).max()))
+                np.testing.assert_array_equal(ig, ir)
+                if (ir >= 0).any():
+                    worst_c = max(worst_c, float(np.abs(vg - vr).max() / np.abs(vr).max()))
+        if t + 1 == W:
+            add_agg(agg, compare_codes(orc, ref, post, ref.img, samp))
+        assert np.isfinite(o).all()
+    say("  full C5 C=4: readout %.3f, cache u %.2e, compensators %.2e, fold: %s"
+        % (worst_o, worst_u, worst_c, agg_text(agg)))
+    assert worst_o <= 1.0
+    assert worst_u <= 1e-4
+    assert worst_c <= 1e-5
     _assert_codes(agg)
 
 
