@@ -1938,9 +1938,11 @@ __device__ __forceinline__ int group_kind(int p0, int c4, int c6, int c8) {
   return 0;
 }
 
-template <int DK>
+// NCH: 16-byte chunk rounds of the staged codes, enough for the pool's largest head
+template <int DK, int NCH>
 __global__ __launch_bounds__((GeoRM<DK>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_mf(KArgs A) {
   using G = GeoRM<DK>;
+  static_assert(NCH <= G::NCH, "chunk rounds");
   constexpr int DV = 128;
   __shared__ RMSmem<DK> rs;
   extern __shared__ u32x4 stage_[];               // the tile's codes, later the row partials
@@ -1971,9 +1973,9 @@ __global__ __launch_bounds__((GeoRM<DK>::NT)) __attribute__((amdgpu_waves_per_eu
   asm volatile("" : "+s"(kinds));
 
   // ---- every global read first ----
-  u32x4 chunk[G::NCH];
+  u32x4 chunk[NCH];
 #pragma unroll
-  for (int i = 0; i < G::NCH; i++) {
+  for (int i = 0; i < NCH; i++) {
     const int off = 16 * (tid + i * G::NT);
     if (off < CB) chunk[i] = *(const u32x4*)(tile + off);
   }
@@ -1998,7 +2000,7 @@ __global__ __launch_bounds__((GeoRM<DK>::NT)) __attribute__((amdgpu_waves_per_eu
   const f32x2 vv = *(const f32x2*)(A.v + x * DV + 2 * l);
   const float bb = A.b[x];
 #pragma unroll
-  for (int i = 0; i < G::NCH; i++) {
+  for (int i = 0; i < NCH; i++) {
     const int off = 16 * (tid + i * G::NT);
     if (off < CB) *(u32x4*)(stage + off) = chunk[i];
   }
@@ -2380,7 +2382,7 @@ __global__ __launch_bounds__((GeoRM<DK>::NT)) __attribute__((amdgpu_waves_per_eu
   }
   lds_barrier();
 #pragma unroll
-  for (int i = 0; i < G::NCH; i++) {
+  for (int i = 0; i < NCH; i++) {
     const int off = 16 * (tid + i * G::NT);
     if (off < CB) *(u32x4*)(tile + off) = *(const u32x4*)(stage + off);
   }
@@ -3237,6 +3239,7 @@ struct stq_pool {
   std::vector<uint32_t> head_off;
   uint64_t hdr, woff, roff, slot_bytes, slots_off, cache_off, cache_stride, total;
   uint32_t rows_stage;                  // per-key-row units: LDS bytes the step kernel stages
+  uint32_t rows_cbmax;                  // per-key-row units: code bytes of the largest head
   uint8_t* dev;
   std::vector<uint8_t> header;  // host staging copy of the header
   hipEvent_t upload = nullptr;  // recorded after the header upload that reads `header`
@@ -3306,6 +3309,7 @@ void layout(const stq_pool_desc* d, stq_pool* p) {
   const uint64_t partb = 4ull * p->dk * (p->dv / 4 + 4);
   const uint64_t codeb = cbmax + 16 + 2 * p->dv;   // codes, read-ahead word, store sink of pivot steps
   p->rows_stage = (uint32_t)(((codeb > partb ? codeb : partb) + 15) / 16 * 16);
+  p->rows_cbmax = (uint32_t)cbmax;
   p->woff = ru256(64 + 8ull * p->H);
   p->roff = ru256(p->woff + 4ull * p->H * p->dk);
   p->hdr = rows ? ru256(p->roff + 2ull * p->H * p->dk + 16ull * p->H) : p->roff;
@@ -3379,10 +3383,15 @@ struct LRows {
 // per-key-row decode step: whole-row waves for d_v = 128, row-sharing waves for d_v = 64
 stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st) {
   const unsigned g = grid_of(A.n, A.H);
-  if (p->dv == 128 && p->dk == 128)
-    hipLaunchKernelGGL((k_rows_mf<128>), dim3(g), dim3(GeoRM<128>::NT), A.stage_bytes, st, A);
-  else if (p->dv == 128)
-    hipLaunchKernelGGL((k_rows_mf<64>), dim3(g), dim3(GeoRM<64>::NT), A.stage_bytes, st, A);
+  // four chunk rounds cover heads of up to 16 KB of codes (d_k = 128), 8 KB (d_k = 64)
+  const bool four = p->rows_cbmax <= 4u * 16u * (p->dk == 128 ? GeoRM<128>::NT : GeoRM<64>::NT);
+  if (p->dv == 128 && p->dk == 128) {
+    if (four) hipLaunchKernelGGL((k_rows_mf<128, 4>), dim3(g), dim3(GeoRM<128>::NT), A.stage_bytes, st, A);
+    else hipLaunchKernelGGL((k_rows_mf<128, GeoRM<128>::NCH>), dim3(g), dim3(GeoRM<128>::NT), A.stage_bytes, st, A);
+  } else if (p->dv == 128) {
+    if (four) hipLaunchKernelGGL((k_rows_mf<64, 4>), dim3(g), dim3(GeoRM<64>::NT), A.stage_bytes, st, A);
+    else hipLaunchKernelGGL((k_rows_mf<64, GeoRM<64>::NCH>), dim3(g), dim3(GeoRM<64>::NT), A.stage_bytes, st, A);
+  }
   else if (p->dk == 128)
     hipLaunchKernelGGL((k_rows_step<128, 64>), dim3(g), dim3(GeoR<128, 64>::NT), A.stage_bytes, st, A);
   else
