@@ -695,7 +695,7 @@ struct WSmem {
   // not written before the fold's last read, whenever it fits there
   static constexpr bool IN_PART = WMAX * DK <= DK * GeoM<DK, DV>::PSTR;
   float kap[IN_PART ? 4 : WMAX * DK] __attribute__((aligned(16)));   // k_s,i / (G_s sigma_i)
-  float vt[DV] __attribute__((aligned(16)));                         // the token's v (fold of a filling token)
+  float dk[WMAX], dq[WMAX];      // a filling token's sum_i g_i k_i kappa_s,i and sum_i g_i q_i kappa_s,i
 };
 
 // bytes per staged u row of the readout kernel (d_v + 16 floats: padding
@@ -914,20 +914,25 @@ __device__ __forceinline__ void window_read(const KArgs& A, WRead<DK, DV>& sm, f
 
 // Fold of a tile's open window: S = G_t S0 + sum_s (G_t/G_s) k_s u_s^T, refit,
 // window emptied.  ns: tokens in the window.  TOK: the window holds ns = W - 1
-// tokens and token x of the call fills it.  That token runs here, on the
-// materialised state: with G_t = fl(G_{ns} a) and g_i = G_t sigma_i,
-//   u_t = b (v - sum_i g_i k_i Y_ij),  o_t = sum_i g_i q_i Y_ij + (k.q) u_t,
-//   Y_ij += (k_i / g_i) u_t,j,
-// Y = S / (G_{ns} sigma) before the token and S / (G_t sigma) after it: the
-// readout kernel's window formula and the fold's materialised state, written
-// as one pass.  The token's (G_t, k_t, u_t) go to the cache as an append
-// would write them, then the window is emptied.
-template <int DK, int DV, int N, bool COMP, bool TOK = false>
+// tokens and token x of the call fills it.  That token's readout takes the
+// readout kernel's form, with G_t = fl(G_{ns} a) and g_i = G_t sigma_i:
+//   sum_i g_i k_i Y_ij = c_j sum_i g_i k_i Q_ij + sum_s d_s u_s,j,
+//   d_s = sum_i g_i k_i kappa_s,i   (and the same with q),
+//   u_t = b (v - that sum),  o_t = (the sum with q) + (k.q) u_t,
+// where Y = S_{ns} / (G_{ns} sigma) = c Q + sum_s kappa_s u_s^T; the codes'
+// matvec runs on the matrix cores.  The token then joins the window as entry
+// s = ns (kappa = k / g, u = u_t), S_W / (G_t sigma) is materialised with it,
+// and its (G_t, k_t, u_t) go to the cache as an append would write them before
+// the window is emptied.  WB: bound on the fold's tokens, window entries and
+// compensators together (W + C <= WB).
+template <int DK, int DV, int N, bool COMP, bool TOK = false, int WB = WMAX>
 __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, WSmem<DK, DV>& ws, uint8_t* tile,
                                             uint8_t* cache, int h, int ns, size_t x = 0) {
   using G = GeoM<DK, DV>;
   constexpr int K = N / 2;
   constexpr bool PIV = (N == 16);
+  constexpr int UB = WB / 4;                   // token quads: lane quad G holds s = 4i + G
+  static_assert(WB <= WMAX && WB % 4 == 0, "token bound");
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));                // the fold kernel loops over tiles: keep lane indices local
   const int w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
@@ -938,26 +943,33 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   int32_t* cntp = (int32_t*)cache;
   float* Gc = (float*)(cache + 4);
   float* Kc = (float*)(cache + 256);
-  float* Uc = Kc + (size_t)W * DK;
+  float* Uc = Kc + (size_t)W * DK;             // W rows of u, then the C compensator rows
   float* kap = WSmem<DK, DV>::IN_PART ? sm.part : ws.kap;
   // ns: tokens in the window (read by the caller), 1 <= ns <= W (TOK: 0 <= ns
-  // = W - 1).  The base's compensators ride along as nc more tokens s = ns +
-  // c: k = e_row, G = 1 relative to the window's start, u = the kept row
-  // (W + C <= 32)
+  // = W - 1).  Entries of the fold: s < ns from the cache, TOK: s = ns the
+  // call's token, then the base's compensators as nc more entries s = nt + c:
+  // k = e_row, G = 1 relative to the window's start, u = the kept row
+  const int nt = ns + (TOK ? 1 : 0);
+  const int nc = PIV || !COMP ? 0 : A.C;
+  const int nall = nt + nc;
+  const int32_t* cidx = (const int32_t*)(cache + 192);
   float Gt = ns ? Gc[ns - 1] : 1.f;
-  float kk = 0.f, qq = 0.f, vt = 0.f, bb = 0.f;
+  constexpr int NS = DK / 64;
+  float kk = 0.f, qq = 0.f, bb = 0.f;
+  float vv[G::NCC], sgl[NS];
+  size_t xu = 0;
   if constexpr (TOK) {
-    const size_t xu = (size_t)__builtin_amdgcn_readfirstlane((int)x);
+    xu = (size_t)__builtin_amdgcn_readfirstlane((int)x);
     const float a = ld_const(A.a + xu);          // the tile's gate and b: scalar loads
     bb = ld_const(A.b + xu);
     kk = A.k[xu * DK + rho];
     qq = A.q[xu * DK + rho];
-    if (tid < DV) vt = A.v[xu * DV + tid];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) vv[c] = A.v[xu * DV + w * G::CPW + 16 * c + n16];
+#pragma unroll
+    for (int q = 0; q < NS; q++) sgl[q] = PIV ? 1.f : bf16f(scl[l + 64 * q]);
     Gt = ns ? Gt * a : a;                        // binary32 running product, as the readout's
   }
-  const int nc = PIV || !COMP ? 0 : A.C;
-  const int32_t* cidx = (const int32_t*)(cache + 192);
-  const float* cval = (const float*)(cache + 256 + 4 * (size_t)W * (DK + DV));
   uint32_t raw[2 * N];
   f16x2 P[32];
 #pragma unroll
@@ -965,18 +977,26 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   float cc[G::NCC];
 #pragma unroll
   for (int c = 0; c < G::NCC; c++) cc[c] = PIV ? 1.f : bf16f(scl[DK + w * G::CPW + 16 * c + n16]);
-  float uq[UQ][G::NCC];
+  // the entries' u at the lane's columns: cache row s (s < ns) or W + c
+  // (compensator c); the call's token and unused slots read row 0 and keep 0
+  float uq[UB][G::NCC];
 #pragma unroll
-  for (int i = 0; i < UQ; i++)
+  for (int i = 0; i < UB; i++) {
+    const int s = 4 * i + Gq;
+    const bool cached = s < ns, comp = s >= nt && s < nall;
+    const int r = cached ? s : (comp ? W + s - nt : 0);
 #pragma unroll
-    for (int c = 0; c < G::NCC; c++)
-      uq[i][c] = 4 * i + Gq < ns ? Uc[(size_t)(4 * i + Gq) * DV + w * G::CPW + 16 * c + n16]
-               : (4 * i + Gq < ns + nc ? cval[(size_t)(4 * i + Gq - ns) * DV + w * G::CPW + 16 * c + n16] : 0.f);
+    for (int c = 0; c < G::NCC; c++) {
+      const float u = Uc[(size_t)r * DV + w * G::CPW + 16 * c + n16];
+      uq[i][c] = cached || comp ? u : 0.f;
+    }
+  }
   const uint32_t sgr = PIV ? 0x3F80u : scl[rho];
   const float wgt = A.weights[(size_t)h * DK + rho];
-  // kappa_s,i = k_s,i / (G_s sigma_i) for every token of the window, 4 rows per
-  // item; a fixed number of passes whose reads all issue before any is used
-  constexpr int KP = (WMAX * DK / 4 + G::NT - 1) / G::NT;
+  // kappa_s,i = k_s,i / (G_s sigma_i) for the cached entries, 4 rows per item; a
+  // fixed number of passes whose reads all issue before any is used (items
+  // past the window read row 0 and store nothing)
+  constexpr int KP = (WB * DK / 4 + G::NT - 1) / G::NT;
   f32x4 kv[KP];
   float gs[KP];
   u32x2 sg4[KP];
@@ -984,26 +1004,31 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
   for (int it = 0; it < KP; it++) {
     const int j = tid + it * G::NT;
     const int s = j / (DK / 4), r0 = 4 * (j - s * (DK / 4));
-    const bool on = j < ns * (DK / 4);
-    kv[it] = on ? *(const f32x4*)(Kc + (size_t)s * DK + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
-    gs[it] = on ? Gc[s] : 1.f;
-    sg4[it] = on && !PIV ? *(const u32x2*)(scl + r0) : u32x2{0x3F803F80u, 0x3F803F80u};
+    const int sv = j < ns * (DK / 4) ? s : 0;
+    kv[it] = *(const f32x4*)(Kc + (size_t)sv * DK + r0);
+    gs[it] = Gc[sv];
+    sg4[it] = PIV ? u32x2{0x3F803F80u, 0x3F803F80u} : *(const u32x2*)(scl + r0);
   }
   if (rsub == 0) sm.gg[rho] = Gt * bf16f(sgr);
+  float sc = 1.f, inv = 1.f;
   if constexpr (TOK) {
-    // the token's per-row factors: g k, g q and k / g (kappa, rowh: free until
-    // the refit), and k.q; v to LDS; the token's k and G to the cache now (an
-    // entry past the ones read below)
+    // binary16 range of the matvec operand: scale by the tile's largest g = G_t sigma
+    float gl = 0.f;
+#pragma unroll
+    for (int q = 0; q < NS; q++) gl = __builtin_fmaxf(gl, sgl[q]);
+    fp16_scale(wave_max_pos(gl) * Gt, sc, inv);
+    // the token's per-row factors: A fragments of (g k, g q), g k and g q for
+    // the window terms, kappa = k / g as entry ns; k.q; its k and G to the cache
     float kq = 0.f;
     if (rsub == 0) {
       const float g = Gt * bf16f(sgr);
+      put_afr<DK, DV, N>(sm, rho, (g * sc) * kk, (g * sc) * qq);
       sm.kappa[0][rho] = g * kk;
       sm.kappa[1][rho] = g * qq;
-      sm.rowh[rho] = kk * __builtin_amdgcn_rcpf(g);
+      kap[ns * DK + rho] = kk * __builtin_amdgcn_rcpf(g);
       kq = kk * qq;
       Kc[(size_t)ns * DK + rho] = kk;
     }
-    if (tid < DV) ws.vt[tid] = vt;
     if (tid == 0) Gc[ns] = Gt;
     kq = wave_sum(kq);
     if (l == 0) sm.kqn[w] = f32x2{kq, 0.f};
@@ -1022,14 +1047,82 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
       *(f32x4*)&kap[s * DK + r0] = o4;
     }
   }
-  // compensator tokens: kappa_{ns+c, i} = [i = row_c] / sigma_i
+  // compensator entries: kappa_{nt+c, i} = [i = row_c] / sigma_i
   for (int j = tid; COMP && j < nc * DK; j += G::NT) {
     const int c = j / DK, i = j - c * DK;
     const int rc = cidx[c];
-    kap[(ns + c) * DK + i] = i == rc ? 1.f / bf16f(scl[i]) : 0.f;
+    kap[(nt + c) * DK + i] = i == rc ? 1.f / bf16f(scl[i]) : 0.f;
   }
   __syncthreads();
   unpack<N>(raw, P);
+  if constexpr (TOK) {
+    // d_s of every entry: 8 consecutive lanes per entry
+    constexpr int TPP = G::NT / 8;
+#pragma unroll
+    for (int it = 0; it < (WB + TPP - 1) / TPP; it++) {
+      if (it * TPP >= nall) break;
+      const int s = tid / 8 + it * TPP;
+      const int sv = s < nall ? s : 0;
+      float ak = 0.f, aq = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < DK / 32; ii++) {
+        const int i = 4 * (tid % 8) + 32 * ii;
+        const f32x4 kv4 = *(const f32x4*)&sm.kappa[0][i];
+        const f32x4 qv4 = *(const f32x4*)&sm.kappa[1][i];
+        const f32x4 ks4 = *(const f32x4*)&kap[sv * DK + i];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          ak = __builtin_fmaf(ks4[e], kv4[e], ak);
+          aq = __builtin_fmaf(ks4[e], qv4[e], aq);
+        }
+      }
+      ak = rb_sum<8>(ak);
+      aq = rb_sum<8>(aq);
+      if (tid % 8 == 0 && s < nall) {
+        ws.dk[s] = ak;
+        ws.dq[s] = aq;
+      }
+    }
+    f32x4 D[G::NCC];
+    matvec<DK, DV>(sm, P, D);
+    __syncthreads();                           // d_s of every entry
+    float kqs = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
+    float pk[G::NCC], pq[G::NCC];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) pk[c] = pq[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < UB; i++) {
+      if (4 * i >= nall) break;
+      const int s = 4 * i + Gq;
+      const float fk = s < nall ? ws.dk[s] : 0.f, fq = s < nall ? ws.dq[s] : 0.f;
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) {
+        pk[c] = __builtin_fmaf(fk, uq[i][c], pk[c]);
+        pq[c] = __builtin_fmaf(fq, uq[i][c], pq[c]);
+      }
+    }
+    float dl[G::NCC];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++) {
+      const int j = w * G::CPW + 16 * c + n16;
+      const float u = cc[c] * ((D[c][0] + D[c][1]) * inv) + g4_sum(pk[c]);
+      const float wq = cc[c] * ((D[c][2] + D[c][3]) * inv) + g4_sum(pq[c]);
+      dl[c] = bb * (vv[c] - u);                  // the same bits in the four lane quads
+      if (Gq == 0) {
+        A.o[xu * DV + j] = __builtin_fmaf(dl[c], kqs, wq);
+        Uc[(size_t)ns * DV + j] = dl[c];           // the token's entry, as an append writes it
+      }
+    }
+    // the token is entry ns: quad ns % 4 of token quad ns / 4
+#pragma unroll
+    for (int i = 0; i < UB; i++)
+      if (i == (ns >> 2)) {
+#pragma unroll
+        for (int c = 0; c < G::NCC; c++) uq[i][c] = Gq == (ns & 3) ? dl[c] : uq[i][c];
+      }
+  }
   opaque(P);
   float Y[64];
 #pragma unroll
@@ -1044,12 +1137,12 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
 #pragma unroll
         for (int i = 0; i < 4; i++) C[c][i] = __builtin_fmaf(code_e<N>(P, e0 + i), cc[c], 0.0f);
       }
-      // four rank-one terms per MFMA: lane quad G carries token 4i + G
+      // four rank-one terms per MFMA: lane quad G carries entry 4i + G
 #pragma unroll
-      for (int i = 0; i < UQ; i++) {
-        if (4 * i >= ns + nc) break;
+      for (int i = 0; i < UB; i++) {
+        if (4 * i >= nall) break;
         const int s = 4 * i + Gq;
-        const float kv = s < ns + nc ? kap[s * DK + r0 + n16] : 0.f;
+        const float kv = s < nall ? kap[s * DK + r0 + n16] : 0.f;
 #pragma unroll
         for (int c = 0; c < G::NCC; c++) C[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, uq[i][c], C[c], 0, 0, 0);
       }
@@ -1060,59 +1153,6 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
         for (int i = 0; i < 4; i++) Y[e0 + i] = C[c][i];
       }
     }
-  if constexpr (TOK) {
-    float kqs = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < G::NW; ww++) kqs += sm.kqn[ww][0];
-    float pu[G::NCC], pw[G::NCC], dl[G::NCC];
-#pragma unroll
-    for (int c = 0; c < G::NCC; c++) pu[c] = pw[c] = 0.f;
-    // one 16-row block of factors at a time: each block's LDS reads wait for
-    // the previous block's sums, so they are not all hoisted (registers)
-    int fo = 4 * erow(0, 0, Gq);
-#pragma unroll
-    for (int rc = 0; rc < G::NRC; rc++)
-#pragma unroll
-      for (int hf = 0; hf < 2; hf++) {
-        const int bo = fo + 4 * (32 * rc + 16 * hf);
-        const f32x4 fk4 = *(const f32x4*)((const uint8_t*)sm.kappa[0] + bo);
-        const f32x4 fq4 = *(const f32x4*)((const uint8_t*)sm.kappa[1] + bo);
-#pragma unroll
-        for (int c = 0; c < G::NCC; c++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int e = 8 * (c * G::NRC + rc) + 4 * hf + i;
-            pu[c] = __builtin_fmaf(fk4[i], Y[e], pu[c]);
-            pw[c] = __builtin_fmaf(fq4[i], Y[e], pw[c]);
-          }
-        asm volatile("" : "+v"(fo) : "v"(pu[0]), "v"(pw[G::NCC - 1]));
-      }
-#pragma unroll
-    for (int c = 0; c < G::NCC; c++) {
-      const int j = w * G::CPW + 16 * c + n16;
-      dl[c] = bb * (ws.vt[j] - g4_sum(pu[c]));  // the same bits in the four lane quads
-      const float wq = g4_sum(pw[c]);
-      if (Gq == 0) {
-        A.o[x * DV + j] = __builtin_fmaf(dl[c], kqs, wq);
-        Uc[(size_t)ns * DV + j] = dl[c];                    // the token's entry, as an append writes it
-      }
-    }
-    int ko = 4 * erow(0, 0, Gq);
-#pragma unroll
-    for (int rc = 0; rc < G::NRC; rc++)
-#pragma unroll
-      for (int hf = 0; hf < 2; hf++) {
-        const f32x4 kc4 = *(const f32x4*)((const uint8_t*)sm.rowh + ko + 4 * (32 * rc + 16 * hf));
-#pragma unroll
-        for (int c = 0; c < G::NCC; c++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int e = 8 * (c * G::NRC + rc) + 4 * hf + i;
-            Y[e] = __builtin_fmaf(kc4[i], dl[c], Y[e]);
-          }
-        asm volatile("" : "+v"(ko) : "v"(Y[8 * rc + 4 * hf]));
-      }
-  }
   if constexpr (PIV) {                           // a binary16 pivot tile refits S itself
 #pragma unroll
     for (int e = 0; e < 64; e++) Y[e] = Gt * Y[e];
@@ -1160,7 +1200,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
 // turn (window_fold<..., TOK>).  An empty launch costs one wave of small
 // workgroups.  Flush: one tile per workgroup, any non-empty window.
 constexpr int FPW = 16;
-template <int DK, int DV, bool STEP, bool COMP>
+template <int DK, int DV, bool STEP, bool COMP, int WB>
 __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4))) void k_window_fold(KArgs A) {
   __shared__ SmemM<DK, DV> sm;
   __shared__ WSmem<DK, DV> ws;
@@ -1192,17 +1232,17 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     first = false;
     if constexpr (STEP) {
       switch (A.head_bits[h]) {
-        case 4: window_fold<DK, DV, 4, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
-        case 6: window_fold<DK, DV, 6, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
-        case 8: window_fold<DK, DV, 8, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
-        default: window_fold<DK, DV, 16, COMP, true>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+        case 4: window_fold<DK, DV, 4, COMP, true, WB>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+        case 6: window_fold<DK, DV, 6, COMP, true, WB>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+        case 8: window_fold<DK, DV, 8, COMP, true, WB>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
+        default: window_fold<DK, DV, 16, COMP, true, WB>(A, sm, ws, tile, cache, h, A.W - 1, tau); break;
       }
     } else {
       switch (A.head_bits[h]) {
-        case 4: window_fold<DK, DV, 4, COMP>(A, sm, ws, tile, cache, h, ns); break;
-        case 6: window_fold<DK, DV, 6, COMP>(A, sm, ws, tile, cache, h, ns); break;
-        case 8: window_fold<DK, DV, 8, COMP>(A, sm, ws, tile, cache, h, ns); break;
-        default: window_fold<DK, DV, 16, COMP>(A, sm, ws, tile, cache, h, ns); break;
+        case 4: window_fold<DK, DV, 4, COMP, false, WB>(A, sm, ws, tile, cache, h, ns); break;
+        case 6: window_fold<DK, DV, 6, COMP, false, WB>(A, sm, ws, tile, cache, h, ns); break;
+        case 8: window_fold<DK, DV, 8, COMP, false, WB>(A, sm, ws, tile, cache, h, ns); break;
+        default: window_fold<DK, DV, 16, COMP, false, WB>(A, sm, ws, tile, cache, h, ns); break;
       }
     }
   }
@@ -3398,6 +3438,15 @@ stq_status dispatch_rows_step(const stq_pool* p, const KArgs& A, hipStream_t st)
     hipLaunchKernelGGL((k_rows_step<64, 64>), dim3(g), dim3(GeoR<64, 64>::NT), A.stage_bytes, st, A);
   return hipGetLastError() == hipSuccess ? STQ_OK : STQ_ERR_HIP;
 }
+// fold kernel with its bound on entries: 16 when the window and its
+// compensators fit (W + C <= 16), else the largest window's 32
+template <int DK, int DV, bool STEP, bool COMP>
+void launch_fold(const KArgs& A, unsigned g, hipStream_t st) {
+  if (A.W + (COMP ? A.C : 0) <= 16)
+    hipLaunchKernelGGL((k_window_fold<DK, DV, STEP, COMP, 16>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
+  else
+    hipLaunchKernelGGL((k_window_fold<DK, DV, STEP, COMP, WMAX>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
+}
 // window mode: readout and append, then the fold of full windows (or, for a flush, of any open one)
 template <int DK, int DV>
 void launch_window(const KArgs& A, bool step, bool narrow, hipStream_t st) {
@@ -3410,14 +3459,12 @@ void launch_window(const KArgs& A, bool step, bool narrow, hipStream_t st) {
     else hipLaunchKernelGGL((k_window_read<DK, DV, false, false>), rg, rb, lds, st, A);
     const unsigned T = (unsigned)A.n * (unsigned)A.H;
     const unsigned g = (T + FPW - 1) / FPW;
-    if (A.C > 0)
-      hipLaunchKernelGGL((k_window_fold<DK, DV, true, true>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
-    else
-      hipLaunchKernelGGL((k_window_fold<DK, DV, true, false>), dim3(g), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    if (A.C > 0) launch_fold<DK, DV, true, true>(A, g, st);
+    else launch_fold<DK, DV, true, false>(A, g, st);
   } else if (A.C > 0) {
-    hipLaunchKernelGGL((k_window_fold<DK, DV, false, true>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    launch_fold<DK, DV, false, true>(A, grid_of(A.n, A.H), st);
   } else {
-    hipLaunchKernelGGL((k_window_fold<DK, DV, false, false>), dim3(grid_of(A.n, A.H)), dim3(GeoM<DK, DV>::NT), 0, st, A);
+    launch_fold<DK, DV, false, false>(A, grid_of(A.n, A.H), st);
   }
 }
 stq_status dispatch_window(const stq_pool* p, const KArgs& A, bool step, hipStream_t st) {
