@@ -114,7 +114,7 @@ BENCH = {
            "workload": "GDN serving pool B=512 H=32 d_k=d_v=128, heads {4b:9, 6b:16, 8b:6, fp16:1}",
            "dtype": "f32 update and refit; the two matvecs on matrix cores with each f32 operand split into "
                     "f16 hi + lo (f32 accumulation); 4/6/8-bit + f16 state"},
-    "C4": {"layers": 8, "kernel": "k_rows_mf<128>", "prof": "k_rows_mf_step",
+    "C4": {"layers": 8, "kernel": "k_rows_mf<128, 4>", "prof": "k_rows_mf_step",
            "metric": "request-head decode steps/s (B=256, H=32, d=128, KDA per-channel gate, "
                      "per-key-row widths)",
            "workload": "KDA pool B=256 H=32 d_k=d_v=128, per-channel gate, key rows "
@@ -123,8 +123,8 @@ BENCH = {
                     "f16 hi + lo (f32 accumulation), the rank-one update on f32 matrix cores; per-key-row "
                     "4/6/8-bit + f16 state"},
     "C5": {"layers": 2,
-           "kernel": "k_window_read<128, 128, false, true> + k_window_fold<128, 128, true, false>",
-           "regex": "k_window_(read<128, 128, false, true>|fold<128, 128, true, false>)",
+           "kernel": "k_window_read<128, 128, false, true> + k_window_fold<128, 128, true, false, 16>",
+           "regex": "k_window_(read<128, 128, false, true>|fold<128, 128, true, false, 16>)",
            "prof": "k_window_step",
            "metric": "request-head decode steps/s (B=512, H=32, d=128, 4-bit GDN, window W=16)",
            "workload": "windowed GDN pool B=512 H=32 d_k=d_v=128, all heads 4-bit, W=16 "
