@@ -552,6 +552,61 @@ def test_comp_window_teacher_forced(torch_cuda, orc, W, C, T):
     _assert_codes(agg)
 
 
+@pytest.mark.parametrize("dk,dv,W,C", [(64, 64, 8, 0), (64, 128, 16, 2), (128, 64, 8, 2)])
+def test_window_shapes(torch_cuda, orc, dk, dv, W, C):
+    """Window mode at the other tile shapes, with the head mix (4/6/8-bit and a
+    binary16 pivot head) and, where C > 0, compensator rows (d_k = 64, W = 16,
+    C = 2 takes the fold's 32-entry bound): teacher-forced through one fold and
+    a token past it, held to the bars of the d = 128 window tests."""
+    say("case window shape", dk, dv, W, C)
+    B, H = 6, 8
+    wl = Workload("C2", B=B, H=H)
+    wl.dk, wl.dv = dk, dv
+    wl.row_weight = wl.row_weight[:, :dk].copy()
+    wl.bits = np.array([4, 6, 8, 16, 6, 4, 8, 6], np.int32)
+    rng = np.random.default_rng(dk * 3 + dv + W + C)
+    P = Pair(orc, wl, n_slots=B + 2, window=W, n_comp=C)
+    slots = rng.permutation(B + 2)[:B]
+    S = (rng.standard_normal((B, H, dk, dv)) * np.exp(rng.normal(0, 1.5, (1, H, dk, 1)))).astype(np.float32)
+    for c in range(B):
+        for h in range(H):
+            for r, f in zip(rng.choice(dk, 2, replace=False), (50.0, 30.0)):
+                S[c, h, r] *= f
+    P.store(slots, S)
+    np.testing.assert_array_equal(P.image(), P.ref.img)
+    f = lambda x: x.astype(np.float32)
+    agg = new_agg()
+    worst_o = worst_u = 0.0
+    for t in range(W + 1):
+        img = P.image()
+        ref = orc.OraclePool(B + 2, H, dk, dv, wl.bits, wl.row_weight, window=W, image=img, n_comp=C)
+        q = rng.standard_normal((B, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k = rng.standard_normal((B, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((B, H, dv))
+        a = rng.uniform(0.9, 1, (B, H)); b = rng.uniform(0, 1, (B, H))
+        o = P.gpu_step(slots, f(q), f(k), f(v), f(a), f(b))
+        o_ref = ref.step(slots, f(q), f(k), f(v), f(a), f(b))
+        post = P.image()
+        worst_o = max(worst_o, readout_ok(o, o_ref))
+        for s in slots:
+            for h in range(H):
+                cg, Gg, Kg, Ug, ig, vg = ref.cache_view(int(s), h, post)
+                cr, Gr, Kr, Ur, ir, vr = ref.cache_view(int(s), h)
+                assert cg == cr == (t + 1) % W
+                np.testing.assert_array_equal(Gg[:cg], Gr[:cr])
+                np.testing.assert_array_equal(Kg[:cg], Kr[:cr])
+                if cg:
+                    worst_u = max(worst_u, float(np.abs(Ug[:cg] - Ur[:cr]).max() / np.abs(Ur[:cr]).max()))
+                np.testing.assert_array_equal(ig, ir)
+        if (t + 1) % W == 0:
+            add_agg(agg, compare_codes(orc, ref, post, ref.img, slots))
+    say("  window %dx%d W=%d C=%d: readout %.3f, cache u %.2e, fold %s"
+        % (dk, dv, W, C, worst_o, worst_u, agg_text(agg)))
+    assert worst_o <= 1.0
+    assert worst_u <= 1e-4
+    _assert_codes(agg)
+
+
 def test_comp_flush(torch_cuda, orc):
     say("case compensators flush")
     W, C = 16, 2
