@@ -30,8 +30,13 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        # STQ_ORACLE_LIB: a copy of the oracle compiled elsewhere (the planted-
+        # mistake tests load mutated copies this way); otherwise this one
+        path = os.environ.get("STQ_ORACLE_LIB")
+        if not path:
+            build()
+            path = _LIB
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         L.orc_tile_bytes.restype = ctypes.c_size_t
