@@ -457,22 +457,21 @@ def prefill_flops(n_tok, H, dk, dv):
     return n_tok * H * (6 * dk * dv + dk * PL + 2 * dv * (PL + 1))
 
 
-def prefill_bench(args):
-    """P3: prefill ingest of a batch of prompts into the C3 pool (GDN head mix,
-    H = 32, d = 128): one step = one stq_prefill call over all prompts.  P4: the
-    same with per-channel (KDA) gates of C4's half-life law on per-head widths
-    of the same mix (the token-by-token path).  P5: P4's prompts into the C4
-    pool itself (per-key-row widths: records decoded and refitted on chip)."""
+def prefill_setup(key, B, Lp, dev):
+    """Pool and prompts of the prefill workloads, drawn on the GPU: P3 the C3
+    pool (GDN head mix, H = 32, d = 128) with GDN half-life gates; P4 per-channel
+    (KDA) gates of C4's half-life law on per-head widths of the same mix; P5 P4's
+    prompts into the C4 pool (per-key-row widths).  B prompts of Lp tokens each,
+    one per slot; the pool's states are stored first.  Returns the workload, the
+    pool and its buffer, and the prefill call's tensors."""
     import dataclasses
 
     import torch
 
     import quantized_linear_attention_amd as stq
     from workloads import Workload
-    dev = torch.device("cuda:0")
-    B, Lp = args.prompts, args.prompt_len
-    kda = args.workload in ("P4", "P5")
-    rows = args.workload == "P5"
+    kda = key in ("P4", "P5")
+    rows = key == "P5"
     wl = Workload("C4" if kda else "C3", B=B)
     if kda and not rows:
         wl.cfg = dataclasses.replace(wl.cfg, unit=0)
@@ -509,6 +508,27 @@ def prefill_bench(args):
         a = torch.clamp(2.0 ** (-1.0 / hp), 0.9, 0.9999).contiguous()
     ss = torch.arange(0, T + 1, Lp, dtype=torch.int32, device=dev)
     o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    return {"wl": wl, "desc": desc, "buf": buf, "pool": pool, "slots": slots, "ss": ss, "o": o, "T": T,
+            "q": q, "k": k, "v": v, "a": a, "b": b}
+
+
+def prefill_bench(args):
+    """P3: prefill ingest of a batch of prompts into the C3 pool (GDN head mix,
+    H = 32, d = 128): one step = one stq_prefill call over all prompts.  P4: the
+    same with per-channel (KDA) gates of C4's half-life law on per-head widths
+    of the same mix (the token-by-token path).  P5: P4's prompts into the C4
+    pool itself (per-key-row widths: records decoded and refitted on chip)."""
+    import torch
+
+    import quantized_linear_attention_amd as stq
+    dev = torch.device("cuda:0")
+    B, Lp = args.prompts, args.prompt_len
+    kda = args.workload in ("P4", "P5")
+    rows = args.workload == "P5"
+    st = prefill_setup(args.workload, B, Lp, dev)
+    wl, pool, slots, ss, o = st["wl"], st["pool"], st["slots"], st["ss"], st["o"]
+    q, k, v, a, b = (st[x] for x in "qkvab")
+    c, H, dk, dv, T = wl.cfg, wl.H, wl.dk, wl.dv, st["T"]
     K = 8 if args.steps is None else args.steps
     Wu = 2 if args.warmup is None else args.warmup
     torch.cuda.synchronize()

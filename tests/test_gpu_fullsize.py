@@ -10,6 +10,8 @@ and a free-running report of how the quantized trajectories drift.
   whole window (16 tokens, the fold included), also with four compensator rows
   per tile: the launches the benchmark times, with sampled tiles re-stepped by
   the oracle from the GPU's bytes (teacher-forced), to the fused step's bar.
+- The prefill at the benchmark's size (64 prompts of 1,024 tokens, P3 and
+  P5), two sampled requests re-run by the oracle, to the prefill bars.
 - Free-running over C3's 64 tokens: the GPU pool and the oracle's pool each
   advance on their own from the same ingested state, next to the exact
   binary64 recurrence without any quantization.  Reported (per-step error
@@ -226,3 +228,43 @@ def test_free_running_c3_report(torch_cuda, orc):
             r = compare_codes(orc, P.ref, P.image(), P.ref.img, slots)
             say("  %5d  %12.2e  %15.2e  %13.2e  %15.2e"
                 % (t + 1, rel(o_g, o_x), rel(o_r, o_x), rel(o_g, o_r), r["mism"] / max(r["codes"], 1)))
+
+
+@pytest.mark.parametrize("key", ["P3", "P5"])
+def test_full_prefill_sampled(torch_cuda, orc, key):
+    """The prefill at the size the benchmark times (bench.py's own setup: 64
+    prompts of 1,024 tokens in one stq_prefill call; P3 into the C3 pool with
+    GDN gates, P5 into the per-key-row C4 pool with per-channel gates).  Two
+    sampled requests (all 32 heads) are re-run by the oracle from the pool's
+    bytes before the call: every readout of their 2,048 tokens, their final
+    states and their codes, to the prefill bars of test_gpu_prefill."""
+    import bench
+    from test_gpu_prefill import _assert_prefill_codes, _state_ok
+    torch = torch_cuda
+    B, Lp = 64, 1024
+    say("case full-size prefill", key, B, Lp)
+    st = bench.prefill_setup(key, B, Lp, torch.device("cuda:0"))
+    wl = st["wl"]
+    torch.cuda.synchronize()
+    pre = st["buf"].cpu().numpy()
+    import quantized_linear_attention_amd as stq
+    stq.stq_prefill(st["pool"], st["slots"], st["ss"], st["q"], st["k"], st["v"], st["a"], st["b"], st["o"])
+    torch.cuda.synchronize()
+    img = st["buf"].cpu().numpy()
+    sample = np.array([0, 37], np.int32)                         # slot c holds prompt c
+    tok = torch.as_tensor(np.concatenate([np.arange(c * Lp, (c + 1) * Lp) for c in sample]), device="cuda")
+    host = {x: st[x][tok].cpu().numpy() for x in "qkvab"}      # the sampled prompts' tokens only
+    o = st["o"][tok].cpu().numpy()
+    c = wl.cfg
+    ref = orc.OraclePool(B, wl.H, wl.dk, wl.dv, np.asarray(wl.bits).reshape(-1), wl.row_weight, c.gate, c.unit, 0,
+                         image=pre)
+    ss = np.arange(0, len(sample) * Lp + 1, Lp, dtype=np.int32)
+    o_ref, S_fin = ref.prefill(sample, ss, host["q"], host["k"], host["v"], host["a"], host["b"], final_state=True)
+    T = len(tok)
+    r = readout_ok(o.reshape(T, 1, wl.H, wl.dv), o_ref.reshape(T, 1, wl.H, wl.dv))
+    w = _state_ok(orc, ref, img, sample, S_fin, [True] * len(sample))
+    res = compare_codes(orc, ref, img, ref.img, sample)
+    say("  %s: readout worst ratio %.3g, state worst ratio %.3g, %s" % (key, r, w, agg_text(res)))
+    assert r <= 1.0
+    assert w <= 1.0
+    _assert_prefill_codes(res)
