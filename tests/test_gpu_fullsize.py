@@ -10,8 +10,8 @@ and a free-running report of how the quantized trajectories drift.
   whole window (16 tokens, the fold included), also with four compensator rows
   per tile: the launches the benchmark times, with sampled tiles re-stepped by
   the oracle from the GPU's bytes (teacher-forced), to the fused step's bar.
-- The prefill at the benchmark's size (64 prompts of 1,024 tokens, P3 and
-  P5), two sampled requests re-run by the oracle, to the prefill bars.
+- The prefill at the benchmark's size (64 prompts of 1,024 tokens, P3, P4
+  and P5), two sampled requests re-run by the oracle, to the prefill bars.
 - Free-running over C3's 64 tokens: the GPU pool and the oracle's pool each
   advance on their own from the same ingested state, next to the exact
   binary64 recurrence without any quantization.  Reported (per-step error
@@ -230,11 +230,12 @@ def test_free_running_c3_report(torch_cuda, orc):
                 % (t + 1, rel(o_g, o_x), rel(o_r, o_x), rel(o_g, o_r), r["mism"] / max(r["codes"], 1)))
 
 
-@pytest.mark.parametrize("key", ["P3", "P5"])
+@pytest.mark.parametrize("key", ["P3", "P4", "P5"])
 def test_full_prefill_sampled(torch_cuda, orc, key):
     """The prefill at the size the benchmark times (bench.py's own setup: 64
     prompts of 1,024 tokens in one stq_prefill call; P3 into the C3 pool with
-    GDN gates, P5 into the per-key-row C4 pool with per-channel gates).  Two
+    GDN gates, P4 the same head mix with per-channel gates, P5 into the
+    per-key-row C4 pool with per-channel gates).  Two
     sampled requests (all 32 heads) are re-run by the oracle from the pool's
     bytes before the call: every readout of their 2,048 tokens, their final
     states and their codes, to the prefill bars of test_gpu_prefill."""
