@@ -509,7 +509,7 @@ def test_comp_store_fetch_bit_exact(torch_cuda, orc):
     np.testing.assert_array_equal(F.cpu().numpy(), P.ref.fetch(slots))
 
 
-@pytest.mark.parametrize("W,C,T", [(8, 3, 17), (4, 8, 9), (16, 4, 17)])
+@pytest.mark.parametrize("W,C,T", [(8, 3, 17), (4, 8, 9), (16, 4, 17), (24, 8, 25)])
 def test_comp_window_teacher_forced(torch_cuda, orc, W, C, T):
     """Window steps with compensator tokens riding the cache path: readout and
     cached u every token, and at each fold the new compensator rows (same
