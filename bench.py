@@ -436,10 +436,6 @@ def split_timing(stq, torch, pools, slots, toks, o, L, K, Wu, wl, spec):
 
 PL = 32                     # tokens per chunk of the prefill kernel
 MFMA_F32_PEAK = 157.3       # TFLOP/s, dense binary32 matrix cores
-# binary32 vector ALUs one lane-op at a time: 256 CUs x 4 SIMDs x 16 lanes x 2
-# (fma) x 2.4 GHz = 78.6 TFLOP/s (the published 157.3 counts packed pairs,
-# which this code does not issue)
-VALU_F32_PEAK = 78.6
 
 
 def method_flops(n_tok, H, dk, dv, per_channel):
@@ -516,8 +512,9 @@ def prefill_bench(args):
     """P3: prefill ingest of a batch of prompts into the C3 pool (GDN head mix,
     H = 32, d = 128): one step = one stq_prefill call over all prompts.  P4: the
     same with per-channel (KDA) gates of C4's half-life law on per-head widths
-    of the same mix (the token-by-token path).  P5: P4's prompts into the C4
-    pool itself (per-key-row widths: records decoded and refitted on chip)."""
+    of the same mix (the chunkwise form with the gate products folded into the
+    keys and queries).  P5: P4's prompts into the C4 pool itself (per-key-row
+    widths: records decoded and refitted on chip)."""
     import torch
 
     import quantized_linear_attention_amd as stq
@@ -545,9 +542,11 @@ def prefill_bench(args):
     per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(K)])
     total_ms = float(ev[0].elapsed_time(ev[K]))
     avg_ms = float(per.mean())
-    # the method's own work (the chunk form issues more: flops_issued)
+    # the method's own work (the chunk form issues more on the matrix cores:
+    # flops_issued; with per-channel gates the gate is a per-chunk scaling of
+    # the keys and queries on the vector ALUs)
     flops = method_flops(T, H, dk, dv, kda)
-    issued = flops if kda else prefill_flops(T, H, dk, dv)
+    issued = prefill_flops(T, H, dk, dv)
     tflops = flops / (avg_ms * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
@@ -581,9 +580,8 @@ def prefill_bench(args):
         "config": {"workload": "prefill of %d prompts x %d tokens into the %s pool H=32 d_k=d_v=128, %s"
                                % (B, Lp, gname, mix),
                    "global_batch": B, "prompt_len": Lp, "heads": H, "d_k": dk, "d_v": dv},
-        "roofline": {"bound": "alu" if kda else "mfma", "achieved": tflops,
-                     "peak": VALU_F32_PEAK if kda else MFMA_F32_PEAK, "unit": "TFLOP/s",
-                     "frac": tflops / (VALU_F32_PEAK if kda else MFMA_F32_PEAK), "traffic": None,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_F32_PEAK, "traffic": None,
                      "kernel": "%s<128, 128, %s>" % ("k_prefill_rows" if rows else "k_prefill", "true" if kda else "false"),
                      "flops_per_launch": flops, "flops_issued_per_launch": issued,
                      "issued_tflops": issued / (avg_ms * 1e-3) / 1e12, "avg_launch_ms": avg_ms,

@@ -296,8 +296,8 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  * [tok][H][d_k]); b_dev [tok][H]; o_dev [tok][H][d_v]; seq_start_dev int32
  * [n+1], non-decreasing (a decreasing pair is an empty request).  All device
  * pointers, owned by the caller.
- * The state runs in binary32 (the GDN path's products on the matrix cores in
- * binary32, the per-channel path's on the vector ALUs):
+ * The state runs in binary32 (its products on the matrix cores in binary32;
+ * the chunks' gate products formed in binary64 and rounded once):
  * S_T and o differ from the exact recurrence by binary32 rounding only, so
  * a final code can differ from R of the exact state where that state sits
  * within rounding of a code boundary.  Requests must name distinct slots.
@@ -305,8 +305,11 @@ stq_status stq_decode_step(stq_pool* pool, const int32_t* slots_dev, int32_t n,
  * stq_window_flush does); the prompt then runs from the base plus its
  * compensator rows, and the final state is written as stq_pool_store writes
  * one (compensator rows taken again, window empty).
- * Every pool kind: GDN gate by the chunkwise form on the matrix cores,
- * per-channel gate by the recurrence token by token; per-key-row units run
+ * Every pool kind, by the chunkwise form on the matrix cores (chunks of 32
+ * tokens; with per-channel gates the chunk's gate products Gamma_t, per key
+ * channel, scale the keys and queries, K.Gamma, Q.Gamma and K/Gamma, and from
+ * a chunk whose smallest Gamma falls below 2^-60, a zero gate included, the
+ * request's remaining tokens run token by token); per-key-row units run
  * the state in record-row order (rows sorted by width, k, q and gates read
  * through the head's record -> row permutation) and write the final state
  * through R for per-key-row widths, packed into the row records on chip. */

@@ -2551,10 +2551,32 @@ struct PKSmem {
   float gb[PL], kq[PL];
 };
 
+// per-channel gates, chunkwise: the chunk's K~ = Gamma . K and Q~ = Gamma . Q,
+// whose space takes the right-hand side once the products have read them,
+// and K^ = K / Gamma (Gamma_t = per-channel product of the chunk's gates up to
+// token t); the token groups' gate products share the space of A, the
+// readout mask and T, which are not live at the chunk's start
+template <int DK, int DV>
+struct PCSmem {
+  union {
+    struct { float kc[PL][DK + 4]; float qc[PL][DK + 4]; } kq;
+    float rd[DV][PLP];             // diag(b) (V - K~ S), transposed; then Delta in its place
+  } u;
+  float kh[PL][DK + 4];
+  union {
+    struct { float am[PL][PLP]; float pm[PL][PLP]; float ti[PL][PLP]; } m;
+    double tot[8][DK];             // [g][channel]: gate product of token group g
+  } v;
+  float gl[DK];                    // Gamma of the chunk's last token
+  float gb[PL];
+  int slow[GeoM<DK, DV>::NW];      // per wave: some Gamma of the chunk below the chunk form's floor
+};
+
 template <int DK, int DV>
 union PrefillSmem {
   PSmem<DK, DV> p;
   PKSmem<DK, DV> k;
+  PCSmem<DK, DV> c;
   SmemM<DK, DV> m;
 };
 
@@ -2661,20 +2683,22 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
     // ---- gate products on the last wave (it has the fewest K K^T blocks): its
     // lane s < PL runs down column s of rho, lane PL down gamma
     const int gl0 = G::NT - 64;
+    // (in binary64: binary32 products of gates just below 1 drop their
+    // second-order term every time, a downward bias; each is rounded once)
     if (tid >= gl0 && tid < gl0 + PL) {
       const int sc = tid - gl0;
-      float r = 1.f;
+      double r = 1.0;
 #pragma unroll
       for (int t = 0; t < PL; t++) {
-        if (t > sc) r *= ps.ga[t];
-        ps.rt[t][sc] = t >= sc ? r : 0.f;
+        if (t > sc) r *= (double)ps.ga[t];
+        ps.rt[t][sc] = t >= sc ? (float)r : 0.f;
       }
     } else if (tid == gl0 + PL) {
-      float g = 1.f;
+      double g = 1.0;
 #pragma unroll
       for (int t = 0; t < PL; t++) {
-        g *= ps.ga[t];
-        ps.gam[t] = g;
+        g *= (double)ps.ga[t];
+        ps.gam[t] = (float)g;
       }
     }
     // ---- S^T K^T and S^T Q^T: this wave's columns x the chunk's tokens
@@ -2960,6 +2984,305 @@ __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps
   return moved;
 }
 
+// Per-channel gates (KDA), chunkwise.  With Gamma_t = a_0 ... a_t (per key
+// channel, the chunk's tokens 0 .. t) the recurrence unrolled over a chunk is
+//   S_t = Diag(Gamma_t) S + sum_{s<=t} Diag(Gamma_t / Gamma_s) k_s delta_s^T,
+// so with K~_t = Gamma_t . k_t, Q~_t = Gamma_t . q_t and K^_s = k_s / Gamma_s
+// the chunk is the scalar-gate chunk form with the decay inside the keys:
+//   A[t][s] = b_t K~_t . K^_s (s < t), Delta = (I + A)^-1 diag(b)(V - K~ S),
+//   O = Q~ S + tril(Q~ K^T^) Delta, S <- Diag(Gamma_last) (S + K^^T Delta).
+// K^ divides by gate products: from a chunk whose last Gamma (the smallest:
+// gates lie in [0, 1]) falls below 2^-60 in some channel, a zero gate
+// included, the request's remaining tokens run token by token (in the chunks
+// before, every K^ entry is at most 2^60 |k|).  Returns
+// nonzero in some thread if some token is not the identity.
+template <int DK, int DV, bool PERM = false>
+__device__ __forceinline__ int prefill_chunks_kda(const KArgs& A, PCSmem<DK, DV>& ps, PKSmem<DK, DV>& pk, float* Y,
+                                                  int tb0, int tb1, int h) {
+  using G = GeoM<DK, DV>;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, Gq = l >> 4, n16 = l & 15;
+  int moved = 0;
+  const int col0 = w * G::CPW;
+  // thread (channel quad c4, token group tg) holds TPT consecutive tokens of
+  // four channels: the gate products run down its tokens, then across groups
+  constexpr int CQ = DK / 4;
+  constexpr int TPT = PL * CQ / G::NT;
+  constexpr int NG = PL / TPT;
+  static_assert(TPT * NG == PL && NG * CQ == G::NT && NG <= 8, "chunk rows");
+  const int c4 = tid % CQ, tg = tid / CQ, d4 = 4 * c4;
+  f32x4 kn[TPT], qn[TPT], an[TPT], vr[G::NCC][2];
+  float bn;
+  // tokens past the end: k = q = v = 0, a = 1, b = 0
+  auto fetch = [&](int t0, int n) {
+#pragma unroll
+    for (int u = 0; u < TPT; u++) {
+      const int t = TPT * tg + u;
+      kn[u] = qn[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      an[u] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if (t < n) {
+        if constexpr (PERM) {                           // original rows of record rows d4 .. d4+3
+          const size_t r = ((size_t)(t0 + t) * A.H + h) * DK;
+          const uint32_t pr = *(const uint32_t*)(A.row_perm + (size_t)h * DK + d4);
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const uint32_t row = (pr >> (8 * i)) & 0xFFu;
+            kn[u][i] = A.k[r + row];
+            qn[u][i] = A.q[r + row];
+            an[u][i] = A.a[r + row];
+          }
+        } else {
+          const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
+          kn[u] = *(const f32x4*)(A.k + r);
+          qn[u] = *(const f32x4*)(A.q + r);
+          an[u] = *(const f32x4*)(A.a + r);
+        }
+      }
+    }
+    bn = 0.f;
+    if (tid < n) bn = A.b[(size_t)(t0 + tid) * A.H + h];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) {
+        const int t = 16 * tb + n16;
+        vr[c][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < n) vr[c][tb] = *(const f32x4*)(A.v + ((size_t)(t0 + t) * A.H + h) * DV + col0 + 16 * c + 4 * Gq);
+      }
+  };
+  int tr = tb1;                         // first token of the token-by-token rest
+  fetch(tb0, min(PL, tb1 - tb0));
+  for (int t0 = tb0; t0 < tb1; t0 += PL) {
+    const int Lc = min(PL, tb1 - t0);
+    // ---- gate products: inside the thread's token group, then the groups before
+    // it, in binary64 (binary32 products of gates just below 1 drop their
+    // second-order term every time, a downward bias that adds up over a chunk);
+    // each Gamma is rounded to binary32 once
+    double gp[TPT][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) gp[0][i] = (double)an[0][i];
+#pragma unroll
+    for (int u = 1; u < TPT; u++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) gp[u][i] = gp[u - 1][i] * (double)an[u][i];
+#pragma unroll
+    for (int i = 0; i < 4; i++) ps.v.tot[tg][d4 + i] = gp[TPT - 1][i];
+    if (tid < PL) ps.gb[tid] = bn;
+#pragma unroll
+    for (int u = 0; u < TPT; u++)
+      moved |= (an[u][0] != 1.f) | (an[u][1] != 1.f) | (an[u][2] != 1.f) | (an[u][3] != 1.f);
+    moved |= bn != 0.f;
+    lds_barrier();
+    double pre[4] = {1.0, 1.0, 1.0, 1.0};
+#pragma unroll
+    for (int g = 0; g < NG - 1; g++)
+      if (g < tg) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) pre[i] *= ps.v.tot[g][d4 + i];
+      }
+    bool slow = false;
+#pragma unroll
+    for (int u = 0; u < TPT; u++) {
+      const int t = TPT * tg + u;
+      f32x4 g4;
+#pragma unroll
+      for (int i = 0; i < 4; i++) g4[i] = (float)(pre[i] * gp[u][i]);
+      f32x4 kh;
+#pragma unroll
+      for (int i = 0; i < 4; i++) kh[i] = kn[u][i] * __builtin_amdgcn_rcpf(g4[i]);
+      *(f32x4*)&ps.u.kq.kc[t][d4] = kn[u] * g4;
+      *(f32x4*)&ps.u.kq.qc[t][d4] = qn[u] * g4;
+      *(f32x4*)&ps.kh[t][d4] = kh;
+      if (u == TPT - 1 && tg == NG - 1) {
+        *(f32x4*)&ps.gl[d4] = g4;
+        slow = !(g4[0] >= 0x1p-60f) | !(g4[1] >= 0x1p-60f) | !(g4[2] >= 0x1p-60f) | !(g4[3] >= 0x1p-60f);
+      }
+    }
+    const bool wslow = __ballot(slow) != 0;
+    if (l == 0) ps.slow[w] = wslow ? 1 : 0;
+    lds_barrier();
+    int sl = 0;
+#pragma unroll
+    for (int ww = 0; ww < G::NW; ww++) sl |= ps.slow[ww];
+    if (sl) {                           // some gate product too small for K^
+      lds_barrier();                    // every wave has read the flags
+      tr = t0;
+      break;
+    }
+    // ---- S^T K~^T and S^T Q~^T: this wave's columns x the chunk's tokens
+    f32x4 ck[G::NCC][2], cq[G::NCC][2];
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) ck[c][tb] = cq[c][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+      for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+          const f32x4 kb = *(const f32x4*)&ps.u.kq.kc[16 * tb + n16][32 * rc + 16 * hf + 4 * Gq];
+          const f32x4 qb = *(const f32x4*)&ps.u.kq.qc[16 * tb + n16][32 * rc + 16 * hf + 4 * Gq];
+#pragma unroll
+          for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const float y = Y[8 * (c * G::NRC + rc) + 4 * hf + i];
+              ck[c][tb] = mfma4(y, kb[i], ck[c][tb]);
+              cq[c][tb] = mfma4(y, qb[i], cq[c][tb]);
+            }
+        }
+    // ---- K~ K^^T and Q~ K^^T on and below the diagonal: 6 blocks dealt to the waves
+    constexpr int NB = (6 + G::NW - 1) / G::NW;
+    f32x4 kq[NB];
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      const int bi = w + j * G::NW;
+      kq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (bi < 6) {
+        const int isq = bi >= 3, bb = bi % 3, tb = bb ? 1 : 0, sb = bb == 2 ? 1 : 0;
+        const float* xr = isq ? &ps.u.kq.qc[16 * tb + n16][4 * Gq] : &ps.u.kq.kc[16 * tb + n16][4 * Gq];
+        const float* kr = &ps.kh[16 * sb + n16][4 * Gq];
+#pragma unroll
+        for (int d0 = 0; d0 < DK; d0 += 16) {
+          const f32x4 xa = *(const f32x4*)(xr + d0), kb = *(const f32x4*)(kr + d0);
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) kq[j] = mfma4(xa[jj], kb[jj], kq[j]);
+        }
+      }
+    }
+    lds_barrier();
+    // ---- A and the readout mask (rows t = 16 tb + 4G + i, column s = 16 sb + n)
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      const int bi = w + j * G::NW;
+      if (bi < 6) {
+        const int isq = bi >= 3, bb = bi % 3, tb = bb ? 1 : 0, sb = bb == 2 ? 1 : 0;
+        const int s = 16 * sb + n16;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int t = 16 * tb + 4 * Gq + i;
+          if (isq) ps.v.m.pm[t][s] = s <= t ? kq[j][i] : 0.f;
+          else ps.v.m.am[t][s] = s < t ? ps.gb[t] * kq[j][i] : 0.f;
+        }
+      }
+    }
+    // ---- right-hand side (columns j = col0 + 16 c + 4G + i, token t = 16 tb + n),
+    // over K~ and Q~, which every wave has read
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) {
+        const int t = 16 * tb + n16, j0 = col0 + 16 * c + 4 * Gq;
+        const float bt = ps.gb[t];
+#pragma unroll
+        for (int i = 0; i < 4; i++) ps.u.rd[j0 + i][t] = bt * (vr[c][tb][i] - ck[c][tb][i]);
+      }
+    lds_barrier();
+    // ---- T = (I + A)^-1 on wave 0, as in the scalar-gate chunks
+    if (w == 0) {
+      const int bo = l & 16, cl = l & 15;
+      float x[16];
+#pragma unroll
+      for (int t = 0; t < 16; t++) {
+        float acc = t == cl ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 0; r < t; r++) acc = __builtin_fmaf(-ps.v.m.am[bo + t][bo + r], x[r], acc);
+        x[t] = acc;
+      }
+      if (l < PL) {
+#pragma unroll
+        for (int t = 0; t < 16; t++) ps.v.m.ti[bo + t][bo + cl] = x[t];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      f32x4 m = {0.f, 0.f, 0.f, 0.f};              // A21 T11: row 4G + i, column n
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 4) m = mfma4(ps.v.m.am[16 + n16][r0 + Gq], ps.v.m.ti[r0 + Gq][n16], m);
+#pragma unroll
+      for (int i = 0; i < 4; i++) ps.v.m.am[16 + 4 * Gq + i][n16] = m[i];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      f32x4 tt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 4) tt = mfma4(ps.v.m.ti[16 + n16][16 + r0 + Gq], ps.v.m.am[16 + r0 + Gq][n16], tt);
+#pragma unroll
+      for (int i = 0; i < 4; i++) ps.v.m.ti[16 + 4 * Gq + i][n16] = -tt[i];
+    }
+    lds_barrier();
+    // ---- Delta = T rhs for this wave's columns, written over rhs
+    f32x4 dl[2][G::NCC];
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r0 = 0; r0 <= 16 * tb; r0 += 16) {
+          const f32x4 ta = *(const f32x4*)&ps.v.m.ti[16 * tb + n16][r0 + 4 * Gq];
+          const f32x4 rb = *(const f32x4*)&ps.u.rd[col0 + 16 * c + n16][r0 + 4 * Gq];
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) d = mfma4(ta[jj], rb[jj], d);
+        }
+        dl[tb][c] = d;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) *(f32x4*)&ps.u.rd[col0 + 16 * c + n16][16 * tb + 4 * Gq] = dl[tb][c];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // ---- readout O^T = S^T Q~^T + Delta^T tril(Q~ K^^T)^T
+#pragma unroll
+    for (int c = 0; c < G::NCC; c++)
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++) {
+        const int t = 16 * tb + n16;
+        f32x4 o = cq[c][tb];
+#pragma unroll
+        for (int s0 = 0; s0 <= 16 * tb; s0 += 16) {
+          const f32x4 da = *(const f32x4*)&ps.u.rd[col0 + 16 * c + n16][s0 + 4 * Gq];
+          const f32x4 pb = *(const f32x4*)&ps.v.m.pm[t][s0 + 4 * Gq];
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) o = mfma4(da[jj], pb[jj], o);
+        }
+        if (t < Lc) *(f32x4*)(A.o + ((size_t)(t0 + t) * A.H + h) * DV + col0 + 16 * c + 4 * Gq) = o;
+      }
+    // ---- state: S <- Diag(Gamma_last) S + (Gamma_last . K^)^T Delta
+    f32x4 wb[G::NCC][2];
+#pragma unroll
+    for (int sg = 0; sg < 2; sg++)
+#pragma unroll
+      for (int c = 0; c < G::NCC; c++) wb[c][sg] = *(const f32x4*)&ps.u.rd[col0 + 16 * c + n16][16 * sg + 4 * Gq];
+#pragma unroll
+    for (int rc = 0; rc < G::NRC; rc++)
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++) {
+        const f32x4 g4 = *(const f32x4*)&ps.gl[32 * rc + 16 * hf + 4 * Gq];   // rows of the lane's elements
+        const float gn = ps.gl[32 * rc + 16 * hf + n16];                      // row of its operand
+        float ka[2][4];                                 // K^ entries: row 32 rc + 16 hf + n, token 16 sg + 4G + jj
+#pragma unroll
+        for (int sg = 0; sg < 2; sg++)
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) ka[sg][jj] = ps.kh[16 * sg + 4 * Gq + jj][32 * rc + 16 * hf + n16] * gn;
+#pragma unroll
+        for (int c = 0; c < G::NCC; c++) {
+          const int e0 = 8 * (c * G::NRC + rc) + 4 * hf;
+          f32x4 C = {Y[e0] * g4[0], Y[e0 + 1] * g4[1], Y[e0 + 2] * g4[2], Y[e0 + 3] * g4[3]};
+#pragma unroll
+          for (int sg = 0; sg < 2; sg++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) C = mfma4(ka[sg][jj], wb[c][sg][jj], C);
+#pragma unroll
+          for (int i = 0; i < 4; i++) Y[e0 + i] = C[i];
+        }
+      }
+    if (t0 + PL < tb1) fetch(t0 + PL, min(PL, tb1 - t0 - PL));
+    lds_barrier();
+  }
+  // from a chunk whose gate products the chunk form cannot divide by, the
+  // request's remaining tokens run token by token
+  if (tr < tb1) moved |= prefill_tokens<DK, DV, PERM>(A, pk, Y, tr, tb1, h);
+  return moved;
+}
+
 // ------------------------------------------------------------------------
 // Prefill into per-key-row tiles.  The state runs in the prefill's lane layout
 // with its rows in record order (sorted by width); the chunk's K, Q and
@@ -3171,7 +3494,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
   if (tb1 <= tb0) return;                            // no tokens: the tile is left as it is
   float Y[64];
   decode_rows_state<DK, DV>(A, (uint8_t*)sh.r.stage, tile, h, Y);
-  const int moved = KDA ? prefill_tokens<DK, DV, true>(A, sh.pre.k, Y, tb0, tb1, h)
+  const int moved = KDA ? prefill_chunks_kda<DK, DV, true>(A, sh.pre.c, sh.pre.k, Y, tb0, tb1, h)
                         : prefill_chunks<DK, DV, true>(A, sh.pre.p, Y, tb0, tb1, h);
   // identity tokens only: the tile is left as it is (the decode step's rule)
   if (!__syncthreads_or(moved)) return;
@@ -3213,7 +3536,8 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
       }
     }
   }
-  const int moved = KDA ? prefill_tokens<DK, DV>(A, sh.k, Y, tb0, tb1, h) : prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
+  const int moved = KDA ? prefill_chunks_kda<DK, DV>(A, sh.c, sh.k, Y, tb0, tb1, h)
+                        : prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
   // identity tokens only: the tile is left as it is (the decode step's rule)
   if (!__syncthreads_or(moved)) return;
   const int rho = (int)threadIdx.x / G::TPR;
@@ -3252,7 +3576,7 @@ __global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per
     Y[e] = st[erow(b % G::NRC, t, Gq) * DV + w * G::CPW + 16 * (b / G::NRC) + n16];
   }
   lds_barrier();
-  if (KDA) prefill_tokens<DK, DV>(A, sh.k, Y, tb0, tb1, h);
+  if (KDA) prefill_chunks_kda<DK, DV>(A, sh.c, sh.k, Y, tb0, tb1, h);
   else prefill_chunks<DK, DV>(A, sh.p, Y, tb0, tb1, h);
 #pragma unroll
   for (int e = 0; e < 64; e++) {

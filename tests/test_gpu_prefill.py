@@ -210,8 +210,11 @@ def test_prefill_window_pool(torch_cuda, orc, W, C):
 
 @pytest.mark.parametrize("dk,dv,zero", [(128, 128, False), (64, 128, True)])
 def test_prefill_per_channel_gate(torch_cuda, orc, dk, dv, zero):
-    """Per-channel (KDA) gates on per-head widths: the token-by-token path, with
-    the KDA half-life law (and whole zero channels when asked)."""
+    """Per-channel (KDA) gates on per-head widths, with the KDA half-life law:
+    the chunkwise form; with zero gates (when asked) a request's tokens from
+    the chunk that holds one run token by token: head 0 of the first request
+    from its first chunk, the other heads from its second (the first chunk
+    chunkwise), head 2 of the last request from its first."""
     import dataclasses
     say("case prefill per-channel gate", dk, dv, zero)
     wl = Workload("C4", B=3, H=8)
@@ -228,7 +231,8 @@ def test_prefill_per_channel_gate(torch_cuda, orc, dk, dv, zero):
 
     def edit(ss, q, k, v, a, b):
         if zero:
-            a[5, :, :7] = 0.0
+            a[5, 0, :7] = 0.0
+            a[40, :, :7] = 0.0
             a[ss[2] + 31, 2, :] = 0.0
 
     out = _run(P, wl, slots, lens, edit if zero else None)
