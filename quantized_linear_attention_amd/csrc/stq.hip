@@ -2570,6 +2570,7 @@ struct PCSmem {
   float gl[DK];                    // Gamma of the chunk's last token
   float gb[PL];
   int slow[GeoM<DK, DV>::NW];      // per wave: some Gamma of the chunk below the chunk form's floor
+  uint8_t rec[DK];                 // per-key-row tiles: record row of each original row
 };
 
 template <int DK, int DV>
@@ -3012,7 +3013,9 @@ __device__ __forceinline__ int prefill_chunks_kda(const KArgs& A, PCSmem<DK, DV>
   const int c4 = tid % CQ, tg = tid / CQ, d4 = 4 * c4;
   f32x4 kn[TPT], qn[TPT], an[TPT], vr[G::NCC][2];
   float bn;
-  // tokens past the end: k = q = v = 0, a = 1, b = 0
+  // tokens past the end: k = q = v = 0, a = 1, b = 0.  Channels in their own
+  // order (16-byte loads); per-key-row tiles take the record order on the LDS
+  // writes (the gate products are per channel, so they commute with it)
   auto fetch = [&](int t0, int n) {
 #pragma unroll
     for (int u = 0; u < TPT; u++) {
@@ -3020,22 +3023,10 @@ __device__ __forceinline__ int prefill_chunks_kda(const KArgs& A, PCSmem<DK, DV>
       kn[u] = qn[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       an[u] = f32x4{1.f, 1.f, 1.f, 1.f};
       if (t < n) {
-        if constexpr (PERM) {                           // original rows of record rows d4 .. d4+3
-          const size_t r = ((size_t)(t0 + t) * A.H + h) * DK;
-          const uint32_t pr = *(const uint32_t*)(A.row_perm + (size_t)h * DK + d4);
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const uint32_t row = (pr >> (8 * i)) & 0xFFu;
-            kn[u][i] = A.k[r + row];
-            qn[u][i] = A.q[r + row];
-            an[u][i] = A.a[r + row];
-          }
-        } else {
-          const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
-          kn[u] = *(const f32x4*)(A.k + r);
-          qn[u] = *(const f32x4*)(A.q + r);
-          an[u] = *(const f32x4*)(A.a + r);
-        }
+        const size_t r = ((size_t)(t0 + t) * A.H + h) * DK + d4;
+        kn[u] = *(const f32x4*)(A.k + r);
+        qn[u] = *(const f32x4*)(A.q + r);
+        an[u] = *(const f32x4*)(A.a + r);
       }
     }
     bn = 0.f;
@@ -3050,6 +3041,9 @@ __device__ __forceinline__ int prefill_chunks_kda(const KArgs& A, PCSmem<DK, DV>
       }
   };
   int tr = tb1;                         // first token of the token-by-token rest
+  if constexpr (PERM) {                 // record row of each original row (read after the first barrier)
+    for (int p = tid; p < DK; p += G::NT) ps.rec[A.row_perm[(size_t)h * DK + p]] = (uint8_t)p;
+  }
   fetch(tb0, min(PL, tb1 - tb0));
   for (int t0 = tb0; t0 < tb1; t0 += PL) {
     const int Lc = min(PL, tb1 - t0);
@@ -3080,6 +3074,9 @@ __device__ __forceinline__ int prefill_chunks_kda(const KArgs& A, PCSmem<DK, DV>
         for (int i = 0; i < 4; i++) pre[i] *= ps.v.tot[g][d4 + i];
       }
     bool slow = false;
+    int rr[4];                          // LDS column of the thread's four channels
+#pragma unroll
+    for (int i = 0; i < 4; i++) rr[i] = PERM ? (int)ps.rec[d4 + i] : d4 + i;
 #pragma unroll
     for (int u = 0; u < TPT; u++) {
       const int t = TPT * tg + u;
@@ -3089,11 +3086,26 @@ __device__ __forceinline__ int prefill_chunks_kda(const KArgs& A, PCSmem<DK, DV>
       f32x4 kh;
 #pragma unroll
       for (int i = 0; i < 4; i++) kh[i] = kn[u][i] * __builtin_amdgcn_rcpf(g4[i]);
-      *(f32x4*)&ps.u.kq.kc[t][d4] = kn[u] * g4;
-      *(f32x4*)&ps.u.kq.qc[t][d4] = qn[u] * g4;
-      *(f32x4*)&ps.kh[t][d4] = kh;
+      const f32x4 kt = kn[u] * g4, qt = qn[u] * g4;
+      if constexpr (PERM) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          ps.u.kq.kc[t][rr[i]] = kt[i];
+          ps.u.kq.qc[t][rr[i]] = qt[i];
+          ps.kh[t][rr[i]] = kh[i];
+        }
+      } else {
+        *(f32x4*)&ps.u.kq.kc[t][d4] = kt;
+        *(f32x4*)&ps.u.kq.qc[t][d4] = qt;
+        *(f32x4*)&ps.kh[t][d4] = kh;
+      }
       if (u == TPT - 1 && tg == NG - 1) {
-        *(f32x4*)&ps.gl[d4] = g4;
+        if constexpr (PERM) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) ps.gl[rr[i]] = g4[i];
+        } else {
+          *(f32x4*)&ps.gl[d4] = g4;
+        }
         slow = !(g4[0] >= 0x1p-60f) | !(g4[1] >= 0x1p-60f) | !(g4[2] >= 0x1p-60f) | !(g4[3] >= 0x1p-60f);
       }
     }

@@ -12,9 +12,10 @@ and a free-running report of how the quantized trajectories drift.
   the oracle from the GPU's bytes (teacher-forced), to the fused step's bar.
 - The prefill at the benchmark's size (64 prompts of 1,024 tokens, P3, P4
   and P5), two sampled requests re-run by the oracle, to the prefill bars.
-- Free-running over C3's 64 tokens: the GPU pool and the oracle's pool each
-  advance on their own from the same ingested state, next to the exact
-  binary64 recurrence without any quantization.  Reported (per-step error
+- Free-running over each decode configuration's own length (C3 64 tokens,
+  C4 32, C5 64): the GPU pool and the oracle's pool each advance on their
+  own from the same ingested state, next to the exact binary64 recurrence
+  without any quantization.  Reported (per-step error
   feeding forward is what the pages quantify), gated only on finiteness.
 """
 import numpy as np
@@ -194,23 +195,29 @@ def test_full_c5_compensators_sampled(torch_cuda, orc):
 
 
 def _exact_step(S, q, k, v, a, b):
-    """The gated delta rule in binary64 on unquantized states [n][H][dk][dv],
-    scalar gate per (request, head): S' = a S + k (b (v - a S^T k))^T, o = S'^T q."""
-    S = S * a[..., None, None]
+    """The gated delta rule in binary64 on unquantized states [n][H][dk][dv]:
+    A = a S (scalar gate per (request, head)) or Diag(a) S (per-channel gate,
+    a [n][H][dk]), S' = A + k (b (v - A^T k))^T, o = S'^T q."""
+    S = S * (a[..., :, None] if a.ndim == 3 else a[..., None, None])
     u = np.einsum("nhij,nhi->nhj", S, k)
     S = S + k[..., :, None] * (b[..., None] * (v - u))[..., None, :]
     return S, np.einsum("nhij,nhi->nhj", S, q)
 
 
-def test_free_running_c3_report(torch_cuda, orc):
-    """C3's generator, 64 tokens, 16 requests x 32 heads: the GPU pool and the
-    oracle's pool step on their own (no teacher forcing).  Reported per token:
-    the GPU's and the oracle's readout error against the exact unquantized
-    recurrence (from the same decoded start), the GPU-vs-oracle readout
-    difference and the fraction of codes in which the two pools differ."""
-    say("case free-running C3, 64 tokens")
-    T = 64
-    wl = Workload("C3", B=16)
+# the configurations' own lengths: C3 64 tokens, C4 32, C5 64 (four windows)
+FREE_RUNS = [("C3", 64), ("C4", 32), ("C5", 64)]
+
+
+@pytest.mark.parametrize("key,T", FREE_RUNS)
+def test_free_running_report(torch_cuda, orc, key, T):
+    """Each configuration's generator over its own length, 16 requests x 32
+    heads: the GPU pool and the oracle's pool step on their own (no teacher
+    forcing).  Reported per token: the GPU's and the oracle's readout error
+    against the exact unquantized recurrence (from the same decoded start),
+    the GPU-vs-oracle readout difference and the fraction of codes in which
+    the two pools differ (window pools: the base, rewritten at each fold)."""
+    say("case free-running %s, %d tokens" % (key, T))
+    wl = Workload(key, B=16)
     P = Pair(orc, wl)
     slots = np.arange(wl.B)
     P.store(slots, wl.state(slots))
