@@ -214,7 +214,9 @@ def test_prefill_per_channel_gate(torch_cuda, orc, dk, dv, zero):
     the chunkwise form; with zero gates (when asked) a request's tokens from
     the chunk that holds one run token by token: head 0 of the first request
     from its first chunk, the other heads from its second (the first chunk
-    chunkwise), head 2 of the last request from its first."""
+    chunkwise), head 2 of the last request from its first; tiny nonzero gates
+    whose chunk product falls below 2^-60 do the same (head 3 of the first
+    request would, from its third chunk)."""
     import dataclasses
     say("case prefill per-channel gate", dk, dv, zero)
     wl = Workload("C4", B=3, H=8)
@@ -234,6 +236,7 @@ def test_prefill_per_channel_gate(torch_cuda, orc, dk, dv, zero):
             a[5, 0, :7] = 0.0
             a[40, :, :7] = 0.0
             a[ss[2] + 31, 2, :] = 0.0
+            a[64:70, 3, 10:20] = 1e-4     # nonzero, but the chunk's product (1e-24) is below the form's floor
 
     out = _run(P, wl, slots, lens, edit if zero else None)
     _check(P, wl, slots, lens, *out, moved=[L > 0 for L in lens])
