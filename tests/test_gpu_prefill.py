@@ -384,6 +384,30 @@ def test_prefill_rows_parity(torch_cuda, orc, dk, dv, gate):
     _check(P, wl, slots, lens, *out, moved=[L > 0 for L in lens])
 
 
+@pytest.mark.parametrize("unit", [0, 1])
+def test_prefill_per_channel_identity(torch_cuda, orc, unit):
+    """Per-channel gates: a request whose tokens are all the identity (every
+    gate 1, b = 0) leaves its tiles' bytes as they are, next to requests that
+    move, on per-head and per-key-row widths."""
+    import dataclasses
+    say("case prefill per-channel identity, unit", unit)
+    wl = Workload("C4", B=3, H=8)
+    if unit == 0:
+        wl.cfg = dataclasses.replace(wl.cfg, unit=0)
+        wl.bits = np.array([4, 6, 8, 16, 6, 4, 8, 6], np.int32)
+    P = Pair(orc, wl, n_slots=4)
+    slots = np.array([3, 1, 0], np.int32)
+    P.store(slots, wl.state(slots))
+    lens = [40, 37, 9]
+
+    def edit(ss, q, k, v, a, b):
+        a[ss[1]:ss[2]] = 1.0
+        b[ss[1]:ss[2]] = 0.0
+
+    out = _run(P, wl, slots, lens, edit)
+    _check(P, wl, slots, lens, *out, moved=[True, False, True])
+
+
 @pytest.mark.parametrize("gate", [1, 0])
 def test_prefill_rows_exact_scaling(torch_cuda, orc, gate):
     """Gates of 1/2 and b = 0: the final state is D(tile) times an exact power
