@@ -384,6 +384,30 @@ def test_prefill_rows_parity(torch_cuda, orc, dk, dv, gate):
     _check(P, wl, slots, lens, *out, moved=[L > 0 for L in lens])
 
 
+def test_prefill_states_gates_one_paths_agree(torch_cuda, orc):
+    """With every gate 1 the per-channel chunk form (Gamma = 1: K~ = K^ = K,
+    Q~ = Q) performs exactly the scalar-gate chunk form's operations, so the
+    two paths must give bit-identical states and readouts."""
+    import torch
+    import quantized_linear_attention_amd as stq
+    say("case prefill states, gates 1: per-channel path against scalar-gate path")
+    wl = Workload("C4", B=2, H=8)
+    ss, q, k, v, a, b = wl.prompts([100, 37])
+    T = int(ss[-1])
+    dev = lambda x: torch.as_tensor(np.ascontiguousarray(x), device="cuda")
+    S0 = wl.state(np.arange(2)).astype(np.float32)
+    S_g, S_k = dev(S0), dev(S0)
+    o_g = torch.empty((T, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+    o_k = torch.empty_like(o_g)
+    stq.stq_prefill_states(S_g, dev(ss), dev(q), dev(k), dev(v), dev(np.ones((T, wl.H), np.float32)), dev(b), o_g,
+                           gate_kind=0)
+    stq.stq_prefill_states(S_k, dev(ss), dev(q), dev(k), dev(v), dev(np.ones((T, wl.H, wl.dk), np.float32)),
+                           dev(b), o_k, gate_kind=1)
+    torch.cuda.synchronize()
+    assert torch.equal(S_g, S_k)
+    assert torch.equal(o_g, o_k)
+
+
 @pytest.mark.parametrize("unit", [0, 1])
 def test_prefill_per_channel_identity(torch_cuda, orc, unit):
     """Per-channel gates: a request whose tokens are all the identity (every
