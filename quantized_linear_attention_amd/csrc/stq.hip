@@ -1165,8 +1165,9 @@ __device__ __forceinline__ void window_fold(const KArgs& A, SmemM<DK, DV>& sm, W
 
 // readout and append of every tile of the call.  NARROW: every head of the
 // pool is 4-bit (the pages' window variant); that path fits 8 waves per SIMD
-// (64 VGPRs) without spilling, and eight workgroups' LDS fit a CU at W = 16.
-// Other pools take the full kernel at 6 waves.
+// (64 VGPRs) without spilling, and eight workgroups' LDS fit a CU at W = 16;
+// with compensator rows the larger LDS keeps it at 7 (whose 72 VGPRs it
+// needs: at 64 it spills).  Other pools take the full kernel at 6 waves.
 template <int DK, int DV, bool COMP, bool NARROW>
 __device__ __forceinline__ void window_read_tile(const KArgs& A, WRead<DK, DV>& sm, float* cst) {
   const int T = A.n * A.H;
@@ -1188,7 +1189,7 @@ __device__ __forceinline__ void window_read_tile(const KArgs& A, WRead<DK, DV>& 
   }
 }
 template <int DK, int DV, bool COMP, bool NARROW>
-__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(NARROW ? 8 : 6))) void k_window_read(KArgs A) {
+__global__ __launch_bounds__((GeoM<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(NARROW ? (COMP ? 7 : 8) : 6))) void k_window_read(KArgs A) {
   __shared__ WRead<DK, DV> sm;
   extern __shared__ float cst_[];               // W (d_k + d_v) floats: the staged window cache
   window_read_tile<DK, DV, COMP, NARROW>(A, sm, cst_);
