@@ -2884,9 +2884,10 @@ __device__ __forceinline__ int prefill_chunks(const KArgs& A, PSmem<DK, DV>& ps,
 // Per-channel gates (KDA): the plain recurrence token by token on the state
 // registers, S <- Diag(a) S + k delta^T with delta = b (v - (Diag(a) S)^T k),
 // o = (Diag(a) S)^T q + delta (k.q): each lane holds 32 rows of 2 (NCC) columns,
-// the column sums close over the four lane groups.  (A chunkwise form would need
-// the per-channel decay inside every K K^T entry.)  Returns nonzero in some
-// thread if some token is not the identity.
+// the column sums close over the four lane groups.  The chunk form below,
+// prefill_chunks_kda, hands a request's remaining tokens to this recurrence
+// from a chunk whose gate products it cannot divide by.  Returns nonzero in
+// some thread if some token is not the identity.
 template <int DK, int DV, bool PERM = false>
 __device__ __forceinline__ int prefill_tokens(const KArgs& A, PKSmem<DK, DV>& ps, float* Y, int tb0, int tb1,
                                               int h) {
