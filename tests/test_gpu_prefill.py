@@ -208,7 +208,7 @@ def test_prefill_window_pool(torch_cuda, orc, W, C):
                 assert np.abs(g[5] - r[5]).max() <= 1e-4 * np.abs(r[5]).max(), (c, h)
 
 
-@pytest.mark.parametrize("dk,dv,zero", [(128, 128, False), (64, 128, True)])
+@pytest.mark.parametrize("dk,dv,zero", [(128, 128, False), (64, 128, True), (64, 64, True), (128, 64, False)])
 def test_prefill_per_channel_gate(torch_cuda, orc, dk, dv, zero):
     """Per-channel (KDA) gates on per-head widths, with the KDA half-life law:
     the chunkwise form; with zero gates (when asked) a request's tokens from
@@ -368,7 +368,7 @@ def _rows_prompts(wl, lens, gate, seed):
     return ss, f(q), f(k), f(v), f(a), f(b)
 
 
-@pytest.mark.parametrize("dk,dv,gate", [(128, 128, 1), (128, 128, 0), (64, 128, 1), (128, 64, 1), (64, 64, 0)])
+@pytest.mark.parametrize("dk,dv,gate", [(128, 128, 1), (128, 128, 0), (64, 128, 1), (128, 64, 1), (64, 64, 0), (64, 64, 1)])
 def test_prefill_rows_parity(torch_cuda, orc, dk, dv, gate):
     """Per-key-row pools through stq_prefill (no binary32 staging): ragged
     prompts, tails inside a chunk, an empty request; per-channel (KDA) and
